@@ -1,0 +1,306 @@
+"""Plain CPU oracle for the NVFP4 KV-cache path.  TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``
+may import this module.  The product package never imports it, and this module imports
+nothing from the product package: the two share no code, tables or constants.
+
+Sources, by page title (section / table named at each function):
+  [cache post]  rstation.ai post "NVFP4 attention cache on W4A4 Qwen3-8B: static key
+                smoothing is near-lossless, key rotations hurt"
+  [OSFP4]       paperlayer.ai summary of arXiv 2610.08231v1, "OSFP4: Joint Optimization of
+                Diagonal Smoothing and Block Scales for NVFP4 Quantization"
+  [QServe rec]  inference-research record "QServe SmoothAttention (4-bit KV cache with an
+                accuracy-preserving correction)"
+  [GPTQ thread] rstation.ai comment thread of u/krylov_schur
+
+What the oracle computes (plain, slow, obviously correct; NumPy, fp64 unless noted):
+  * calibrate           -- static per-channel key smoothing s = sqrt(absmax) with window
+                           position 0 excluded, r = 1/s, and per-tensor fp32 scales g.
+  * key_transform       -- fp32 smoothing multiply, optional unnormalised Hadamard-128
+                           butterfly in a fixed stage order (this *is* the encoding input,
+                           so it is computed in fp32 exactly as specified).
+  * quantize_rows       -- NVFP4 encoding: per 16-element block an E4M3 scale chosen so the
+                           block absmax maps to 6, then E2M1 codes; both roundings are
+                           round-to-nearest-even on the EXACT real quotient.
+  * dequantize          -- code value * block scale * tensor scale, in fp64 (exact).
+  * query_transform     -- q*s, optionally H(q*s)/128, in fp64.
+  * attention           -- textbook softmax attention over the dequantised cache, fp64.
+
+Readings taken where the pages leave a step open (each is repeated in the design notes):
+  - tensor scale g = amax / (6*448), from calibration windows, over ALL positions of the
+    transformed keys (the sink is not clipped); g = 1 when amax = 0.
+  - E4M3 is the OCP E4M3FN variant (bias 7, subnormals, max 448, no infinities).
+  - block scale = E4M3 round-to-nearest-even of A_b/(6 g), saturating to 448; quotients at
+    or below 2^-10 give scale 0, and a zero scale gives an all-zero block.
+  - E2M1 rounding is to nearest with ties to the even code; magnitudes >= 6 give 6; a zero
+    magnitude is stored as the +0 code.
+  - smoothing multiplies keys by r = fl32(1/s) and queries by s; V is never transformed.
+  - Hadamard is the Sylvester +-1 matrix applied to keys unnormalised (stages h=1..64,
+    (a,b) -> (a+b, a-b), each rounded to fp32); the query side carries the exact 1/128.
+  - smoothing is applied before the Hadamard basis when both are selected.
+
+Every function here is pinned by a CPU test against something other than itself
+(brute-force nearest search with exact rationals, closed forms printed on the pages,
+algebraic invariants, and a library attention routine); no function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+HEAD_DIM = 128
+BLOCK = 16
+N_BLOCKS = HEAD_DIM // BLOCK
+
+FLAG_SMOOTH = 1
+FLAG_HADAMARD = 2
+
+# Largest E2M1 magnitude ([OSFP4] section 1: the FP4 constellation tops out at 6) and
+# largest finite E4M3FN value (bias 7, mantissa 0b110 at exponent 15).
+E2M1_MAX = 6.0
+E4M3_MAX = 448.0
+TENSOR_SCALE_DIVISOR = E2M1_MAX * E4M3_MAX  # 2688: amax maps to 6 * 448
+
+
+# ----------------------------------------------------------------------------------------
+# Number formats ([OSFP4] appendix D.1: E2M1 values, E4M3 scales per 16 channels and an
+# FP32 tensor scale; appendix I: the scale constellation is the positive E4M3 points).
+# ----------------------------------------------------------------------------------------
+def e2m1_decode(code: int) -> float:
+    """Value of a 4-bit E2M1 code: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0."""
+    sign = -1.0 if (code >> 3) & 1 else 1.0
+    e = (code >> 1) & 3
+    m = code & 1
+    if e == 0:
+        mag = 0.5 * m                      # subnormal: m * 2^(1-1) * 1/2
+    else:
+        mag = 2.0 ** (e - 1) * (1.0 + m / 2.0)
+    return sign * mag
+
+
+def e4m3_decode(code: int) -> float:
+    """Value of an 8-bit E4M3FN code: sign bit 7, exponent bits 6..3 (bias 7), mantissa 2..0.
+    Exponent 15 with mantissa 7 is NaN; there is no infinity."""
+    sign = -1.0 if (code >> 7) & 1 else 1.0
+    e = (code >> 3) & 15
+    m = code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    if e == 0:
+        mag = (m / 8.0) * 2.0 ** (1 - 7)
+    else:
+        mag = 2.0 ** (e - 7) * (1.0 + m / 8.0)
+    return sign * mag
+
+
+E2M1_MAG_GRID = np.array([e2m1_decode(c) for c in range(8)], dtype=np.float64)   # codes 0..7
+E4M3_GRID = np.array([e4m3_decode(c) for c in range(127)], dtype=np.float64)     # 0 .. 448
+
+
+def rne_grid_index(a: np.ndarray, unit: np.ndarray, grid: np.ndarray) -> np.ndarray:
+    """Index of the point of ``grid`` nearest to the exact quotient a/unit, ties to the even
+    index; quotients beyond the last point give the last index (saturation).
+
+    ``grid`` is increasing and starts at 0.  The midpoint between grid[k] and grid[k+1] is
+    passed when a > mid_k*unit, or when a == mid_k*unit and k+1 is even.  Callers guarantee
+    that a and every mid_k*unit are exact in fp64 (a is an fp32 value, unit is a product of
+    at most 26 significant bits, each midpoint has at most 5), so each comparison is exact.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    unit = np.broadcast_to(np.asarray(unit, dtype=np.float64), a.shape)
+    mids = (grid[:-1] + grid[1:]) / 2.0
+    idx = np.zeros(a.shape, dtype=np.int64)
+    for k, mk in enumerate(mids):
+        thr = mk * unit
+        idx += (a > thr) | ((a == thr) & ((k + 1) % 2 == 0))
+    return idx
+
+
+# ----------------------------------------------------------------------------------------
+# Key transform ([cache post] cache-config table rows "static per-channel smoothing" and
+# "Hadamard-128 on head_dim"; [QServe rec] SmoothAttention).  fp32, fixed op order.
+# ----------------------------------------------------------------------------------------
+def hadamard_butterfly_fp32(y: np.ndarray) -> np.ndarray:
+    """Unnormalised Sylvester Hadamard along the last axis (length 128) in fp32: stages
+    h = 1, 2, 4, ..., 64; in each stage every pair (i, i+h) with (i & h) == 0 becomes
+    (fl32(y_i + y_{i+h}), fl32(y_i - y_{i+h}))."""
+    y = np.array(y, dtype=np.float32, copy=True)
+    n = y.shape[-1]
+    lead = y.shape[:-1]
+    h = 1
+    while h < n:
+        v = y.reshape(lead + (n // (2 * h), 2, h))
+        a = v[..., 0, :]
+        b = v[..., 1, :]
+        s = (a + b).astype(np.float32)
+        d = (a - b).astype(np.float32)
+        y = np.stack([s, d], axis=-2).reshape(lead + (n,))
+        h *= 2
+    return y
+
+
+def sylvester_hadamard(n: int = HEAD_DIM) -> np.ndarray:
+    """Dense Sylvester matrix H_n, H_1 = [1], H_2k = [[H_k, H_k], [H_k, -H_k]] (int64)."""
+    H = np.ones((1, 1), dtype=np.int64)
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def key_transform(x: np.ndarray, r: np.ndarray | None, flags: int) -> np.ndarray:
+    """Post-RoPE key rows x (any float dtype holding bf16 values, last axis 128) -> fp32 rows
+    that get quantised.  Smoothing: y_j = fl32(x_j * r_j); then the Hadamard butterfly."""
+    y = np.asarray(x, dtype=np.float32)
+    if flags & FLAG_SMOOTH:
+        y = (y * np.asarray(r, dtype=np.float32)).astype(np.float32)
+    if flags & FLAG_HADAMARD:
+        y = hadamard_butterfly_fp32(y)
+    return y
+
+
+# ----------------------------------------------------------------------------------------
+# Calibration ([cache post] smoothing row: sqrt(absmax) from 4 windows, position 0
+# excluded; [OSFP4] section 3: a static calibration-based global scale lets blocks be
+# quantised online before the whole tensor exists).
+# ----------------------------------------------------------------------------------------
+def calibrate(k_win: np.ndarray | None, v_win: np.ndarray | None,
+              exclude_pos0: bool = True, k_flags: int = FLAG_SMOOTH):
+    """k_win, v_win: [W][T][Hkv][128] arrays of bf16 values (as float).
+    Returns (s [Hkv][128] f32, r [Hkv][128] f32, g [2] f32) with g = (g_K, g_V).
+    A part whose windows are None is returned as None (s, r) / NaN (g entry)."""
+    s = r = None
+    g = np.array([np.nan, np.nan], dtype=np.float32)
+    if k_win is not None:
+        k = np.asarray(k_win, dtype=np.float64)
+        kk = k[:, 1:] if exclude_pos0 else k
+        a = np.abs(kk).max(axis=(0, 1)) if kk.shape[1] > 0 else np.zeros(k.shape[2:])
+        # fp32 sqrt and reciprocal, each correctly rounded (fp64 then one rounding to fp32
+        # is exact-rounding for sqrt and division: 53 >= 2*24 + 2).
+        s = np.where(a == 0.0, 1.0, np.sqrt(a)).astype(np.float32)
+        r = (np.float32(1.0) / s).astype(np.float32)
+        y = key_transform(np.asarray(k_win, dtype=np.float32), r[None, None], k_flags)
+        g[0] = _tensor_scale(np.abs(y.astype(np.float64)).max())
+    if v_win is not None:
+        g[1] = _tensor_scale(np.abs(np.asarray(v_win, dtype=np.float64)).max())
+    return s, r, g
+
+
+def _tensor_scale(amax: float) -> np.float32:
+    """g = fl32(amax / 2688), or 1 when amax is 0."""
+    if amax == 0.0:
+        return np.float32(1.0)
+    return np.float32(np.float64(np.float32(amax)) / TENSOR_SCALE_DIVISOR)
+
+
+# ----------------------------------------------------------------------------------------
+# NVFP4 encoding ([OSFP4] section 1: 16-entry groups, E4M3 scales, FP4 max 6, absmax-to-6
+# flushes entries 24x below the block max; section 3: absmax-to-6 per 16-entry group at
+# inference; [cache post] opening paragraph: 16-blocks along head_dim, post-RoPE K/V).
+# ----------------------------------------------------------------------------------------
+def quantize_rows(y32: np.ndarray, g: float):
+    """Rows of 128 fp32 values -> (codes u8 [..., 64], scales u8 [..., 8]).
+
+    Block b = elements 16b..16b+15.  A_b = max |y|; scale code S_b = E4M3 RNE of the exact
+    A_b/(6g), saturating at 448; sigma_b = value(S_b).  Element magnitude code =
+    E2M1 RNE of the exact |y|/(sigma_b g) (0 when sigma_b = 0); nibble = 0 for magnitude 0,
+    else sign<<3 | magnitude.  Byte k = nibble(2k) | nibble(2k+1) << 4."""
+    y32 = np.asarray(y32, dtype=np.float32)
+    lead = y32.shape[:-1]
+    y = y32.astype(np.float64).reshape(lead + (N_BLOCKS, BLOCK))
+    g64 = np.float64(np.float32(g))
+    A = np.abs(y).max(axis=-1)
+    S = rne_grid_index(A, 6.0 * g64, E4M3_GRID)
+    sigma = E4M3_GRID[S]
+    unit = (sigma * g64)[..., None] * np.ones_like(y)
+    mag = rne_grid_index(np.abs(y), unit, E2M1_MAG_GRID)
+    mag = np.where((sigma == 0.0)[..., None], 0, mag)
+    sign = np.signbit(y32.reshape(y.shape)).astype(np.int64)
+    nib = np.where(mag == 0, 0, (sign << 3) | mag).reshape(lead + (HEAD_DIM,))
+    codes = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+    return codes, S.astype(np.uint8)
+
+
+def unpack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """u8 [..., 64] -> nibbles [..., 128] (low nibble = even element)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    out = np.empty(codes.shape[:-1] + (2 * codes.shape[-1],), dtype=np.int64)
+    out[..., 0::2] = codes & 0xF
+    out[..., 1::2] = codes >> 4
+    return out
+
+
+E2M1_ALL = np.array([e2m1_decode(c) for c in range(16)], dtype=np.float64)
+E4M3_ALL = np.array([e4m3_decode(c) for c in range(256)], dtype=np.float64)
+
+
+def dequantize(codes: np.ndarray, scales: np.ndarray, g: float) -> np.ndarray:
+    """x_hat_j = e2m1(nibble_j) * sigma_b * g in fp64 (exact: 2 + 4 + 24 significant bits)."""
+    nib = unpack_nibbles(codes)
+    lead = nib.shape[:-1]
+    vals = E2M1_ALL[nib].reshape(lead + (N_BLOCKS, BLOCK))
+    sig = E4M3_ALL[np.asarray(scales, dtype=np.int64)][..., None]
+    return (vals * sig * np.float64(np.float32(g))).reshape(lead + (HEAD_DIM,))
+
+
+# ----------------------------------------------------------------------------------------
+# Decode attention ([cache post] opening paragraph: attention runs over the fake-quantised
+# post-RoPE cache; smoothing row: SmoothAttention, keys divided and queries multiplied by s;
+# Hadamard rows: an orthogonal basis change on head_dim).
+# ----------------------------------------------------------------------------------------
+def query_transform(q: np.ndarray, s: np.ndarray | None, flags: int) -> np.ndarray:
+    """q [..., 128] (bf16 values) -> q' in fp64: q*s, then H(q*s)/128 when Hadamard is on.
+    ``s`` broadcasts against q (one row per KV head of each query head)."""
+    qp = np.asarray(q, dtype=np.float64)
+    if flags & FLAG_SMOOTH:
+        qp = qp * np.asarray(s, dtype=np.float64)
+    if flags & FLAG_HADAMARD:
+        H = sylvester_hadamard(HEAD_DIM).astype(np.float64)
+        qp = qp @ H.T / 128.0
+    return qp
+
+
+def attention(qp: np.ndarray, k_hat: list, v_hat: list, seq_lens, sm_scale: float):
+    """Textbook GQA decode attention in fp64.
+
+    qp: [B][Hq][128] transformed queries; k_hat[b], v_hat[b]: [n_b][Hkv][128] dequantised
+    cache of sequence b (n_b >= seq_lens[b]).  Query head hq reads KV head hq // (Hq/Hkv).
+    Output [B][Hq][128]; a sequence with no cached tokens gives zeros."""
+    qp = np.asarray(qp, dtype=np.float64)
+    B, Hq, D = qp.shape
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n == 0:
+            continue
+        K = np.asarray(k_hat[b], dtype=np.float64)[:n]
+        V = np.asarray(v_hat[b], dtype=np.float64)[:n]
+        Hkv = K.shape[1]
+        grp = Hq // Hkv
+        for hq in range(Hq):
+            h = hq // grp
+            e = sm_scale * (K[:, h, :] @ qp[b, hq])
+            p = np.exp(e - e.max())
+            p /= p.sum()
+            out[b, hq] = p @ V[:, h, :]
+    return out
+
+
+# ----------------------------------------------------------------------------------------
+# Sizes ([cache post] closing paragraph: BF16 cache size per token; [GPTQ thread] results
+# table: NVFP4 at 4.50 bits per value).
+# ----------------------------------------------------------------------------------------
+def row_bytes(fmt: str, head_dim: int = HEAD_DIM) -> int:
+    """Bytes of one (token, KV head) row: bf16 = 2*D; nvfp4 = D/2 code bytes + D/16 scales."""
+    if fmt == "bf16":
+        return 2 * head_dim
+    if fmt == "nvfp4":
+        return head_dim // 2 + head_dim // BLOCK
+    raise ValueError(fmt)
+
+
+def cache_bytes_per_token(k_fmt: str, v_fmt: str, num_kv_heads: int, num_layers: int,
+                          head_dim: int = HEAD_DIM) -> int:
+    return num_layers * num_kv_heads * (row_bytes(k_fmt, head_dim) + row_bytes(v_fmt, head_dim))
+
+
+def bits_per_value(fmt: str, head_dim: int = HEAD_DIM) -> float:
+    return 8.0 * row_bytes(fmt, head_dim) / head_dim

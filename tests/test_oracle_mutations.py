@@ -1,0 +1,109 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case swaps one oracle function for a copy with a plausible mistake (wrong tie rule,
+wrong grid, wrong divisor, dropped term, swapped sign or index, transposed operand) and
+checks that at least one pin test fails.  Mistakes are planted only in the oracle, on the
+CPU.
+"""
+import numpy as np
+import pytest
+
+from oracle import nvfp4_oracle as O
+from tests import test_oracle_codec as C
+from tests import test_oracle_transforms as T
+
+
+def _ties_to_odd(a, unit, grid):
+    a = np.asarray(a, dtype=np.float64)
+    unit = np.broadcast_to(np.asarray(unit, dtype=np.float64), a.shape)
+    mids = (grid[:-1] + grid[1:]) / 2.0
+    idx = np.zeros(a.shape, dtype=np.int64)
+    for k, mk in enumerate(mids):
+        thr = mk * unit
+        idx += (a > thr) | ((a == thr) & ((k + 1) % 2 == 1))
+    return idx
+
+
+def _quantize_absmax_to_4(y32, g):
+    return ORIG_Q(np.asarray(y32, np.float32) * np.float32(1.5), g)
+
+
+def _quantize_swapped_nibbles(y32, g):
+    codes, scales = ORIG_Q(y32, g)
+    return ((codes >> 4) | (codes << 4)).astype(np.uint8), scales
+
+
+def _butterfly_wrong_sign(y):
+    y = np.array(y, dtype=np.float32, copy=True)
+    n = y.shape[-1]
+    lead = y.shape[:-1]
+    h = 1
+    while h < n:
+        v = y.reshape(lead + (n // (2 * h), 2, h))
+        a, b = v[..., 0, :], v[..., 1, :]
+        y = np.stack([(a + b).astype(np.float32), (b - a).astype(np.float32)], -2).reshape(lead + (n,))
+        h *= 2
+    return y
+
+
+def _key_transform_times_s(x, r, flags):
+    rr = None if r is None else (np.float32(1) / np.asarray(r, np.float32)).astype(np.float32)
+    return ORIG_KT(x, rr, flags)
+
+
+def _calibrate_keep_pos0(k_win, v_win, exclude_pos0=True, k_flags=O.FLAG_SMOOTH):
+    return ORIG_CAL(k_win, v_win, exclude_pos0=False, k_flags=k_flags)
+
+
+def _attention_wrong_group(qp, k_hat, v_hat, seq_lens, sm_scale):
+    qp = np.asarray(qp, np.float64)
+    B, Hq, D = qp.shape
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n == 0:
+            continue
+        K = np.asarray(k_hat[b])[:n]
+        V = np.asarray(v_hat[b])[:n]
+        Hkv = K.shape[1]
+        for hq in range(Hq):
+            h = hq % Hkv                      # interleaved instead of grouped mapping
+            e = sm_scale * (K[:, h] @ qp[b, hq])
+            p = np.exp(e - e.max())
+            out[b, hq] = (p / p.sum()) @ V[:, h]
+    return out
+
+
+def _dequant_drop_g(codes, scales, g):
+    return ORIG_DQ(codes, scales, 1.0)
+
+
+ORIG_Q = O.quantize_rows
+ORIG_KT = O.key_transform
+ORIG_CAL = O.calibrate
+ORIG_DQ = O.dequantize
+
+CASES = [
+    ("rne_grid_index", _ties_to_odd, [C.test_e4m3_block_scale_vs_fraction_brute_force,
+                                      C.test_e2m1_constructed_ties_and_midpoints]),
+    ("E2M1_MAG_GRID", np.array([0, .5, 1, 1.5, 2, 3, 4, 5.0]), [C.test_e2m1_table_matches_hand_enumeration_and_max6]),
+    ("quantize_rows", _quantize_absmax_to_4, [C.test_quantize_rows_vs_fraction_brute_force_random_rows]),
+    ("quantize_rows", _quantize_swapped_nibbles, [C.test_quantize_rows_vs_fraction_brute_force_random_rows]),
+    ("hadamard_butterfly_fp32", _butterfly_wrong_sign, [T.test_butterfly_unit_vectors_equal_dense_columns]),
+    ("key_transform", _key_transform_times_s, [T.test_smoothing_preserves_scores_up_to_rounding]),
+    ("calibrate", _calibrate_keep_pos0, [T.test_calibrate_excludes_position0_and_rounds_exactly]),
+    ("attention", _attention_wrong_group, [T.test_attention_matches_torch_sdpa_fp64]),
+    ("dequantize", _dequant_drop_g, [C.test_dequantize_exact_and_roundtrip_error_bound]),
+]
+
+
+@pytest.mark.parametrize("name,mutant,pins", CASES, ids=[f"{c[0]}-{i}" for i, c in enumerate(CASES)])
+def test_planted_mistake_is_caught(monkeypatch, name, mutant, pins):
+    monkeypatch.setattr(O, name, mutant)
+    caught = 0
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, f"planted mistake in {name} not caught"
