@@ -1,0 +1,180 @@
+/*
+ * nvfp4kv.h -- C ABI of the NVFP4 attention-KV-cache library for AMD MI355X (gfx950).
+ *
+ * The operations (sources named by page title and section):
+ *   [cache post] rstation.ai post "NVFP4 attention cache on W4A4 Qwen3-8B: static key
+ *                smoothing is near-lossless, key rotations hurt": post-RoPE cached keys and
+ *                values quantised to NVFP4 in 16-element blocks along head_dim (opening
+ *                paragraph); static per-channel key smoothing sqrt(absmax) from 4 calibration
+ *                windows with position 0 excluded, optional Hadamard-128 key basis
+ *                (cache-config table); attention runs over the quantised cache.
+ *   [OSFP4]      paperlayer.ai summary of arXiv 2610.08231v1 "OSFP4: Joint Optimization of
+ *                Diagonal Smoothing and Block Scales for NVFP4 Quantization": E2M1 values,
+ *                E4M3 scale per 16 entries, FP32 tensor scale (appendix D.1); block scale
+ *                set so the block absmax maps to 6 (section 1); a static calibration-based
+ *                global scale for online quantisation (section 3).
+ *   [QServe rec] inference-research record "QServe SmoothAttention (4-bit KV cache ...)":
+ *                smoothing keys by a per-channel factor and folding it into the query.
+ *
+ * Numerics (fixed here where the pages leave them open):
+ *   block scale S_b = E4M3FN round-to-nearest-even of the exact A_b/(6 g), saturating at 448;
+ *   element code  = E2M1 round-to-nearest-even (ties to the even code) of the exact
+ *                   |y|/(sigma_b g), saturating at 6; a zero magnitude is stored as code 0;
+ *   g = amax/2688 from calibration (1 when amax = 0); keys are multiplied by r = fl32(1/s)
+ *   before quantisation, queries by s; the Hadamard key basis is the unnormalised Sylvester
+ *   butterfly in fp32, stages h = 1,2,..,64, applied after smoothing; the query side carries
+ *   the exact 1/128.  V is never transformed.
+ *
+ * Conventions for every entry point:
+ *   - All buffers are DEVICE memory owned by the caller.  The library allocates nothing,
+ *     keeps no mutable global state except a thread-local last-error string, never
+ *     synchronises, and enqueues its kernels on `stream` (a hipStream_t passed as void*;
+ *     NULL = the legacy default stream).
+ *   - Argument errors are detected on the host and returned BEFORE any HIP call, so they can
+ *     be exercised on a machine without a GPU.  HIP failures return NVKV_ERR_HIP; the text is
+ *     in nvkv_last_error().
+ *   - Device-side data the host cannot see (slot numbers, page-table entries, sequence
+ *     lengths) is range-checked by the kernels: out-of-range rows are skipped, never written.
+ *   - head_dim is fixed at 128.  Non-finite K/V/Q inputs give unspecified results.
+ *
+ * Cache layout of one layer (page_size tokens per page, multiple of 16; a contiguous cache is
+ * num_pages = batch with one page of max-context tokens per sequence):
+ *   NVFP4 codes   u8  [num_pages][Hkv][page_size][64]    (K and V alike)
+ *                 byte k of a row = element 2k in the low nibble | element 2k+1 in the high
+ *                 nibble; nibble = sign<<3 | E2M1 magnitude code.
+ *   NVFP4 scales  u8  [num_pages][Hkv][page_size/4][8][4] (K and V alike)
+ *                 the E4M3FN scale of block b (elements 16b..16b+15) of token t of a page is
+ *                 byte ((t/4)*8 + b)*4 + t%4 of that (page, head).
+ *   BF16 rows     u16 [num_pages][Hkv][page_size][128]   (keys only)
+ */
+#ifndef NVFP4KV_H
+#define NVFP4KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define NVKV_API __attribute__((visibility("default")))
+#else
+#define NVKV_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nvkv_status {
+  NVKV_OK = 0,
+  NVKV_ERR_NULL = 1,        /* a required pointer is NULL                                  */
+  NVKV_ERR_SHAPE = 2,       /* a count or size is out of range (<= 0, head_dim != 128, ...) */
+  NVKV_ERR_UNSUPPORTED = 3, /* a valid but unimplemented combination of formats/flags      */
+  NVKV_ERR_WORKSPACE = 4,   /* workspace missing, too small or not 256-byte aligned        */
+  NVKV_ERR_HIP = 5          /* a HIP runtime call failed (see nvkv_last_error)             */
+} nvkv_status;
+
+enum { NVKV_FMT_BF16 = 0, NVKV_FMT_NVFP4 = 1 };
+enum { NVKV_K_SMOOTH = 1u, NVKV_K_HADAMARD = 2u };
+enum { NVKV_PART_CODES = 0, NVKV_PART_SCALES = 1 };
+
+#define NVKV_HEAD_DIM 128
+#define NVKV_TENSOR_SCALE_DIVISOR 2688.0f /* 6 * 448: calibrated amax maps to 6 * E4M3 max */
+
+/* One layer of cache plus its static calibration state.  Pointers are device memory. */
+typedef struct nvkv_layer {
+  int32_t num_kv_heads;       /* Hkv >= 1                                                  */
+  int32_t head_dim;           /* must be 128                                               */
+  int32_t page_size;          /* tokens per page, a positive multiple of 16                */
+  int32_t num_pages;          /* pages in k_data / v_data                                  */
+  int32_t k_fmt;              /* NVKV_FMT_NVFP4 or NVKV_FMT_BF16                           */
+  int32_t v_fmt;              /* NVKV_FMT_NVFP4                                            */
+  uint32_t k_flags;           /* NVKV_K_SMOOTH | NVKV_K_HADAMARD; 0 for BF16 keys          */
+  int32_t reserved;           /* must be 0                                                 */
+  void *k_data;               /* NVFP4 codes or BF16 rows, layout above                    */
+  void *v_data;               /* NVFP4 codes                                               */
+  uint8_t *k_scales;          /* NVFP4 scales (NULL for BF16 keys)                         */
+  uint8_t *v_scales;          /* NVFP4 scales                                              */
+  const float *k_smooth;      /* s [Hkv][128]: query side; required when NVKV_K_SMOOTH     */
+  const float *k_inv_smooth;  /* r [Hkv][128] = fl32(1/s): key side; required with SMOOTH  */
+  const float *global_scale;  /* [2] = {g_K, g_V}; g_K unused for BF16 keys                */
+} nvkv_layer;
+
+/*
+ * Static calibration ([cache post] cache-config table, smoothing rows; [OSFP4] section 3).
+ *   k_win, v_win: bf16 [W][T][Hkv][128] calibration windows (either may be NULL, not both).
+ *   From k_win:  s[h][j] = fl32(sqrt(a)), a = max |k| over all windows and positions t >= 1
+ *                (t >= 0 when exclude_pos0 == 0); s = 1 where a = 0.  r = fl32(1/s).
+ *                g_out[0] = fl32(A_K / 2688), A_K = max |y| over every window, position
+ *                (including 0) and head of the keys transformed as selected by k_flags
+ *                (smoothing by r, then the Hadamard butterfly); 1 when A_K = 0.
+ *   From v_win:  g_out[1] = fl32(A_V / 2688), A_V = max |v|; 1 when A_V = 0.
+ *   s_out, r_out: fp32 [Hkv][128] (needed when k_win != NULL); g_out: fp32 [2].  Entries whose
+ *   input is NULL are left untouched.  s_out and g_out double as the reduction buffers, so
+ *   they must not alias the inputs.  W >= 1, T >= 1, Hkv >= 1.
+ */
+NVKV_API nvkv_status nvkv_calibrate_key_smoothing(const uint16_t *k_win, const uint16_t *v_win,
+                                         int32_t W, int32_t T, int32_t Hkv,
+                                         int32_t exclude_pos0, uint32_t k_flags,
+                                         float *s_out, float *r_out, float *g_out,
+                                         void *stream);
+
+/*
+ * Quantise-and-append ([cache post] opening paragraph and table; [OSFP4] sections 1, 3 and
+ * appendix D.1).  k_new, v_new: bf16 [N][Hkv][128] post-RoPE rows of N new tokens.
+ * slot_mapping: int32 [N], device; slot = page * page_size + offset.  Rows whose slot is
+ * negative or >= num_pages * page_size are skipped.  Keys are transformed per
+ * layer->k_flags (NVFP4 keys) and encoded with g_K; values with g_V; BF16 keys are copied.
+ * Each written row replaces the previous contents of its slot.  N >= 0 (N = 0 is a no-op).
+ */
+NVKV_API nvkv_status nvkv_quantize_append_kv(const nvkv_layer *layer,
+                                    const uint16_t *k_new, const uint16_t *v_new,
+                                    const int32_t *slot_mapping, int32_t N, void *stream);
+
+/*
+ * Workspace needed by nvkv_decode_attention_nvfp4 for the same (B, Hq, Hkv, max_seq_len,
+ * split_tokens).  split_tokens = 0 selects the library's own split size; otherwise it must
+ * be a positive multiple of 32 (tokens handled by one workgroup).  Returns 0 for invalid arguments.
+ */
+NVKV_API size_t nvkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len,
+                                   int32_t split_tokens);
+
+/*
+ * Fused GQA decode attention over the packed cache ([cache post]: attention over the
+ * quantised post-RoPE cache; [QServe rec]: the smoothing factor folded into the query).
+ *   q:          bf16 [B][Hq][128], post-RoPE, untransformed (the library applies q*s and
+ *               the 1/128-normalised Hadamard as layer->k_flags select).
+ *   page_table: int32 [B][max_pages_per_seq], device; token t of sequence b lives in page
+ *               page_table[b][t / page_size] at offset t % page_size.
+ *   seq_lens:   int32 [B], device; tokens already in the cache (the current token is
+ *               appended before this call).  Attention covers tokens [0, seq_lens[b]) with
+ *               no mask; seq_lens[b] = 0 gives a zero output row.  Lengths above
+ *               min(max_seq_len, max_pages_per_seq * page_size) are clamped to it.
+ *   Query head hq reads KV head hq / (Hq / Hkv); Hq must be 4 * Hkv.
+ *   out:        fp32 [B][Hq][128] = softmax(sm_scale * q' . k_hat) v_hat.
+ *   workspace:  device scratch of at least nvkv_decode_workspace_bytes(...) bytes, 256-byte
+ *               aligned; its contents need no initialisation and are clobbered.
+ */
+NVKV_API nvkv_status nvkv_decode_attention_nvfp4(const nvkv_layer *layer,
+                                        const uint16_t *q, int32_t B, int32_t Hq,
+                                        const int32_t *page_table, int32_t max_pages_per_seq,
+                                        const int32_t *seq_lens, int32_t max_seq_len,
+                                        float sm_scale, float *out,
+                                        void *workspace, size_t workspace_bytes,
+                                        int32_t split_tokens, void *stream);
+
+/* Bytes of one cache array of one layer: fmt NVKV_FMT_*, part NVKV_PART_*; 0 if invalid
+ * (including a BF16 scales array, which does not exist). */
+NVKV_API size_t nvkv_cache_array_bytes(int32_t fmt, int32_t part, int32_t num_pages, int32_t Hkv,
+                              int32_t page_size);
+
+/* Bytes per cached token across `layers` layers ([cache post] closing paragraph gives the
+ * BF16 figure 144 KiB/token for 36 layers x 8 KV heads x 128). */
+NVKV_API size_t nvkv_cache_bytes_per_token(int32_t k_fmt, int32_t v_fmt, int32_t Hkv, int32_t layers);
+
+NVKV_API const char *nvkv_status_string(nvkv_status status);
+NVKV_API const char *nvkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4KV_H */

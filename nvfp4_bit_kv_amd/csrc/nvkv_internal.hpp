@@ -1,0 +1,29 @@
+// Internal declarations shared by the C ABI layer and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/nvfp4kv.h"
+
+namespace nvkv {
+
+hipError_t launch_quantize_append(const nvkv_layer& L, const uint16_t* k_new, const uint16_t* v_new,
+                                  const int32_t* slots, int32_t N, hipStream_t stream);
+
+hipError_t launch_calibrate(const uint16_t* k_win, const uint16_t* v_win, int32_t W, int32_t T, int32_t hkv,
+                            int32_t exclude_pos0, uint32_t k_flags, float* s_out, float* r_out, float* g_out,
+                            hipStream_t stream);
+
+// Decode split plan: number of splits and tokens per split for a call.
+struct DecodePlan {
+  int32_t split_tokens;   // tokens handled by one workgroup (multiple of 32)
+  int32_t n_splits;       // workgroups per (sequence, KV head)
+};
+DecodePlan plan_decode(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t split_tokens);
+size_t decode_workspace_bytes(int32_t B, int32_t Hkv, const DecodePlan& plan);
+
+hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, int32_t B, int32_t Hq, const int32_t* page_table,
+                         int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                         float* out, void* workspace, const DecodePlan& plan, hipStream_t stream);
+
+}  // namespace nvkv

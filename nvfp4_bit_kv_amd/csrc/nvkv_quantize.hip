@@ -1,0 +1,203 @@
+// Quantise/append and calibration kernels (gfx950).  Compiled with -ffp-contract=off.
+//
+// [cache post] = rstation.ai post "NVFP4 attention cache on W4A4 Qwen3-8B: static key
+// smoothing is near-lossless, key rotations hurt": post-RoPE keys/values are quantised to
+// NVFP4 in 16-blocks along head_dim (opening paragraph); keys are smoothed per channel by
+// sqrt(absmax) calibrated on 4 windows without position 0, optionally in a Hadamard-128 basis
+// (cache-config table).  [OSFP4] = paperlayer.ai summary of arXiv 2610.08231v1: the global
+// scale is static and calibration-based so blocks can be quantised as they arrive (section 3).
+//
+// Thread layout of every row kernel: 8 lanes per 128-element row, one 16-element block per
+// lane, 8 rows per wavefront, 4 wavefronts (32 rows) per workgroup.  Rows are independent;
+// the only cross-lane traffic is the Hadamard butterfly's three block-pair stages.
+#include "nvkv_encode.hpp"
+#include "nvkv_internal.hpp"
+
+namespace nvkv {
+
+constexpr int kRowsPerWg = 32;
+
+struct AppendArgs {
+  const uint16_t* src;        // bf16 [N][Hkv][128]
+  const int32_t* slots;       // [N]
+  int32_t n_rows;             // N * Hkv
+  int32_t hkv;
+  int32_t page_size;
+  int64_t max_slot;           // num_pages * page_size
+  uint8_t* codes;             // NVFP4 codes or BF16 rows
+  uint8_t* scales;            // NVFP4 scales (unused for BF16)
+  const float* inv_smooth;    // r [Hkv][128]
+  const float* gscale;        // &g_K or &g_V
+  uint32_t flags;             // key transform flags (0 for V)
+  int32_t fmt;                // NVKV_FMT_*
+};
+
+struct AppendPair {
+  AppendArgs a[2];            // [0] = keys, [1] = values
+  int32_t wg_k;               // workgroups that serve keys
+};
+
+__global__ void __launch_bounds__(256) k_quantize_append(AppendPair p) {
+  const int which = (static_cast<int>(blockIdx.x) >= p.wg_k) ? 1 : 0;
+  const AppendArgs a = which ? p.a[1] : p.a[0];   // uniform select, no dynamic indexing
+  const int wg = static_cast<int>(blockIdx.x) - (which ? p.wg_k : 0);
+  const int lane = threadIdx.x & 63;
+  const int blk = lane & 7;
+  const int row = wg * kRowsPerWg + (threadIdx.x >> 3);
+  if (row >= a.n_rows) return;                      // whole 8-lane row groups leave together
+  const int n = row / a.hkv;
+  const int h = row - n * a.hkv;
+  const int32_t slot = a.slots[n];
+  if (slot < 0 || static_cast<int64_t>(slot) >= a.max_slot) return;
+  const int32_t page = slot / a.page_size;
+  const int32_t off = slot - page * a.page_size;
+  const int64_t row_index = (static_cast<int64_t>(page) * a.hkv + h) * a.page_size + off;
+
+  float y[kBlock];
+  uint4 raw0, raw1;
+  load_block_bf16(a.src + static_cast<int64_t>(row) * kHeadDim + blk * kBlock, y, raw0, raw1);
+
+  if (a.fmt == 0) {  // BF16 keys: plain copy of the row
+    uint4* dst = reinterpret_cast<uint4*>(a.codes + row_index * (kHeadDim * 2) + blk * 32);
+    dst[0] = raw0;
+    dst[1] = raw1;
+    return;
+  }
+  if (a.flags & 1u) smooth_block(y, a.inv_smooth + h * kHeadDim + blk * kBlock);
+  if (a.flags & 2u) hadamard_row(y, blk);
+
+  uint32_t lo, hi;
+  const uint32_t S = encode_block(y, *a.gscale, lo, hi);
+  *reinterpret_cast<uint2*>(a.codes + row_index * 64 + blk * 8) = make_uint2(lo, hi);
+  const int64_t sbase = (static_cast<int64_t>(page) * a.hkv + h) * a.page_size * 8;
+  a.scales[sbase + ((off >> 2) * 8 + blk) * 4 + (off & 3)] = static_cast<uint8_t>(S);
+}
+
+// ---------------------------------------------------------------------------------------
+// Calibration.  Max reductions over non-negative fp32 use unsigned atomicMax on the bit
+// patterns (order-preserving, deterministic).  s_out and g_out serve as the reduction
+// buffers and are rewritten in place by the finalise kernels.
+// ---------------------------------------------------------------------------------------
+__global__ void k_calib_clear(uint32_t* s_bits, int n, uint32_t* g_bits, int clear_gk, int clear_gv) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) s_bits[i] = 0u;
+  if (i == 0) {
+    if (clear_gk) g_bits[0] = 0u;
+    if (clear_gv) g_bits[1] = 0u;
+  }
+}
+
+constexpr int kCalibTokChunk = 32;
+
+// grid: (ceil(T / 32), W); each thread owns channel pairs c2 = tid, tid+256, ...
+__global__ void __launch_bounds__(256) k_calib_channel_absmax(const uint16_t* __restrict__ k_win, int T,
+                                                              int hkv, int t_begin, uint32_t* s_bits) {
+  const int C2 = hkv * kHeadDim / 2;
+  const int w = blockIdx.y;
+  const int t0 = max(static_cast<int>(blockIdx.x) * kCalibTokChunk, t_begin);
+  const int t1 = min(static_cast<int>(blockIdx.x + 1) * kCalibTokChunk, T);
+  const uint32_t* base = reinterpret_cast<const uint32_t*>(k_win) + static_cast<int64_t>(w) * T * C2;
+  for (int c2 = threadIdx.x; c2 < C2; c2 += blockDim.x) {
+    float m0 = 0.0f, m1 = 0.0f;
+    for (int t = t0; t < t1; ++t) {
+      const uint32_t v = base[static_cast<int64_t>(t) * C2 + c2];
+      m0 = fmaxf(m0, fabsf(bf16_to_f32(v & 0xFFFFu)));
+      m1 = fmaxf(m1, fabsf(bf16_to_f32(v >> 16)));
+    }
+    if (t0 < t1) {
+      atomicMax(&s_bits[2 * c2], __float_as_uint(m0));
+      atomicMax(&s_bits[2 * c2 + 1], __float_as_uint(m1));
+    }
+  }
+}
+
+// s = fl32(sqrt(a)) (1 where a = 0), r = fl32(1/s); both correctly rounded.
+__global__ void k_calib_finalize_sr(float* s_out, float* r_out, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float a = __uint_as_float(reinterpret_cast<uint32_t*>(s_out)[i]);
+  const float s = (a == 0.0f) ? 1.0f : sqrt_rn_f32(a);
+  s_out[i] = s;
+  r_out[i] = div_rn_f32(1.0f, s);
+}
+
+// Row absmax of the transformed keys (all positions) or the raw values; one atomic per
+// 8-row group.  Rows: W*T*Hkv.
+__global__ void __launch_bounds__(256) k_calib_transform_amax(const uint16_t* __restrict__ src, int64_t n_rows,
+                                                              int hkv, const float* __restrict__ r,
+                                                              uint32_t flags, uint32_t* g_bits) {
+  const int lane = threadIdx.x & 63;
+  const int blk = lane & 7;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerWg + (threadIdx.x >> 3);
+  if (row >= n_rows) return;
+  const int h = static_cast<int>(row % hkv);
+  float y[kBlock];
+  uint4 raw0, raw1;
+  load_block_bf16(src + row * kHeadDim + blk * kBlock, y, raw0, raw1);
+  if (flags & 1u) smooth_block(y, r + h * kHeadDim + blk * kBlock);
+  if (flags & 2u) hadamard_row(y, blk);
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kBlock; ++i) m = fmaxf(m, fabsf(y[i]));
+  m = fmaxf(m, xor_lanes(m, 1));
+  m = fmaxf(m, xor_lanes(m, 2));
+  m = fmaxf(m, xor_lanes(m, 4));
+  if (blk == 0) atomicMax(g_bits, __float_as_uint(m));
+}
+
+// g = fl32(A / 2688) (1 where A = 0), correctly rounded.
+__global__ void k_calib_finalize_g(float* g_out, int do_k, int do_v) {
+  const int i = threadIdx.x;
+  if (i > 1 || (i == 0 && !do_k) || (i == 1 && !do_v)) return;
+  const float A = __uint_as_float(reinterpret_cast<uint32_t*>(g_out)[i]);
+  g_out[i] = (A == 0.0f) ? 1.0f : div_rn_f32(A, 2688.0f);
+}
+
+// ---------------------------------------------------------------------------------------
+// Host launchers (argument validation happens in the C ABI layer before these run).
+// ---------------------------------------------------------------------------------------
+hipError_t launch_quantize_append(const nvkv_layer& L, const uint16_t* k_new, const uint16_t* v_new,
+                                  const int32_t* slots, int32_t N, hipStream_t stream) {
+  AppendPair p{};
+  const int32_t rows = N * L.num_kv_heads;
+  const int64_t max_slot = static_cast<int64_t>(L.num_pages) * L.page_size;
+  p.a[0] = AppendArgs{k_new, slots, rows, L.num_kv_heads, L.page_size, max_slot,
+                      static_cast<uint8_t*>(L.k_data), L.k_scales, L.k_inv_smooth,
+                      L.global_scale + 0, L.k_fmt == NVKV_FMT_NVFP4 ? L.k_flags : 0u, L.k_fmt};
+  p.a[1] = AppendArgs{v_new, slots, rows, L.num_kv_heads, L.page_size, max_slot,
+                      static_cast<uint8_t*>(L.v_data), L.v_scales, nullptr,
+                      L.global_scale + 1, 0u, L.v_fmt};
+  const int wg = (rows + kRowsPerWg - 1) / kRowsPerWg;
+  p.wg_k = wg;
+  hipLaunchKernelGGL(k_quantize_append, dim3(2 * wg), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_calibrate(const uint16_t* k_win, const uint16_t* v_win, int32_t W, int32_t T, int32_t hkv,
+                            int32_t exclude_pos0, uint32_t k_flags, float* s_out, float* r_out, float* g_out,
+                            hipStream_t stream) {
+  const int C = hkv * kHeadDim;
+  uint32_t* s_bits = reinterpret_cast<uint32_t*>(s_out);
+  uint32_t* g_bits = reinterpret_cast<uint32_t*>(g_out);
+  const int do_k = k_win != nullptr, do_v = v_win != nullptr;
+  hipLaunchKernelGGL(k_calib_clear, dim3((C + 255) / 256), dim3(256), 0, stream, s_bits, do_k ? C : 0, g_bits,
+                     do_k, do_v);
+  const int64_t rows = static_cast<int64_t>(W) * T * hkv;
+  const int64_t wg_rows = (rows + kRowsPerWg - 1) / kRowsPerWg;
+  if (do_k) {
+    const int t_begin = exclude_pos0 ? 1 : 0;
+    hipLaunchKernelGGL(k_calib_channel_absmax, dim3((T + kCalibTokChunk - 1) / kCalibTokChunk, W), dim3(256), 0,
+                       stream, k_win, T, hkv, t_begin, s_bits);
+    hipLaunchKernelGGL(k_calib_finalize_sr, dim3((C + 255) / 256), dim3(256), 0, stream, s_out, r_out, C);
+    hipLaunchKernelGGL(k_calib_transform_amax, dim3(static_cast<unsigned>(wg_rows)), dim3(256), 0, stream, k_win,
+                       rows, hkv, r_out, k_flags, g_bits + 0);
+  }
+  if (do_v) {
+    hipLaunchKernelGGL(k_calib_transform_amax, dim3(static_cast<unsigned>(wg_rows)), dim3(256), 0, stream, v_win,
+                       rows, hkv, nullptr, 0u, g_bits + 1);
+  }
+  hipLaunchKernelGGL(k_calib_finalize_g, dim3(1), dim3(64), 0, stream, g_out, do_k, do_v);
+  return hipGetLastError();
+}
+
+}  // namespace nvkv

@@ -115,3 +115,51 @@ CONFIGS = {
     "prefill": dict(cfg=3, layers=36, B=16, T=8192, hkv=8, hq=32, kind="lognormal", Tw=2048),
     "long":    dict(cfg=4, layers=36, B=64, T=32768, hkv=8, hq=32, kind="outlier", Tw=2048),
 }
+
+
+# ----------------------------------------------------------------------------------------
+# Device-side generation of the same distributions for workloads too large to build on the
+# host (seeded torch generator per layer; values differ from the NumPy stream, the
+# distribution and structure are the same).
+# ----------------------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def make_keys_device(kind: str, cfg: int, layer: int, B: int, T: int, hkv: int, sink: bool = True,
+                     role: int = ROLE_K, t_offset: int = 0, seed_index: int = 0, d: int = HEAD_DIM):
+    """Keys bf16 [B][T][Hkv][D] on the current GPU; positions t_offset .. t_offset+T-1."""
+    torch = _torch()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed_of(cfg, role, layer, seed_index))
+    sc = torch.from_numpy(channel_scales(kind, cfg, layer, hkv, d).astype(np.float32)).cuda()
+    x = torch.randn((B, T, hkv, d), generator=gen, device="cuda", dtype=torch.float32) * sc
+    if kind == "lognormal":
+        half = d // 2
+        inv = torch.pow(torch.tensor(1e6, dtype=torch.float64),
+                        -torch.arange(half, dtype=torch.float64) * 2.0 / d).cuda()
+        pos = torch.arange(t_offset, t_offset + T, dtype=torch.float64, device="cuda")
+        ang = (pos[:, None] * inv[None, :])
+        c = torch.cos(ang).float()[None, :, None, :]
+        s = torch.sin(ang).float()[None, :, None, :]
+        x1, x2 = x[..., :half], x[..., half:]
+        x = torch.cat([x1 * c - x2 * s, x2 * c + x1 * s], dim=-1)
+    if sink and t_offset == 0 and T > 0:
+        x[:, 0] *= 40.0
+    return x.to(torch.bfloat16)
+
+
+def make_values_device(cfg: int, layer: int, B: int, T: int, hkv: int, role: int = ROLE_V,
+                       seed_index: int = 0, d: int = HEAD_DIM):
+    torch = _torch()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed_of(cfg, role, layer, seed_index))
+    return torch.randn((B, T, hkv, d), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+
+def make_queries_device(cfg: int, layer: int, B: int, hq: int, d: int = HEAD_DIM):
+    torch = _torch()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed_of(cfg, ROLE_Q, layer))
+    return torch.randn((B, hq, d), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)

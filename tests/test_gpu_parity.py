@@ -1,0 +1,306 @@
+"""GPU parity: the native library against the CPU oracle on the same seeded inputs.
+
+* calibration outputs s, r, g and packed codes / scales: bit-exact;
+* decode attention: max |err| <= 1e-3 * max|V_hat| over the layer's cache and per-(b, q-head)
+  relative L2 <= 1e-4 against the fp64 oracle.
+Workloads: the tiny reference (1 KV head, 4 query heads, context 256) and one Qwen3-8B-shaped
+layer (8 KV heads, 32 query heads, batch 4, context 2304); contiguous and 16-token paged
+caches with a shuffled page table; every key-transform combination; BF16 keys.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import nvfp4_oracle as O
+from synth import kv_inputs as S
+from tests import _pipeline as P
+from tests.conftest import gpu_available
+
+pytestmark = pytest.mark.gpu
+
+FLAG_SETS = [0, 1, 2, 3]
+ATOL_FRAC = 1e-3
+REL_L2 = 1e-4
+
+
+def gpu_calibrate(nk, kw, vw, hkv, flags, exclude_pos0=True):
+    W, Tw = kw.shape[0], kw.shape[1]
+    s = torch.empty((hkv, 128), dtype=torch.float32, device="cuda")
+    r = torch.empty_like(s)
+    g = torch.empty(2, dtype=torch.float32, device="cuda")
+    nk.calibrate_key_smoothing(P.to_dev_u16(kw), P.to_dev_u16(vw), W, Tw, hkv, exclude_pos0, flags, s, r, g)
+    torch.cuda.synchronize()
+    return s, r, g
+
+
+def gpu_fill_cache(nk, k, v, hkv, flags, pages, s, r, g, k_fmt=1, chunk=None):
+    """Append every token of every sequence; returns the CacheLayer."""
+    B, T = k.shape[0], k.shape[1]
+    cache = nk.CacheLayer(pages.num_pages, pages.page_size, hkv, k_fmt=k_fmt, k_flags=flags if k_fmt == 1 else 0)
+    cache.smooth.copy_(s)
+    cache.inv_smooth.copy_(r)
+    cache.gscale.copy_(g)
+    L = cache.struct()
+    slots = np.concatenate([pages.slots(b, 0, T) for b in range(B)])
+    kk = k.reshape(B * T, hkv, 128)
+    vv = v.reshape(B * T, hkv, 128)
+    step = chunk or B * T
+    for i in range(0, B * T, step):
+        nk.quantize_append_kv(L, P.to_dev_u16(kk[i:i + step]), P.to_dev_u16(vv[i:i + step]),
+                              P.to_dev_i32(slots[i:i + step]), min(step, B * T - i))
+    torch.cuda.synchronize()
+    return cache
+
+
+def oracle_layer(k, v, kw, vw, flags, exclude_pos0=True):
+    kwf, vwf = S.bf16_to_f32(kw), S.bf16_to_f32(vw)
+    s, r, g = O.calibrate(kwf, vwf, exclude_pos0=exclude_pos0, k_flags=flags)
+    y = O.key_transform(S.bf16_to_f32(k), r[None, None], flags)
+    kc, ks = O.quantize_rows(y, g[0])
+    vc, vs = O.quantize_rows(S.bf16_to_f32(v), g[1])
+    return s, r, g, kc, ks, vc, vs
+
+
+@pytest.mark.parametrize("name", ["tiny", "layer"])
+@pytest.mark.parametrize("flags", FLAG_SETS)
+def test_calibrate_bit_exact(lib, name, flags):
+    c, k, v, kw, vw, q = P.workload(name)
+    for excl in (True, False):
+        s, r, g = gpu_calibrate(lib, kw, vw, c["hkv"], flags, excl)
+        so, ro, go = O.calibrate(S.bf16_to_f32(kw), S.bf16_to_f32(vw), exclude_pos0=excl, k_flags=flags)
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+        assert np.array_equal(r.cpu().numpy().view(np.uint32), ro.view(np.uint32))
+        assert np.array_equal(g.cpu().numpy().view(np.uint32), go.view(np.uint32)), (g, go)
+
+
+@pytest.mark.parametrize("name", ["tiny", "layer"])
+@pytest.mark.parametrize("flags", FLAG_SETS)
+@pytest.mark.parametrize("paged", [False, True])
+def test_quantize_bit_exact(lib, name, flags, paged):
+    c, k, v, kw, vw, q = P.workload(name)
+    s, r, g = gpu_calibrate(lib, kw, vw, c["hkv"], flags)
+    so, ro, go, kc, ks, vc, vs = oracle_layer(k, v, kw, vw, flags)
+    assert np.array_equal(g.cpu().numpy(), go)
+    pages = P.Pages(c["B"], c["T"], paged)
+    cache = gpu_fill_cache(lib, k, v, c["hkv"], flags, pages, s, r, g, chunk=1000 if name == "layer" else None)
+    kd, ksd = cache.k_data.cpu().numpy(), cache.k_scales.cpu().numpy()
+    vd, vsd = cache.v_data.cpu().numpy(), cache.v_scales.cpu().numpy()
+    for b in range(c["B"]):
+        gc, gs = P.rows_from_cache_vec(kd, ksd, pages, c["hkv"], b, c["T"])
+        assert np.array_equal(gs, ks[b]), f"K scales differ, seq {b}"
+        assert np.array_equal(gc, kc[b]), f"K codes differ, seq {b}"
+        gc, gs = P.rows_from_cache_vec(vd, vsd, pages, c["hkv"], b, c["T"])
+        assert np.array_equal(gs, vs[b]), f"V scales differ, seq {b}"
+        assert np.array_equal(gc, vc[b]), f"V codes differ, seq {b}"
+
+
+def oracle_decode(q, so, flags, kc, ks, vc, vs, go, seq_lens, hkv, k_bf16=None):
+    B, Hq = q.shape[0], q.shape[1]
+    grp = Hq // hkv
+    qf = S.bf16_to_f32(q).astype(np.float64)
+    if k_bf16 is None:
+        s_per_q = np.repeat(so, grp, axis=0)[None]               # [1][Hq][128]
+        qp = O.query_transform(qf, s_per_q, flags)
+        khat = [O.dequantize(kc[b], ks[b], go[0]) for b in range(B)]
+    else:
+        qp = qf
+        khat = [S.bf16_to_f32(k_bf16[b]).astype(np.float64) for b in range(B)]
+    vhat = [O.dequantize(vc[b], vs[b], go[1]) for b in range(B)]
+    out = O.attention(qp, khat, vhat, seq_lens, P.sm_scale())
+    vmax = max(float(np.abs(vh).max()) for vh in vhat)
+    return out, vmax
+
+
+def gpu_decode(nk, cache, q, pages, seq_lens, max_seq_len, split_tokens=0):
+    B, Hq = q.shape[0], q.shape[1]
+    out = torch.full((B, Hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    wsb = nk.decode_workspace_bytes(B, Hq, cache.hkv, max_seq_len, split_tokens)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
+    nk.decode_attention_nvfp4(cache.struct(), P.to_dev_u16(q), B, Hq, P.to_dev_i32(pages.table),
+                              pages.table.shape[1], P.to_dev_i32(np.asarray(seq_lens)), max_seq_len, P.sm_scale(),
+                              out, ws, wsb, split_tokens)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def assert_close(got, ref, vmax, seq_lens):
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - ref)
+    assert err.max() <= ATOL_FRAC * vmax, f"max abs err {err.max():.3e} > {ATOL_FRAC * vmax:.3e}"
+    for b in range(ref.shape[0]):
+        if seq_lens[b] == 0:
+            assert np.all(got[b] == 0)
+            continue
+        num = np.linalg.norm(got[b] - ref[b], axis=-1)
+        den = np.linalg.norm(ref[b], axis=-1)
+        rel = num / np.maximum(den, 1e-30)
+        assert rel.max() <= REL_L2, f"seq {b}: rel L2 {rel.max():.3e} > {REL_L2}"
+
+
+@pytest.mark.parametrize("name", ["tiny", "layer"])
+@pytest.mark.parametrize("flags", FLAG_SETS)
+@pytest.mark.parametrize("paged", [False, True])
+def test_decode_parity(lib, name, flags, paged):
+    c, k, v, kw, vw, q = P.workload(name)
+    s, r, g = gpu_calibrate(lib, kw, vw, c["hkv"], flags)
+    so, ro, go, kc, ks, vc, vs = oracle_layer(k, v, kw, vw, flags)
+    pages = P.Pages(c["B"], c["T"], paged)
+    cache = gpu_fill_cache(lib, k, v, c["hkv"], flags, pages, s, r, g)
+    seq = [c["T"]] * c["B"]
+    ref, vmax = oracle_decode(q, so, flags, kc, ks, vc, vs, go, seq, c["hkv"])
+    for split in (0, 32, 96, P.ceil_to(c["T"], 32)):
+        got = gpu_decode(lib, cache, q, pages, seq, c["T"], split)
+        assert_close(got, ref, vmax, seq)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_decode_ragged_and_empty_sequences(lib, paged):
+    c, k, v, kw, vw, q = P.workload("layer", T=300)
+    flags = 1
+    s, r, g = gpu_calibrate(lib, kw, vw, c["hkv"], flags)
+    so, ro, go, kc, ks, vc, vs = oracle_layer(k, v, kw, vw, flags)
+    pages = P.Pages(c["B"], c["T"], paged)
+    cache = gpu_fill_cache(lib, k, v, c["hkv"], flags, pages, s, r, g)
+    for seq in ([0, 1, 15, 16], [17, 31, 33, 300], [299, 0, 64, 65], [128, 129, 255, 257]):
+        ref, vmax = oracle_decode(q, so, flags, kc, ks, vc, vs, go, seq, c["hkv"])
+        for split in (0, 32, 64, 320):
+            got = gpu_decode(lib, cache, q, pages, seq, 300, split)
+            assert_close(got, ref, vmax, seq)
+
+
+def test_decode_split_invariance_and_determinism(lib):
+    c, k, v, kw, vw, q = P.workload("layer")
+    flags = 1
+    s, r, g = gpu_calibrate(lib, kw, vw, c["hkv"], flags)
+    pages = P.Pages(c["B"], c["T"], True)
+    cache = gpu_fill_cache(lib, k, v, c["hkv"], flags, pages, s, r, g)
+    seq = [c["T"]] * c["B"]
+    outs = [gpu_decode(lib, cache, q, pages, seq, c["T"], sp) for sp in (0, 32, 128, 512, 2304)]
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 1e-5 * np.max(np.abs(outs[0]))
+    a = gpu_decode(lib, cache, q, pages, seq, c["T"], 128)
+    b = gpu_decode(lib, cache, q, pages, seq, c["T"], 128)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_bf16_keys_nvfp4_values(lib, paged):
+    """The 'NVFP4 V only' cache configuration: keys stay bf16, values NVFP4."""
+    c, k, v, kw, vw, q = P.workload("layer")
+    s, r, g = gpu_calibrate(lib, kw, vw, c["hkv"], 0)
+    so, ro, go, kc, ks, vc, vs = oracle_layer(k, v, kw, vw, 0)
+    pages = P.Pages(c["B"], c["T"], paged)
+    cache = gpu_fill_cache(lib, k, v, c["hkv"], 0, pages, s, r, g, k_fmt=0)
+    kd = cache.k_data.cpu().numpy()
+    for b in range(c["B"]):
+        assert np.array_equal(P.bf16_rows_from_cache(kd, pages, c["hkv"], b, c["T"]), k[b])
+        gc, gs = P.rows_from_cache_vec(cache.v_data.cpu().numpy(), cache.v_scales.cpu().numpy(), pages,
+                                       c["hkv"], b, c["T"])
+        assert np.array_equal(gc, vc[b]) and np.array_equal(gs, vs[b])
+    seq = [c["T"], 1000, 17, 2048]
+    ref, vmax = oracle_decode(q, so, 0, kc, ks, vc, vs, go, seq, c["hkv"], k_bf16=k)
+    for split in (0, 64):
+        got = gpu_decode(lib, cache, q, pages, seq, c["T"], split)
+        assert_close(got, ref, vmax, seq)
+
+
+def test_special_rows_bit_exact(lib):
+    """Rows built to hit the codec's corner cases: zero and underflowing blocks (scale 0),
+    E4M3 subnormal scales, saturated scales, exact E2M1 midpoints, signed zeros."""
+    rng = np.random.default_rng(11)
+    hkv, N = 2, 96
+    g_val = np.float32(2.0 ** -7)
+    rows = (rng.standard_normal((N, hkv, 128)) * np.exp(rng.uniform(-6, 1, (N, hkv, 128)))).astype(np.float32)
+    rows[0, 0] = 0.0
+    rows[1, 0, :16] = 1e-20                                  # scale underflows to 0
+    rows[2, 0, :16] = 3e-4                                   # A/(6g) in the E4M3 subnormal range
+    rows[3, 0, :16] = 4e4                                    # saturates the scale (0x7E)
+    rows[4, 0, ::2] = -0.0
+    # exact E2M1 midpoints with a representable block scale: A = 6 * sigma * g, sigma = 3
+    unit = np.float32(3.0) * g_val
+    rows[5, 1, 0] = np.float32(18.0) * g_val
+    for i, m in enumerate([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]):
+        rows[5, 1, 1 + i] = np.float32(m) * unit
+    kbits = S.bf16_round(rows)
+    vbits = S.bf16_round(rows[::-1].copy())
+    k32, v32 = S.bf16_to_f32(kbits), S.bf16_to_f32(vbits)
+    assert np.array_equal(k32[5, 1, :8], rows[5, 1, :8])     # midpoints survive bf16 rounding
+    g = np.array([g_val, g_val], np.float32)
+    kc, ks = O.quantize_rows(k32, g[0])
+    vc, vs = O.quantize_rows(v32, g[1])
+    pages = P.Pages(1, N, True)
+    cache = lib.CacheLayer(pages.num_pages, pages.page_size, hkv, k_flags=0)
+    cache.gscale.copy_(torch.from_numpy(g))
+    lib.quantize_append_kv(cache.struct(), P.to_dev_u16(kbits), P.to_dev_u16(vbits),
+                           P.to_dev_i32(pages.slots(0, 0, N)), N)
+    torch.cuda.synchronize()
+    gc, gs = P.rows_from_cache_vec(cache.k_data.cpu().numpy(), cache.k_scales.cpu().numpy(), pages, hkv, 0, N)
+    assert np.array_equal(gs, ks) and np.array_equal(gc, kc)
+    gc, gs = P.rows_from_cache_vec(cache.v_data.cpu().numpy(), cache.v_scales.cpu().numpy(), pages, hkv, 0, N)
+    assert np.array_equal(gs, vs) and np.array_equal(gc, vc)
+    assert 0 in ks[:, 0, 0] and 0x7E in ks[:, 0, 0] and np.any((ks > 0) & (ks < 8))
+
+
+def test_append_canaries_and_skipped_slots(lib):
+    """Only the addressed slots change; negative and out-of-range slots write nothing."""
+    rng = np.random.default_rng(12)
+    hkv, N = 3, 40
+    pages = P.Pages(2, 64, True, spare=2)
+    cache = lib.CacheLayer(pages.num_pages, pages.page_size, hkv, k_flags=3, fill=0xA5)
+    cache.smooth.fill_(1.5)
+    cache.inv_smooth.copy_(torch.full_like(cache.smooth, 1 / 1.5))
+    cache.gscale.fill_(0.01)
+    before = [t.cpu().numpy().copy() for t in (cache.k_data, cache.k_scales, cache.v_data, cache.v_scales)]
+    k = S.bf16_round(rng.standard_normal((N, hkv, 128)).astype(np.float32))
+    v = S.bf16_round(rng.standard_normal((N, hkv, 128)).astype(np.float32))
+    slots = pages.slots(1, 5, 5 + N).copy()
+    slots[3] = -1
+    slots[7] = pages.num_pages * pages.page_size          # one past the end
+    slots[8] = 2 ** 31 - 1
+    lib.quantize_append_kv(cache.struct(), P.to_dev_u16(k), P.to_dev_u16(v), P.to_dev_i32(slots), N)
+    torch.cuda.synchronize()
+    after = [t.cpu().numpy() for t in (cache.k_data, cache.k_scales, cache.v_data, cache.v_scales)]
+    written = set(int(x) for i, x in enumerate(slots) if i not in (3, 7, 8))
+    ps = pages.page_size
+    for arr_b, arr_a, row_bytes, is_scale in zip(before, after, (64, 8, 64, 8), (False, True, False, True)):
+        if not is_scale:
+            b3 = arr_b.reshape(pages.num_pages, hkv, ps, row_bytes)
+            a3 = arr_a.reshape(pages.num_pages, hkv, ps, row_bytes)
+            for pg in range(pages.num_pages):
+                for off in range(ps):
+                    same = np.array_equal(b3[pg, :, off], a3[pg, :, off])
+                    assert same == ((pg * ps + off) not in written)
+        else:
+            b5 = arr_b.reshape(pages.num_pages, hkv, ps // 4, 8, 4)
+            a5 = arr_a.reshape(pages.num_pages, hkv, ps // 4, 8, 4)
+            for pg in range(pages.num_pages):
+                for off in range(ps):
+                    same = np.array_equal(b5[pg, :, off // 4, :, off % 4], a5[pg, :, off // 4, :, off % 4])
+                    if (pg * ps + off) not in written:
+                        assert same
+
+
+def test_error_paths_on_gpu_host(lib):
+    """Argument errors still come back as status codes with a GPU present."""
+    L = lib.Layer()
+    with pytest.raises(lib.NvkvError) as e:
+        lib.quantize_append_kv(L, None, None, None, 1)
+    assert e.value.status == 2
+
+
+def test_calibrate_rounding_wide_range(lib):
+    """s = fl32(sqrt(a)), r = fl32(1/s), g = fl32(A/2688) correctly rounded over absmax values
+    spanning many binades (one window, position 1 carries every channel's absmax)."""
+    rng = np.random.default_rng(21)
+    hkv = 64
+    kw = np.zeros((1, 2, hkv, 128), np.float32)
+    kw[0, 0] = 1e8                                           # position 0 is excluded
+    kw[0, 1] = rng.choice([-1, 1], (hkv, 128)) * np.exp(rng.uniform(-60, 60, (hkv, 128)))
+    kbits = S.bf16_round(kw)
+    vbits = S.bf16_round(rng.standard_normal((1, 2, hkv, 128)).astype(np.float32) * 3e-30)
+    for flags in (0, 1):
+        s, r, g = gpu_calibrate(lib, kbits, vbits, hkv, flags)
+        so, ro, go = O.calibrate(S.bf16_to_f32(kbits), S.bf16_to_f32(vbits), exclude_pos0=True, k_flags=flags)
+        assert np.array_equal(s.cpu().numpy(), so)
+        assert np.array_equal(r.cpu().numpy(), ro)
+        assert np.array_equal(g.cpu().numpy().view(np.uint32), go.view(np.uint32))
