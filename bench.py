@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--sweep-splits", default="",
+                    help="comma-separated split sizes: report the decode launch time of each")
     ap.add_argument("--profile-pass", action="store_true",
                     help="short run for rocprofv3: few steps, no CPU baseline")
     return ap.parse_args()
@@ -91,7 +93,7 @@ class Workload:
         self.k_new, self.v_new, self.q = [], [], []
         self.out = torch.empty((self.L, B, self.hq, 128), dtype=torch.float32, device=dev)
         self.wsb = nk.decode_workspace_bytes(B, self.hq, hkv, T, split_tokens)
-        self.ws = torch.empty(max(self.wsb, 256), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(max(self.wsb, 256), dtype=torch.uint8, device=dev)
         self._build()
 
     def _build(self):
@@ -148,7 +150,7 @@ class Workload:
         return self.B * self.hkv * self.T * per_tok + self.B * self.hq * (256 + 512)
 
     def append_bytes_per_layer(self):
-        return self.B * self.hkv * ((256 + row_bytes(self.k_fmt) if self.k_fmt else 512) + 256 + 72)
+        return self.B * self.hkv * ((256 + row_bytes(self.k_fmt)) + (256 + 72))
 
     def step_bytes(self):
         return self.L * (self.decode_bytes_per_layer() + self.append_bytes_per_layer())
@@ -176,23 +178,38 @@ def capture(torch, fn):
 
 
 def decode_launch_times(torch, wl, reps):
-    """Per-launch duration of decode_attention_nvfp4 from HIP events recorded on the launch
-    stream right before and after each call; a spin kernel holds the stream first so every
-    call is already queued when the GPU reaches it (no host-launch gaps inside a pair)."""
-    stream = torch.cuda.current_stream()
-    n = wl.L * reps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    torch.cuda._sleep(int(2e8))
-    i = 0
-    for r in range(reps):
-        cp = r % wl.copies
-        for l in range(wl.L):
-            ev[i][0].record(stream)
-            wl.layer_step(cp, l, decode_only=True)
-            ev[i][1].record(stream)
-            i += 1
+    """Average duration of one decode_attention_nvfp4 call (its kernels back to back, no host
+    gaps): a HIP graph of the decode calls of all layers of a cache copy is replayed between
+    two HIP events on the launch stream; one sample per replay, divided by the layer count."""
+    graphs = [capture(torch, lambda cp=cp: [wl.layer_step(cp, l, decode_only=True) for l in range(wl.L)])
+              for cp in range(wl.copies)]
+    for gr in graphs:
+        gr.replay()
     torch.cuda.synchronize()
-    return np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3    # seconds
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for r in range(reps):
+        ev[r][0].record(stream)
+        graphs[r % len(graphs)].replay()
+        ev[r][1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3 / wl.L     # seconds per call
+
+
+def sweep_splits(torch, wl, splits):
+    """Average decode launch time per split size (tuning aid, printed to stderr)."""
+    saved = (wl.split_tokens, wl.wsb, wl.ws)
+    res = {}
+    for sp in splits:
+        wl.split_tokens = sp
+        wl.wsb = wl.nk.decode_workspace_bytes(wl.B, wl.hq, wl.hkv, wl.T, sp)
+        wl.ws = torch.zeros(max(wl.wsb, 256), dtype=torch.uint8, device="cuda")
+        d = decode_launch_times(torch, wl, reps=10)
+        res[sp] = (float(np.mean(d)) * 1e6, float(np.min(d)) * 1e6)
+        print(f"[sweep] split_tokens={sp}: avg {res[sp][0]:.2f} us  min {res[sp][1]:.2f} us  "
+              f"-> {wl.decode_bytes_per_layer() / np.mean(d) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
+    wl.split_tokens, wl.wsb, wl.ws = saved
+    return res
 
 
 def check_against_oracle(wl):
@@ -297,11 +314,13 @@ def main():
     replay_ok = bool(torch.equal(wl.out, eager0))
 
     print("[bench] per-launch decode timing", file=sys.stderr, flush=True)
-    durs = decode_launch_times(torch, wl, reps=max(2, min(10, args.steps // 10)))
+    durs = decode_launch_times(torch, wl, reps=max(3, min(30, args.steps // 5)))
     avg_launch = float(np.mean(durs))
     dec_bytes = wl.decode_bytes_per_layer()
     achieved = dec_bytes / avg_launch / 1e9
 
+    if args.sweep_splits:
+        sweep_splits(torch, wl, [int(x) for x in args.sweep_splits.split(",")])
     check = None if args.no_check else check_against_oracle(wl)
     base = None if args.no_cpu_baseline else cpu_baseline(wl)
 
@@ -331,7 +350,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "decode_attention_nvfp4 (split-K decode + merge) per layer",
+            "kernel": "k_decode (decode_attention_nvfp4: split-K decode + in-kernel cross-split merge), per layer",
             "bytes_per_launch": dec_bytes, "avg_launch_us": round(avg_launch * 1e6, 3),
             "min_launch_us": round(float(np.min(durs)) * 1e6, 3),
         },

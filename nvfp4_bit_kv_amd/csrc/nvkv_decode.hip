@@ -7,9 +7,9 @@
 // the smoothing factor is folded into the query; attention is kept memory-bound so the 4-bit
 // cache pays off.
 //
-// Work decomposition: one workgroup (4 wavefronts) per (split, KV head, sequence); the split's
-// tokens are cut into 32-token iterations dealt round-robin to the 4 wavefronts.  Per
-// iteration a wavefront does:
+// Work decomposition: one workgroup (4..16 wavefronts) per (split, KV head, sequence); the
+// split's tokens are cut into 32-token iterations dealt round-robin to the wavefronts; the
+// plan aims at about one workgroup per CU.  Per iteration a wavefront does:
 //   QK  S^T[32 tok x 16 col] = Khat[32 x 128] Q'^T: 2 x 4 MFMA 16x16x32 f16.  Khat = code *
 //       sigma (exact in fp16); the 16 columns are (query head i, term t): the query is split
 //       into hi + lo fp16 terms (t = 0, 1; columns t = 2, 3 are zero) so the product keeps
@@ -22,11 +22,18 @@
 // for column c) is exactly the A-operand layout PV needs, so no transpose is required.
 // V codes are read token-major: lane (c, g) fetches the dword of dims 8c..8c+7 of its 8
 // tokens and serves column c of PV instruction v as dim 8c + v.
-// Dequantisation: nibble -> fp16 (value * 2^8) through a v_perm byte table, E4M3 scale ->
-// fp16 (sigma * 2^-8) by a bit shift, one v_pk_mul_f16 per element pair; the product is the
-// exact code * sigma.
+// Dequantisation: nibble -> fp16 (value * 2^8) with the gfx950 scaled FP4 convert (it
+// applies only the exponent of its scale operand, so the scale is 2^8), E4M3 scale -> fp16
+// (sigma * 2^-8) by a bit shift, one v_pk_mul_f16 per element pair; the product is the exact
+// code * sigma.
 // Partials (unnormalised O, running max m, sum l) are merged across wavefronts in LDS and,
-// when a sequence has several splits, across workgroups by k_decode_merge.
+// when a sequence has several splits, across workgroups by the last workgroup of the
+// (sequence, KV head) to finish: partials travel through device-coherent stores and loads
+// and one arrival counter per (sequence, KV head) in the workspace (reset by that
+// workgroup), so a single launch produces the output without any cache writeback.
+// Latency: the query row, page-table entries and the first two iterations' cache loads are
+// issued at kernel start, before the sequence length is known; later iterations are
+// software-pipelined two deep.
 #include "nvkv_device.hpp"
 #include "nvkv_internal.hpp"
 
@@ -38,7 +45,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kMaxWaves = 16;   // wavefronts per workgroup: 4..16 (runtime, blockDim.x / 64)
 constexpr int kIterTok = 32;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyMax = 8.0f;
@@ -56,6 +63,7 @@ struct DecodeArgs {
   float* out;                 // fp32 [B][Hq][128]
   float* ws_o;                // [B][Hkv][n_splits][4][128]
   float* ws_ml;               // [B][Hkv][n_splits][4][2]
+  unsigned* counters;         // [B][Hkv] arrival counters, zero between calls
   int32_t hkv, hq, page_size, num_pages, max_pages_per_seq, seq_cap;
   int32_t split_tokens, n_splits;
   uint32_t k_flags;
@@ -68,87 +76,379 @@ __device__ __forceinline__ float dpp_xor1(float x) {
 __device__ __forceinline__ float dpp_xor2(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
 }
-
-// fp16 high bytes of e2m1 magnitude * 256 for magnitude codes 0..7:
-// {0, 128, 256, 384, 512, 768, 1024, 1536} -> 0x00 0x58 0x5C 0x5E | 0x60 0x62 0x64 0x66.
-constexpr uint32_t kLutLo = 0x5E5C5800u;
-constexpr uint32_t kLutHi = 0x66646260u;
-
-// High bytes (sign included) of the fp16 images of the even / odd nibbles of a code dword.
-__device__ __forceinline__ void nibble_high_bytes(uint32_t d, uint32_t& even, uint32_t& odd) {
-  even = __builtin_amdgcn_perm(kLutHi, kLutLo, d & 0x07070707u) | ((d << 4) & 0x80808080u);
-  odd = __builtin_amdgcn_perm(kLutHi, kLutLo, (d >> 4) & 0x07070707u) | (d & 0x80808080u);
+// rotate right within a row of 16 lanes by 4 / 8 (with xor 1, 2 first: max over the row)
+__device__ __forceinline__ float dpp_row_ror4(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_row_ror8(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));
 }
 
-// [0x00, lo.byte k, 0x00, hi.byte k]: two fp16 values with zero low bytes.
-__device__ __forceinline__ uint32_t pair_bytes(uint32_t hi_src, uint32_t lo_src, int k) {
-  const uint32_t sel = 0x0Cu | (uint32_t(k) << 8) | (0x0Cu << 16) | (uint32_t(4 + k) << 24);
-  return __builtin_amdgcn_perm(hi_src, lo_src, sel);
+// Reductions over the four 16-lane rows (lanes l, l^16, l^32, l^48) with the gfx950 row-swap
+// permutes: pure VALU, so they never wait on outstanding scalar loads.
+__device__ __forceinline__ float rows_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
 __device__ __forceinline__ half2v as_half2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 __device__ __forceinline__ uint32_t as_u32(half2v h) { return __builtin_bit_cast(uint32_t, h); }
 
 // 8 key elements of one code dword (dims 8u..8u+7 relative) times the block scale pair.
+// The gfx950 scaled FP4 convert applies only the exponent of its f32 scale, so it is asked
+// for value * 2^8 (exact) and one packed f16 multiply by sigma * 2^-8 gives code * sigma.
+// Byte k (constant) of a code dword -> two fp16 values * 2^8.
+template <int K>
+__device__ __forceinline__ half2v fp4_pair_x256(uint32_t d) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 256.0f, K);
+}
+
 __device__ __forceinline__ half8 dequant_dword(uint32_t d, half2v sig2) {
-  uint32_t ev, od;
-  nibble_high_bytes(d, ev, od);
-  half8 r;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const half2v v = as_half2(pair_bytes(od, ev, k)) * sig2;
-    r[2 * k] = v[0];
-    r[2 * k + 1] = v[1];
-  }
-  return r;
+  const half2v v0 = fp4_pair_x256<0>(d) * sig2, v1 = fp4_pair_x256<1>(d) * sig2;
+  const half2v v2 = fp4_pair_x256<2>(d) * sig2, v3 = fp4_pair_x256<3>(d) * sig2;
+  return half8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
 }
 
 // E4M3 scale byte (masked to 7 bits) -> fp16 bits of sigma * 2^-8, duplicated in both halves.
 __device__ __forceinline__ half2v scale_pair_same(uint32_t s) { return as_half2((s & 0x7Fu) * 0x00800080u); }
 
+// Registers of one 32-token iteration, filled by issue_loads() well before they are used.
+template <bool KBF16> struct KLoads;
+template <> struct KLoads<false> {
+  u32x4 kc[2];          // codes of dims 32g..32g+31 of token (half eta, row c)
+  uint32_t ks[2][2];    // scale bytes of blocks 2g, 2g+1 of that token
+};
+template <> struct KLoads<true> {
+  u32x4 kr[2][4];       // bf16 dims 32g..32g+31 of token (half eta, row c)
+};
+template <bool KBF16> struct IterLoads {
+  KLoads<KBF16> k;
+  uint32_t vd[8];       // V code dwords (dims 8c..8c+7) of tokens T(g, e)
+  uint32_t vs[2];       // V scale dwords (4 tokens of quad g of each half, block c>>1)
+};
+
+struct HalfAddr {
+  int64_t kv_row;       // (page * Hkv + h) * ps + in-page offset of the half's first token
+  int64_t sc_base;      // byte base of the (page, head) scale array
+  int off16;
+  bool ok;              // page index in range
+};
+
+// Page-table entries of the two 16-token halves of an iteration (scalar loads, issued one
+// iteration before the cache loads that need them).  Tokens at or beyond t_hi are mapped
+// into [0, t_hi) so every access stays inside the sequence's pages.
+struct IterPages {
+  int32_t pg[2];
+  int off16[2];
+};
+
+__device__ __forceinline__ IterPages load_pages(const DecodeArgs& a, const int32_t* ptab, int t, int t_hi) {
+  IterPages r;
+#pragma unroll
+  for (int eta = 0; eta < 2; ++eta) {
+    int tb = t + 16 * eta;
+    if (tb >= t_hi) tb = (t_hi - 1) & ~15;
+    if (tb < 0) tb = 0;
+    r.pg[eta] = ptab[tb / a.page_size];
+    r.off16[eta] = tb % a.page_size;
+  }
+  return r;
+}
+
+__device__ __forceinline__ void half_addrs(const DecodeArgs& a, const IterPages& P, int h, HalfAddr (&ha)[2]) {
+#pragma unroll
+  for (int eta = 0; eta < 2; ++eta) {
+    const int32_t pg = P.pg[eta];
+    ha[eta].ok = static_cast<uint32_t>(pg) < static_cast<uint32_t>(a.num_pages);
+    const int64_t pgc = ha[eta].ok ? pg : 0;
+    ha[eta].off16 = P.off16[eta];
+    ha[eta].kv_row = (pgc * a.hkv + h) * a.page_size + P.off16[eta];
+    ha[eta].sc_base = (pgc * a.hkv + h) * a.page_size * 8;
+  }
+}
+
 template <bool KBF16>
-__global__ void __launch_bounds__(256) k_decode(DecodeArgs a) {
+__device__ __forceinline__ void issue_loads(const DecodeArgs& a, const HalfAddr (&ha)[2], int c, int g,
+                                            IterLoads<KBF16>& L) {
+#pragma unroll
+  for (int eta = 0; eta < 2; ++eta) {
+    const int64_t row = ha[eta].kv_row + c;
+    if constexpr (!KBF16) {
+      L.k.kc[eta] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.k_codes + row * 64 + 16 * g));
+      const int tok = ha[eta].off16 + c;
+      const uint8_t* sb = a.k_scales + ha[eta].sc_base + ((tok >> 2) * 8 + 2 * g) * 4 + (tok & 3);
+      L.k.ks[eta][0] = sb[0];
+      L.k.ks[eta][1] = sb[4];
+    } else {
+      const u32x4* kr = reinterpret_cast<const u32x4*>(a.k_codes + row * (kHeadDim * 2) + 64 * g);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) L.k.kr[eta][u] = __builtin_nontemporal_load(kr + u);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      L.vd[4 * eta + j] = __builtin_nontemporal_load(
+          reinterpret_cast<const uint32_t*>(a.v_codes + (ha[eta].kv_row + 4 * g + j) * 64 + 4 * c));
+    const int quad = (ha[eta].off16 >> 2) + g;
+    L.vs[eta] = *reinterpret_cast<const uint32_t*>(a.v_scales + ha[eta].sc_base + (quad * 8 + (c >> 1)) * 4);
+  }
+}
+
+// Online-softmax state of one wavefront.
+struct SoftmaxState {
+  float m_ref;          // lazy running max of the lane's head (base-2 units)
+  float l_acc;          // lane's share of the denominator
+  floatx4 acc[8];       // PV accumulators: rows (head g, term r), column c <-> dim 8c + v
+};
+
+// PV for dims 8c + 2K and 8c + 2K + 1 (instructions v = 2K, 2K + 1).
+template <int K>
+__device__ __forceinline__ void pv_pair(const uint32_t (&vd)[8], const half2v (&sig)[4], const half8& ap,
+                                        SoftmaxState& st) {
+  uint32_t xk[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) xk[e] = as_u32(fp4_pair_x256<K>(vd[e]));
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi) {
+    const uint32_t sel = hi ? 0x07060302u : 0x05040100u;   // high or low f16 half of each
+    u32x4 bw;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) bw[p] = as_u32(as_half2(__builtin_amdgcn_perm(xk[2 * p + 1], xk[2 * p], sel)) * sig[p]);
+    st.acc[2 * K + hi] =
+        __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(half8, bw), st.acc[2 * K + hi], 0, 0, 0);
+  }
+}
+
+template <bool KBF16>
+__device__ __forceinline__ void compute_iter(const IterLoads<KBF16>& L, const HalfAddr (&ha)[2], const u32x4 (&qb)[4],
+                                             float descale, int t0, int t_end, int c, int g, SoftmaxState& st) {
+  const int term = c & 3;
+  // ---- QK^T: rows = tokens (c), columns = (head, query term) ----
+  floatx4 sacc[2];
+#pragma unroll
+  for (int eta = 0; eta < 2; ++eta) {
+    sacc[eta] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (!KBF16) {
+      const half2v s0 = scale_pair_same(L.k.ks[eta][0]);
+      const half2v s1 = scale_pair_same(L.k.ks[eta][1]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const half8 ak = dequant_dword(L.k.kc[eta][u], u < 2 ? s0 : s1);
+        sacc[eta] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, __builtin_bit_cast(half8, qb[u]), sacc[eta], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        sacc[eta] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, L.k.kr[eta][u]),
+                                                             __builtin_bit_cast(bf16x8, qb[u]), sacc[eta], 0, 0, 0);
+    }
+  }
+  // ---- scores: sum the query terms of a head (columns 4i..4i+3), mask ragged tails ----
+  // A wave-uniform flag skips the masking when all 32 tokens are valid.
+  const bool full = (t0 + kIterTok <= t_end) && ha[0].ok && ha[1].ok;
+  float s[8];
+  float bmax = -INFINITY;
+#pragma unroll
+  for (int eta = 0; eta < 2; ++eta) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = sacc[eta][r];
+      x += dpp_xor1(x);
+      x += dpp_xor2(x);
+      if (!full) {
+        const bool ok = (t0 + 16 * eta + 4 * g + r) < t_end && ha[eta].ok;
+        x = ok ? x : -INFINITY;
+      }
+      s[4 * eta + r] = x;
+      bmax = fmaxf(bmax, x);
+    }
+  }
+  bmax = rows_max(bmax) * descale;              // descale > 0: max commutes with it
+  // ---- lazy running max: it moves only when a block max exceeds it by more than 8 ----
+  const bool need = bmax > st.m_ref + kLazyMax;
+  if (__any(need)) {
+    const float m_new = need ? bmax : st.m_ref;
+    const float alpha = exp2f(st.m_ref - m_new);          // 0 on the first block
+    st.m_ref = m_new;
+    st.l_acc *= alpha;
+    // PV rows of lane group g belong to head g, whose alpha sits in lane 4g
+    const float al0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0));
+    const float al1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 4));
+    const float al2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 8));
+    const float al3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 12));
+    const float alpha_row = g == 0 ? al0 : (g == 1 ? al1 : (g == 2 ? al2 : al3));
+#pragma unroll
+    for (int v = 0; v < 8; ++v) st.acc[v] *= alpha_row;
+  }
+  const float neg_m = (st.m_ref == -INFINITY) ? 0.0f : -st.m_ref;   // a fully masked block keeps p = 0
+  // p = 2^(s*descale - m) <= 256; A operand of PV: row term 0 = hi(p), term 1 = lo(p) =
+  // p - hi(p), terms 2, 3 = 0 (hi/lo by round-toward-zero packed converts: |p - hi - lo| <
+  // 2^-20 p).
+  u32x4 apw;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * k], descale, neg_m));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * k + 1], descale, neg_m));
+    st.l_acc += p0 + p1;
+    const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+    const half2v lo = __builtin_bit_cast(
+        half2v, __builtin_amdgcn_cvt_pkrtz(p0 - static_cast<float>(hi[0]), p1 - static_cast<float>(hi[1])));
+    apw[k] = term == 0 ? as_u32(hi) : (term == 1 ? as_u32(lo) : 0u);
+  }
+  const half8 ap = __builtin_bit_cast(half8, apw);
+  // ---- V: zero masked tokens, dequantise, PV ----
+  // xk[e] = (dims 8c+2k, 8c+2k+1) of token T(g, e) as value * 2^8; instruction v = 2k + hi
+  // takes dim 8c + v of tokens (2p, 2p+1) and multiplies by their scale pair sig[p].
+  uint32_t vd[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    uint32_t d = L.vd[e];
+    if (!full) {
+      const int eta = e >> 2;
+      const bool ok = (t0 + 16 * eta + 4 * g + (e & 3)) < t_end && ha[eta].ok;
+      d = ok ? d : 0u;
+    }
+    vd[e] = d;
+  }
+  half2v sig[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t w = L.vs[p >> 1] & 0x7F7F7F7Fu;
+    const int j0 = 2 * (p & 1);
+    const uint32_t sel = 0x0Cu | (uint32_t(j0) << 8) | (0x0Cu << 16) | (uint32_t(j0 + 1) << 24);
+    sig[p] = as_half2(__builtin_amdgcn_perm(w, w, sel) >> 1);
+  }
+  pv_pair<0>(vd, sig, ap, st);
+  pv_pair<1>(vd, sig, ap, st);
+  pv_pair<2>(vd, sig, ap, st);
+  pv_pair<3>(vd, sig, ap, st);
+}
+
+// Device-coherent 64-bit store / load (relaxed, device scope): they bypass the
+// non-coherent per-die L2 state, which is what the cross-workgroup merge needs.
+__device__ __forceinline__ void store_coherent_f2(float* p, float x, float y) {
+  const unsigned long long v = (static_cast<unsigned long long>(__float_as_uint(y)) << 32) | __float_as_uint(x);
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_coherent_f2(const float* p) {
+  const unsigned long long v = __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(static_cast<uint32_t>(v)), __uint_as_float(static_cast<uint32_t>(v >> 32)));
+}
+// s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15): wait for this wave's vector memory operations
+// (stores included) to complete.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Cross-split log-sum-exp merge run by the last workgroup of (b, h): wavefront w owns query
+// head 4h + w, lane l its dims 2l, 2l+1.  Splits are read 16 at a time with device-coherent
+// loads, all loads of a group independent (one memory round trip per group), and folded in
+// with a running max.
+constexpr int kMaxSplits = 1024;
+constexpr int kMergeGroup = 16;
+
+__device__ __forceinline__ void merge_splits(const DecodeArgs& a, int64_t unit, int i, int d0) {
+  const int n = a.n_splits;
+  float M = -INFINITY, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  for (int s0 = 0; s0 < n; s0 += kMergeGroup) {
+    float2 ml[kMergeGroup], o[kMergeGroup];
+#pragma unroll
+    for (int k = 0; k < kMergeGroup; ++k) {
+      const int sp = s0 + k < n ? s0 + k : n - 1;
+      const int64_t slot = (unit * n + sp) * 4 + i;
+      ml[k] = load_coherent_f2(a.ws_ml + slot * 2);
+      o[k] = load_coherent_f2(a.ws_o + slot * kHeadDim + d0);
+      if (s0 + k >= n) ml[k].y = 0.0f;                // padding entry: no weight
+    }
+    float mx = M;
+#pragma unroll
+    for (int k = 0; k < kMergeGroup; ++k) mx = ml[k].y > 0.0f ? fmaxf(mx, ml[k].x) : mx;
+    if (mx == -INFINITY) continue;                     // nothing in this group or before
+    const float sc = exp2f(M - mx);                    // 0 while M is still -inf
+    L *= sc;
+    o0 *= sc;
+    o1 *= sc;
+#pragma unroll
+    for (int k = 0; k < kMergeGroup; ++k) {
+      const float w = ml[k].y > 0.0f ? exp2f(ml[k].x - mx) : 0.0f;
+      L += w * ml[k].y;
+      o0 += w * o[k].x;
+      o1 += w * o[k].y;
+    }
+    M = mx;
+  }
+  const float f = L > 0.0f ? a.gscale[1] / L : 0.0f;
+  const int b = static_cast<int>(unit / a.hkv), h = static_cast<int>(unit % a.hkv);
+  *reinterpret_cast<float2*>(a.out + (static_cast<int64_t>(b) * a.hq + 4 * h + i) * kHeadDim + d0) =
+      make_float2(o0 * f, o1 * f);
+}
+
+// PIPE2: two register buffers and up to 8 wavefronts per workgroup (long splits, several
+// iterations per wavefront); otherwise one buffer and few enough registers for 16
+// wavefronts per workgroup (short splits, about one iteration per wavefront).
+template <bool KBF16, bool PIPE2>
+__global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
 
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[4][4][kHeadDim];   // [head][term][dim]
   __shared__ float q_descale[4];
-  __shared__ float red_m[kWaves][4], red_l[kWaves][4];
-  __shared__ __attribute__((aligned(16))) float red_o[kWaves][4][kHeadDim];
+  __shared__ float red_m[kMaxWaves][4], red_l[kMaxWaves][4];
+  __shared__ __attribute__((aligned(16))) float red_o[kMaxWaves][4][kHeadDim];
+  const int nw = static_cast<int>(blockDim.x) >> 6;
+  __shared__ int mrg_last;
 
+  const int64_t unit = static_cast<int64_t>(b) * a.hkv + h;
+  const int32_t* ptab = a.page_table + static_cast<int64_t>(b) * a.max_pages_per_seq;
+
+  // ---- start every independent memory access first: query row, sequence length, pages ----
+  const bool q_wave = wave < 4;                 // wavefronts 0..3 prepare query heads 4h..4h+3
+  const int hq_w = 4 * h + (q_wave ? wave : 0);
+  const uint32_t qw = reinterpret_cast<const uint32_t*>(a.q + (static_cast<int64_t>(b) * a.hq + hq_w) * kHeadDim)[lane];
+  float2 sv = make_float2(1.0f, 1.0f);
+  if (!KBF16 && (a.k_flags & NVKV_K_SMOOTH)) sv = reinterpret_cast<const float2*>(a.smooth + h * kHeadDim)[lane];
+  const float gk = KBF16 ? 1.0f : a.gscale[0];
   int seq_len = a.seq_lens[b];
   seq_len = seq_len < 0 ? 0 : (seq_len > a.seq_cap ? a.seq_cap : seq_len);
   const int t_begin = split * a.split_tokens;
   const int t_end = min(t_begin + a.split_tokens, seq_len);
-  const int64_t unit = static_cast<int64_t>(b) * a.hkv + h;
+  const bool empty = t_begin >= t_end;                      // uniform across the workgroup
 
-  if (t_begin >= t_end) {      // empty split (uniform across the workgroup)
-    if (a.n_splits == 1) {
-      for (int i = tid; i < 4 * kHeadDim; i += 256)
-        a.out[(static_cast<int64_t>(b) * a.hq + 4 * h) * kHeadDim + i] = 0.0f;
-    } else if (tid < 4) {
-      float* ml = a.ws_ml + ((unit * a.n_splits + split) * 4 + tid) * 2;
-      ml[0] = -INFINITY;
-      ml[1] = 0.0f;
-    }
-    return;
+  // First two iterations of this wavefront: addresses and loads are issued before the
+  // sequence length arrives, bounded by the kernel arguments only (t_lim >= t_end), so the
+  // cache traffic overlaps the query prologue; tokens in [t_end, t_lim) are masked later.
+  const int t_lim = min(t_begin + a.split_tokens, a.seq_cap);
+  const int step = kIterTok * nw;
+  int t0 = t_begin + kIterTok * wave;
+  IterLoads<KBF16> buf0, buf1;
+  HalfAddr ha0[2], ha1[2];
+  if (t0 < t_lim) {
+    half_addrs(a, load_pages(a, ptab, t0, t_lim), h, ha0);
+    issue_loads<KBF16>(a, ha0, c, g, buf0);
   }
+  if (PIPE2 && t0 + step < t_lim) {
+    half_addrs(a, load_pages(a, ptab, t0 + step, t_lim), h, ha1);
+    issue_loads<KBF16>(a, ha1, c, g, buf1);
+  }
+  IterPages pnext = load_pages(a, ptab, t0 + (PIPE2 ? 2 : 1) * step, t_lim > 0 ? t_lim : 1);
 
-  // ---------------- query prologue: wavefront w prepares query head 4h + w ----------------
-  {
-    const int hq = 4 * h + wave;
-    const uint32_t qw = reinterpret_cast<const uint32_t*>(a.q + (static_cast<int64_t>(b) * a.hq + hq) * kHeadDim)[lane];
+  // ---------------- query prologue: wavefront w < 4 prepares query head 4h + w ----------------
+  if (!empty && q_wave) {
     float x0 = bf16_to_f32(qw & 0xFFFFu), x1 = bf16_to_f32(qw >> 16);
     float scale = a.sm_scale * kLog2e;
     if (!KBF16) {
-      if (a.k_flags & NVKV_K_SMOOTH) {
-        const float2 sv = reinterpret_cast<const float2*>(a.smooth + h * kHeadDim)[lane];
-        x0 *= sv.x;
-        x1 *= sv.y;
-      }
+      x0 *= sv.x;
+      x1 *= sv.y;
       if (a.k_flags & NVKV_K_HADAMARD) {
-        float u0 = x0 + x1, u1 = x0 - x1;
+        const float u0 = x0 + x1, u1 = x0 - x1;
         x0 = u0;
         x1 = u1;
 #pragma unroll
@@ -160,269 +460,153 @@ __global__ void __launch_bounds__(256) k_decode(DecodeArgs a) {
         }
         scale *= (1.0f / 128.0f);
       }
-      scale *= a.gscale[0];
+      scale *= gk;
     }
     x0 *= scale;
     x1 *= scale;
     float m = fmaxf(fabsf(x0), fabsf(x1));
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+    m = fmaxf(m, dpp_xor1(m));
+    m = fmaxf(m, dpp_xor2(m));
+    m = fmaxf(m, dpp_row_ror4(m));
+    m = fmaxf(m, dpp_row_ror8(m));
+    m = rows_max(m);
     int e = 0;
     if (m > 0.0f) frexpf(m, &e);
     const int p2 = KBF16 ? 0 : 14 - e;           // max |x| * 2^p2 in [2^13, 2^14)
     x0 = ldexpf(x0, p2);
     x1 = ldexpf(x1, p2);
-    uint32_t t0, t1, t2;
-    if (!KBF16) {
+    uint32_t w0, w1, w2;
+    if constexpr (!KBF16) {
       const _Float16 h0 = static_cast<_Float16>(x0), h1 = static_cast<_Float16>(x1);
       const _Float16 l0 = static_cast<_Float16>(x0 - static_cast<float>(h0));
       const _Float16 l1 = static_cast<_Float16>(x1 - static_cast<float>(h1));
-      t0 = __builtin_bit_cast(uint16_t, h0) | (uint32_t(__builtin_bit_cast(uint16_t, h1)) << 16);
-      t1 = __builtin_bit_cast(uint16_t, l0) | (uint32_t(__builtin_bit_cast(uint16_t, l1)) << 16);
-      t2 = 0u;
+      w0 = __builtin_bit_cast(uint16_t, h0) | (uint32_t(__builtin_bit_cast(uint16_t, h1)) << 16);
+      w1 = __builtin_bit_cast(uint16_t, l0) | (uint32_t(__builtin_bit_cast(uint16_t, l1)) << 16);
+      w2 = 0u;
     } else {
       const uint32_t a0 = f32_to_bf16_rne(x0), a1 = f32_to_bf16_rne(x1);
       const float r0 = x0 - bf16_to_f32(a0), r1 = x1 - bf16_to_f32(a1);
       const uint32_t b0 = f32_to_bf16_rne(r0), b1 = f32_to_bf16_rne(r1);
       const uint32_t c0 = f32_to_bf16_rne(r0 - bf16_to_f32(b0)), c1 = f32_to_bf16_rne(r1 - bf16_to_f32(b1));
-      t0 = a0 | (a1 << 16);
-      t1 = b0 | (b1 << 16);
-      t2 = c0 | (c1 << 16);
+      w0 = a0 | (a1 << 16);
+      w1 = b0 | (b1 << 16);
+      w2 = c0 | (c1 << 16);
     }
-    reinterpret_cast<uint32_t*>(q_lds[wave][0])[lane] = t0;
-    reinterpret_cast<uint32_t*>(q_lds[wave][1])[lane] = t1;
-    reinterpret_cast<uint32_t*>(q_lds[wave][2])[lane] = t2;
+    reinterpret_cast<uint32_t*>(q_lds[wave][0])[lane] = w0;
+    reinterpret_cast<uint32_t*>(q_lds[wave][1])[lane] = w1;
+    reinterpret_cast<uint32_t*>(q_lds[wave][2])[lane] = w2;
     reinterpret_cast<uint32_t*>(q_lds[wave][3])[lane] = 0u;
     if (lane == 0) q_descale[wave] = ldexpf(1.0f, -p2);
   }
   __syncthreads();
 
-  // B operand of QK (Q'^T): lane (c, g) = column c = (head c>>2, term c&3); instruction u,
-  // item e <-> dim 32g + 8u + e.
-  u32x4 qb[4];
+  SoftmaxState st;
+  st.m_ref = -INFINITY;
+  st.l_acc = 0.0f;
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    qb[u] = *reinterpret_cast<const u32x4*>(&q_lds[c >> 2][c & 3][32 * g + 8 * u]);
-  const float descale = q_descale[c >> 2];
-  const int term = c & 3;
+  for (int v = 0; v < 8; ++v) st.acc[v] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  float m_ref = -INFINITY;   // running (lazy) max of this lane's head, base-2 units
-  float l_acc = 0.0f;        // this lane's share of the softmax denominator
-  floatx4 acc[8];
+  if (!empty) {
+    // B operand of QK (Q'^T): lane (c, g) = column c = (head c>>2, term c&3); instruction u,
+    // item e <-> dim 32g + 8u + e.
+    u32x4 qb[4];
 #pragma unroll
-  for (int v = 0; v < 8; ++v) acc[v] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int u = 0; u < 4; ++u)
+      qb[u] = *reinterpret_cast<const u32x4*>(&q_lds[c >> 2][c & 3][32 * g + 8 * u]);
+    const float descale = q_descale[c >> 2];
 
-  const int32_t* ptab = a.page_table + static_cast<int64_t>(b) * a.max_pages_per_seq;
-  const int ps = a.page_size;
-
-  for (int t0 = t_begin + kIterTok * wave; t0 < t_end; t0 += kIterTok * kWaves) {
-    // ---- page lookup per 16-token half (clamped into the valid range for addressing) ----
-    int64_t kv_row[2];       // (page * Hkv + h) * ps + page offset of the half's first token
-    int64_t sc_base[2];      // byte base of the (page, head) scale array
-    int off16[2];
-    bool page_ok[2];
-#pragma unroll
-    for (int eta = 0; eta < 2; ++eta) {
-      int tb = t0 + 16 * eta;
-      if (tb >= t_end) tb = (t_end - 1) & ~15;
-      const int32_t pg = ptab[tb / ps];
-      page_ok[eta] = static_cast<uint32_t>(pg) < static_cast<uint32_t>(a.num_pages);
-      const int64_t pgc = page_ok[eta] ? pg : 0;
-      off16[eta] = tb % ps;
-      kv_row[eta] = (pgc * a.hkv + h) * ps + off16[eta];
-      sc_base[eta] = (pgc * a.hkv + h) * ps * 8;
-    }
-
-    // ---- QK^T ----
-    floatx4 sacc[2];
-#pragma unroll
-    for (int eta = 0; eta < 2; ++eta) {
-      sacc[eta] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-      const int64_t row = kv_row[eta] + c;          // A row m = c: token t0 + 16 eta + c
-      if (!KBF16) {
-        const u32x4 kc = *reinterpret_cast<const u32x4*>(a.k_codes + row * 64 + 16 * g);
-        const int tok = off16[eta] + c;
-        const uint8_t* sb = a.k_scales + sc_base[eta] + ((tok >> 2) * 8 + 2 * g) * 4 + (tok & 3);
-        const half2v s0 = scale_pair_same(sb[0]);
-        const half2v s1 = scale_pair_same(sb[4]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const half8 ak = dequant_dword(kc[u], u < 2 ? s0 : s1);
-          sacc[eta] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, __builtin_bit_cast(half8, qb[u]), sacc[eta], 0, 0, 0);
-        }
-      } else {
-        const u32x4* kr = reinterpret_cast<const u32x4*>(a.k_codes + row * (kHeadDim * 2) + 64 * g);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const u32x4 kw = kr[u];
-          sacc[eta] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw),
-                                                               __builtin_bit_cast(bf16x8, qb[u]), sacc[eta], 0, 0, 0);
-        }
+    // Software pipeline: two register buffers hold the next two iterations' cache data and
+    // the page entries of the iteration after them are already loaded, so neither the
+    // vector loads nor the page lookups sit on the critical path.
+    if constexpr (!PIPE2) {
+      while (t0 < t_end) {
+        compute_iter<KBF16>(buf0, ha0, qb, descale, t0, t_end, c, g, st);
+        t0 += step;
+        if (t0 >= t_end) break;
+        half_addrs(a, pnext, h, ha0);
+        issue_loads<KBF16>(a, ha0, c, g, buf0);
+        pnext = load_pages(a, ptab, t0 + step, t_end);
       }
     }
-
-    // ---- scores: sum the query terms (columns 4i..4i+3), descale, mask ----
-    float s[8];
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int eta = 0; eta < 2; ++eta) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float x = sacc[eta][r];
-        x += dpp_xor1(x);
-        x += dpp_xor2(x);
-        x *= descale;
-        const int tok = t0 + 16 * eta + 4 * g + r;
-        const bool ok = tok < t_end && page_ok[eta];
-        x = ok ? x : -INFINITY;
-        s[4 * eta + r] = x;
-        bmax = fmaxf(bmax, x);
+    while (PIPE2 && t0 < t_end) {
+      compute_iter<KBF16>(buf0, ha0, qb, descale, t0, t_end, c, g, st);
+      t0 += step;
+      if (t0 >= t_end) break;
+      if (t0 + step < t_end) {
+        half_addrs(a, pnext, h, ha0);
+        issue_loads<KBF16>(a, ha0, c, g, buf0);
+        pnext = load_pages(a, ptab, t0 + 2 * step, t_end);
       }
-    }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-
-    // ---- lazy running max: move it only when the block max exceeds it by > 8 ----
-    const bool need = bmax > m_ref + kLazyMax;
-    if (__any(need)) {
-      const float m_new = need ? bmax : m_ref;
-      const float alpha = exp2f(m_ref - m_new);       // 0 on the first block
-      m_ref = m_new;
-      l_acc *= alpha;
-      const float alpha_row = __shfl(alpha, 4 * g, 64);   // PV rows of lane group g = head g
-#pragma unroll
-      for (int v = 0; v < 8; ++v) acc[v] *= alpha_row;
-    }
-
-    // ---- probabilities -> A operand of PV (row c: head c>>2, term c&3) ----
-    const float m_sub = (m_ref == -INFINITY) ? 0.0f : m_ref;   // a fully masked block keeps p = 0
-    half8 ap;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = exp2f(s[e] - m_sub);
-      l_acc += p;
-      const _Float16 ph = static_cast<_Float16>(p);
-      const _Float16 pl = static_cast<_Float16>(p - static_cast<float>(ph));
-      ap[e] = term == 0 ? ph : (term == 1 ? pl : static_cast<_Float16>(0.0f));
-    }
-
-    // ---- V: codes of dims 8c..8c+7 for tokens T(g, e) = 16*(e>>2) + 4g + (e&3) ----
-    uint32_t vd[8];
-    uint32_t vsc[2];
-#pragma unroll
-    for (int eta = 0; eta < 2; ++eta) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tok_rel = 4 * g + j;
-        const bool ok = (t0 + 16 * eta + tok_rel) < t_end && page_ok[eta];
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(a.v_codes + (kv_row[eta] + tok_rel) * 64 + 4 * c);
-        vd[4 * eta + j] = ok ? w : 0u;
+      compute_iter<KBF16>(buf1, ha1, qb, descale, t0, t_end, c, g, st);
+      t0 += step;
+      if (t0 + step < t_end) {
+        half_addrs(a, pnext, h, ha1);
+        issue_loads<KBF16>(a, ha1, c, g, buf1);
+        pnext = load_pages(a, ptab, t0 + 2 * step, t_end);
       }
-      const int quad = (off16[eta] >> 2) + g;
-      vsc[eta] = *reinterpret_cast<const uint32_t*>(a.v_scales + sc_base[eta] + (quad * 8 + (c >> 1)) * 4) & 0x7F7F7F7Fu;
-    }
-    half2v sig[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t w = vsc[p >> 1];
-      const int j0 = 2 * (p & 1);
-      const uint32_t sel = 0x0Cu | (uint32_t(j0) << 8) | (0x0Cu << 16) | (uint32_t(j0 + 1) << 24);
-      sig[p] = as_half2(__builtin_amdgcn_perm(w, w, sel) >> 1);
-    }
-    uint32_t hev[8], hod[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) nibble_high_bytes(vd[e], hev[e], hod[e]);
-
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      half8 bv;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t lo = (v & 1) ? hod[2 * p] : hev[2 * p];
-        const uint32_t hi = (v & 1) ? hod[2 * p + 1] : hev[2 * p + 1];
-        const half2v x = as_half2(pair_bytes(hi, lo, v >> 1)) * sig[p];
-        bv[2 * p] = x[0];
-        bv[2 * p + 1] = x[1];
-      }
-      acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, bv, acc[v], 0, 0, 0);
     }
   }
 
   // ---------------- wavefront partials -> LDS -> workgroup partial ----------------
-  float l_tot = l_acc;
-  l_tot += __shfl_xor(l_tot, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  if (g == 0 && term == 0) {
-    red_m[wave][c >> 2] = m_ref;
+  const float l_tot = rows_sum(st.l_acc);
+  if (g == 0 && (c & 3) == 0) {
+    red_m[wave][c >> 2] = st.m_ref;
     red_l[wave][c >> 2] = l_tot;
   }
   {
-    float o8[8];
-#pragma unroll
-    for (int v = 0; v < 8; ++v) o8[v] = acc[v][0] + acc[v][1];   // rows (head g, terms 0,1)
     float4* dst = reinterpret_cast<float4*>(&red_o[wave][g][8 * c]);
-    dst[0] = make_float4(o8[0], o8[1], o8[2], o8[3]);
-    dst[1] = make_float4(o8[4], o8[5], o8[6], o8[7]);
+    dst[0] = make_float4(st.acc[0][0] + st.acc[0][1], st.acc[1][0] + st.acc[1][1],
+                         st.acc[2][0] + st.acc[2][1], st.acc[3][0] + st.acc[3][1]);
+    dst[1] = make_float4(st.acc[4][0] + st.acc[4][1], st.acc[5][0] + st.acc[5][1],
+                         st.acc[6][0] + st.acc[6][1], st.acc[7][0] + st.acc[7][1]);
   }
   __syncthreads();
 
-  {
-    const int i = tid >> 6;              // head
-    const int d0 = 2 * (tid & 63);       // dims d0, d0+1
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w][i]);
-    float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+  // threads 0..255 own (head i, dims d0, d0+1) in the merges; the others only take part in
+  // the barriers
+  const bool owner = tid < 256;
+  const int i = (tid >> 6) & 3;
+  const int d0 = 2 * (tid & 63);
+  float M = -INFINITY, Lw = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  if (owner) {
+    for (int w = 0; w < nw; ++w) M = fmaxf(M, red_l[w][i] > 0.0f ? red_m[w][i] : -INFINITY);
+    for (int w = 0; w < nw; ++w) {
       if (red_l[w][i] > 0.0f) {
         const float wt = exp2f(red_m[w][i] - M);
-        L += wt * red_l[w][i];
+        Lw += wt * red_l[w][i];
         o0 += wt * red_o[w][i][d0];
         o1 += wt * red_o[w][i][d0 + 1];
       }
     }
-    const float gv = a.gscale[1];
-    if (a.n_splits == 1) {
-      const float f = L > 0.0f ? gv / L : 0.0f;
-      float2* o = reinterpret_cast<float2*>(a.out + (static_cast<int64_t>(b) * a.hq + 4 * h + i) * kHeadDim + d0);
-      *o = make_float2(o0 * f, o1 * f);
-    } else {
-      const int64_t slot = (unit * a.n_splits + split) * 4 + i;
-      *reinterpret_cast<float2*>(a.ws_o + slot * kHeadDim + d0) = make_float2(o0 * gv, o1 * gv);
-      if ((tid & 63) == 0) {
-        a.ws_ml[slot * 2 + 0] = M;
-        a.ws_ml[slot * 2 + 1] = L;
-      }
+  }
+  if (a.n_splits == 1) {
+    if (owner) {
+      const float f = Lw > 0.0f ? a.gscale[1] / Lw : 0.0f;
+      float* out_row = a.out + (static_cast<int64_t>(b) * a.hq + 4 * h + i) * kHeadDim + d0;
+      *reinterpret_cast<float2*>(out_row) = make_float2(o0 * f, o1 * f);
     }
+    return;
   }
-}
-
-// Cross-split log-sum-exp merge: grid (Hkv, B), 256 threads = 4 heads x 64 dim pairs.
-__global__ void __launch_bounds__(256) k_decode_merge(DecodeArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int i = threadIdx.x >> 6, d0 = 2 * (threadIdx.x & 63);
-  const int64_t unit = static_cast<int64_t>(b) * a.hkv + h;
-  float M = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s) {
-    const float* ml = a.ws_ml + ((unit * a.n_splits + s) * 4 + i) * 2;
-    if (ml[1] > 0.0f) M = fmaxf(M, ml[0]);
+  // ---- cross-workgroup merge: the last workgroup of (b, h) to arrive combines the splits ----
+  // Partials are written with device-coherent stores and read with device-coherent loads, so
+  // no cache writeback or invalidate is needed (a device-scope fence would write back and
+  // invalidate the whole L2 of the die).  Each wavefront waits until its stores have
+  // completed before the workgroup barrier; only then does one thread count the arrival.
+  if (owner) {
+    const int64_t slot = (unit * a.n_splits + split) * 4 + i;
+    store_coherent_f2(a.ws_o + slot * kHeadDim + d0, o0, o1);
+    if ((tid & 63) == 0) store_coherent_f2(a.ws_ml + slot * 2, M, Lw);
   }
-  float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  for (int s = 0; s < a.n_splits; ++s) {
-    const int64_t slot = (unit * a.n_splits + s) * 4 + i;
-    const float l = a.ws_ml[slot * 2 + 1];
-    if (l > 0.0f) {
-      const float wt = exp2f(a.ws_ml[slot * 2] - M);
-      const float2 o = *reinterpret_cast<const float2*>(a.ws_o + slot * kHeadDim + d0);
-      L += wt * l;
-      o0 += wt * o.x;
-      o1 += wt * o.y;
-    }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(a.counters + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    mrg_last = (prev == static_cast<unsigned>(a.n_splits - 1)) ? 1 : 0;
   }
-  const float f = L > 0.0f ? 1.0f / L : 0.0f;
-  *reinterpret_cast<float2*>(a.out + (static_cast<int64_t>(b) * a.hq + 4 * h + i) * kHeadDim + d0) =
-      make_float2(o0 * f, o1 * f);
+  __syncthreads();
+  if (!mrg_last || !owner) return;
+  merge_splits(a, unit, i, d0);
+  if (tid == 0) __hip_atomic_store(a.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -431,26 +615,47 @@ __global__ void __launch_bounds__(256) k_decode_merge(DecodeArgs a) {
 DecodePlan plan_decode(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t split_tokens) {
   DecodePlan p{};
   const int32_t len = max_seq_len > 0 ? max_seq_len : 1;
+  const int64_t iters = (len + kIterTok - 1) / kIterTok;          // 32-token iterations
+  int64_t per;                                                    // iterations per split
   if (split_tokens <= 0) {
-    // Aim at ~1024 workgroups in flight (4 per CU over 256 CUs) without cutting a split below
-    // one iteration per wavefront.
-    const int64_t iters = (len + kIterTok - 1) / kIterTok;
+    // About one workgroup per CU (256): splits per (sequence, KV head) = 256 / units, at
+    // least one; the wavefronts of a workgroup take one iteration each when that fits in 16
+    // wavefronts, otherwise 8 wavefronts share the split's iterations.
     const int64_t units = static_cast<int64_t>(B) * Hkv;
-    int64_t per = (units * iters + 1023) / 1024;
-    if (per < kWaves) per = kWaves;
-    if (per > iters) per = iters;
-    split_tokens = static_cast<int32_t>(per * kIterTok);
+    int64_t ns = (256 + units / 2) / units;
+    if (ns < 1) ns = 1;
+    if (ns > iters) ns = iters;
+    per = (iters + ns - 1) / ns;
+  } else {
+    per = split_tokens / kIterTok;
   }
-  p.split_tokens = split_tokens;
-  p.n_splits = (len + split_tokens - 1) / split_tokens;
+  // the merge of a sequence visits splits in groups; bound their number
+  const int64_t min_per = (iters + kMaxSplits - 1) / kMaxSplits;
+  if (per < min_per) per = min_per;
+  if (per < 1) per = 1;
+  p.split_tokens = static_cast<int32_t>(per * kIterTok);
+  p.n_splits = static_cast<int32_t>((len + p.split_tokens - 1) / p.split_tokens);
+  if (per <= kMaxWaves) {
+    p.pipe2 = false;
+    p.waves = static_cast<int32_t>(per < 4 ? 4 : per);
+  } else {
+    p.pipe2 = true;
+    p.waves = 8;
+  }
   return p;
 }
 
+namespace {
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+}
+
+// Workspace layout: [arrival counters: B*Hkv u32][(m, l) per split and head][O per split
+// and head].  The counters come first so that their place does not depend on the split
+// count: calls with different split counts may share a workspace.
 size_t decode_workspace_bytes(int32_t B, int32_t Hkv, const DecodePlan& plan) {
   const size_t slots = static_cast<size_t>(B) * Hkv * plan.n_splits * 4;
-  const size_t o_bytes = (slots * kHeadDim * sizeof(float) + 255) & ~size_t(255);
-  const size_t ml_bytes = (slots * 2 * sizeof(float) + 255) & ~size_t(255);
-  return o_bytes + ml_bytes;
+  return align256(static_cast<size_t>(B) * Hkv * sizeof(unsigned)) + align256(slots * 2 * sizeof(float)) +
+         align256(slots * kHeadDim * sizeof(float));
 }
 
 hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, int32_t B, int32_t Hq, const int32_t* page_table,
@@ -468,9 +673,11 @@ hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, int32_t B, int3
   a.seq_lens = seq_lens;
   a.out = out;
   const size_t slots = static_cast<size_t>(B) * L.num_kv_heads * plan.n_splits * 4;
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                     ((slots * kHeadDim * sizeof(float) + 255) & ~size_t(255)));
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const size_t cnt_bytes = align256(static_cast<size_t>(B) * L.num_kv_heads * sizeof(unsigned));
+  a.counters = reinterpret_cast<unsigned*>(ws);
+  a.ws_ml = reinterpret_cast<float*>(ws + cnt_bytes);
+  a.ws_o = reinterpret_cast<float*>(ws + cnt_bytes + align256(slots * 2 * sizeof(float)));
   a.hkv = L.num_kv_heads;
   a.hq = Hq;
   a.page_size = L.page_size;
@@ -483,12 +690,14 @@ hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, int32_t B, int3
   a.k_flags = L.k_flags;
   a.sm_scale = sm_scale;
   const dim3 grid(plan.n_splits, L.num_kv_heads, B);
-  if (L.k_fmt == NVKV_FMT_BF16)
-    hipLaunchKernelGGL(k_decode<true>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(k_decode<false>, grid, dim3(256), 0, stream, a);
-  if (plan.n_splits > 1)
-    hipLaunchKernelGGL(k_decode_merge, dim3(L.num_kv_heads, B), dim3(256), 0, stream, a);
+  const dim3 block(64 * plan.waves);
+  if (L.k_fmt == NVKV_FMT_BF16) {
+    if (plan.pipe2) hipLaunchKernelGGL((k_decode<true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k_decode<true, false>), grid, block, 0, stream, a);
+  } else {
+    if (plan.pipe2) hipLaunchKernelGGL((k_decode<false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k_decode<false, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -18,6 +18,8 @@ hipError_t launch_calibrate(const uint16_t* k_win, const uint16_t* v_win, int32_
 struct DecodePlan {
   int32_t split_tokens;   // tokens handled by one workgroup (multiple of 32)
   int32_t n_splits;       // workgroups per (sequence, KV head)
+  int32_t waves;          // wavefronts per workgroup (4..16)
+  bool pipe2;             // two-deep software pipeline (several iterations per wavefront)
 };
 DecodePlan plan_decode(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t split_tokens);
 size_t decode_workspace_bytes(int32_t B, int32_t Hkv, const DecodePlan& plan);

@@ -47,15 +47,16 @@ __global__ void __launch_bounds__(256) k_quantize_append(AppendPair p) {
   if (row >= a.n_rows) return;                      // whole 8-lane row groups leave together
   const int n = row / a.hkv;
   const int h = row - n * a.hkv;
+  // independent loads first (row data, slot, tensor scale); the slot check comes after
+  float y[kBlock];
+  uint4 raw0, raw1;
+  load_block_bf16(a.src + static_cast<int64_t>(row) * kHeadDim + blk * kBlock, y, raw0, raw1);
   const int32_t slot = a.slots[n];
+  const float gsc = a.fmt == 0 ? 1.0f : *a.gscale;
   if (slot < 0 || static_cast<int64_t>(slot) >= a.max_slot) return;
   const int32_t page = slot / a.page_size;
   const int32_t off = slot - page * a.page_size;
   const int64_t row_index = (static_cast<int64_t>(page) * a.hkv + h) * a.page_size + off;
-
-  float y[kBlock];
-  uint4 raw0, raw1;
-  load_block_bf16(a.src + static_cast<int64_t>(row) * kHeadDim + blk * kBlock, y, raw0, raw1);
 
   if (a.fmt == 0) {  // BF16 keys: plain copy of the row
     uint4* dst = reinterpret_cast<uint4*>(a.codes + row_index * (kHeadDim * 2) + blk * 32);
@@ -67,7 +68,7 @@ __global__ void __launch_bounds__(256) k_quantize_append(AppendPair p) {
   if (a.flags & 2u) hadamard_row(y, blk);
 
   uint32_t lo, hi;
-  const uint32_t S = encode_block(y, *a.gscale, lo, hi);
+  const uint32_t S = encode_block(y, gsc, lo, hi);
   *reinterpret_cast<uint2*>(a.codes + row_index * 64 + blk * 8) = make_uint2(lo, hi);
   const int64_t sbase = (static_cast<int64_t>(page) * a.hkv + h) * a.page_size * 8;
   a.scales[sbase + ((off >> 2) * 8 + blk) * 4 + (off & 3)] = static_cast<uint8_t>(S);
