@@ -1,19 +1,27 @@
 #!/usr/bin/env python3
 """Benchmark of the NVFP4 KV-cache hot path on one MI355X.
 
-Default workload: one decode step of a Qwen3-8B-shaped attention cache -- 36 layers x 8 KV
-heads x head_dim 128, 32 query heads, batch 4 x 2304 cached tokens, 16-token pages with a
-shuffled page table, keys and values NVFP4 with static per-channel key smoothing.  A step
-runs, for every layer, quantize_append_kv of the new token of each sequence followed by
-decode_attention_nvfp4 over all 2304 tokens (the whole hot path: quantise -> pack -> split-K
-decode -> merge).  Steps replay HIP graphs over 3 rotating copies of the 36-layer cache
-(1.15 GB, beyond the 256 MB last-level cache).
+Default workload ("step36"): one decode step of a Qwen3-8B-shaped attention cache.
+  - shape: 36 layers x 8 KV heads x head_dim 128, 32 query heads, batch 4 x 2304 cached
+    tokens, 16-token pages with a shuffled page table;
+  - cache: keys and values NVFP4, static per-channel key smoothing;
+  - a step runs, for every layer, quantize_append_kv of the new token of each sequence and
+    then decode_attention_nvfp4 over all 2304 tokens: quantise -> pack -> split-K decode ->
+    merge;
+  - steps replay HIP graphs over 3 rotating copies of the 36-layer cache (1.15 GB, beyond the
+    256 MB last-level cache).
+Other workloads (run by hand with --workload):
+  - step36-vonly, step36-hadamard, step36-had-smooth: the same step with other cache formats;
+  - long: decode step at batch 64 x 32768 context (87 GB packed cache);
+  - prefill, prefill-hadamard: quantize_append_kv of 16 x 8192 new tokens into each of 36
+    paged layers.
 
-Printed: one JSON line with the step throughput (algorithmic bytes / step time), tokens/s,
-the roofline of the decode kernel (algorithmic bytes per launch / average launch time from
-HIP events), and the CPU oracle timed on a bounded sample of the same workload.
-
-    python bench.py [--steps K] [--warmup W] [--workload step36|step36-vonly|step36-hadamard|long]
+Printed: one JSON line with
+  - the step throughput (algorithmic bytes / step time) and tokens/s;
+  - the roofline of the dominant kernel: algorithmic bytes per launch / average launch time,
+    from HIP events around graph replays on the launch stream;
+  - the CPU oracle timed on a bounded sample of the same workload;
+  - a sampled parity check of the timed configuration against the oracle.
 """
 from __future__ import annotations
 
@@ -32,6 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "NVFP4-KV decode attention: achieved HBM GB/s (% of peak) and tokens/s"
 HBM_PEAK_GBS = 8000.0
 PAGE = 16
+SM_SCALE = 1.0 / math.sqrt(128)
 
 
 def parse():
@@ -39,8 +48,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="step36")
-    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--workload", default="step36",
+                    help="step36 | step36-vonly | step36-hadamard | step36-had-smooth | long | prefill | "
+                         "prefill-hadamard")
+    ap.add_argument("--copies", type=int, default=0, help="rotating cache copies (0: workload default)")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
@@ -52,11 +63,14 @@ def parse():
 
 
 VARIANTS = {
-    "step36": dict(cfg="step36", k_fmt=1, flags=1, label="K+V NVFP4, K smoothed"),
-    "step36-vonly": dict(cfg="step36", k_fmt=0, flags=0, label="K bf16, V NVFP4"),
-    "step36-hadamard": dict(cfg="step36", k_fmt=1, flags=2, label="K+V NVFP4, K Hadamard-128"),
-    "step36-had-smooth": dict(cfg="step36", k_fmt=1, flags=3, label="K+V NVFP4, K smoothed + Hadamard-128"),
-    "long": dict(cfg="long", k_fmt=1, flags=1, label="K+V NVFP4, K smoothed"),
+    "step36": dict(cfg="step36", k_fmt=1, flags=1, copies=3, label="K+V NVFP4, K smoothed"),
+    "step36-vonly": dict(cfg="step36", k_fmt=0, flags=0, copies=3, label="K bf16, V NVFP4"),
+    "step36-hadamard": dict(cfg="step36", k_fmt=1, flags=2, copies=3, label="K+V NVFP4, K Hadamard-128"),
+    "step36-had-smooth": dict(cfg="step36", k_fmt=1, flags=3, copies=3,
+                              label="K+V NVFP4, K smoothed + Hadamard-128"),
+    "long": dict(cfg="long", k_fmt=1, flags=1, copies=1, label="K+V NVFP4, K smoothed"),
+    "prefill": dict(cfg="prefill", k_fmt=1, flags=1, copies=1, label="K smoothed"),
+    "prefill-hadamard": dict(cfg="prefill", k_fmt=1, flags=3, copies=1, label="K smoothed + Hadamard-128"),
 }
 
 
@@ -64,7 +78,26 @@ def row_bytes(fmt):
     return 256 if fmt == 0 else 72
 
 
-class Workload:
+def f32_of(torch, t):
+    """bf16 torch tensor (host) -> fp32 numpy array of the same values."""
+    from synth import kv_inputs as S
+    return S.bf16_to_f32(t.contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+def calib_windows_device(torch, S, c, l):
+    kw = torch.cat([S.make_keys_device(c["kind"], c["cfg"], l, 1, c["Tw"], c["hkv"], role=S.ROLE_WIN0 + w)
+                    for w in range(4)])
+    vw = torch.cat([S.make_values_device(c["cfg"], l, 1, c["Tw"], c["hkv"], role=S.ROLE_WIN0 + 4 + w)
+                    for w in range(4)])
+    return kw, vw
+
+
+class DecodeStep:
+    """Decode-step workloads: per layer, append the new token of every sequence, then attend."""
+
+    metric = METRIC
+    kernel_label = "k_decode (decode_attention_nvfp4: split-K decode + in-kernel cross-split merge), per layer"
+
     def __init__(self, name, copies, split_tokens):
         import torch
         import nvfp4_bit_kv_amd as nk
@@ -72,10 +105,10 @@ class Workload:
         self.torch, self.nk, self.S = torch, nk, S
         v = VARIANTS[name]
         c = S.CONFIGS[v["cfg"]]
-        self.name, self.v, self.c = name, v, c
+        self.name, self.variant, self.c = name, v, c
         self.B, self.T, self.hkv, self.hq, self.L = c["B"], c["T"], c["hkv"], c["hq"], c["layers"]
         self.k_fmt, self.flags = v["k_fmt"], v["flags"]
-        self.copies = copies
+        self.copies = copies or v["copies"]
         self.split_tokens = split_tokens
         B, T, hkv = self.B, self.T, self.hkv
         self.pps = (T + PAGE - 1) // PAGE
@@ -85,50 +118,65 @@ class Workload:
         dev = "cuda"
         self.table = torch.from_numpy(self.table_np).to(dev)
         t = np.arange(T)
-        slots = self.table_np[:, t // PAGE] * PAGE + t % PAGE          # [B][T]
-        self.slots_np = slots.astype(np.int32)
+        self.slots_np = (self.table_np[:, t // PAGE] * PAGE + t % PAGE).astype(np.int32)    # [B][T]
         self.seq_lens = torch.full((B,), T, dtype=torch.int32, device=dev)
         self.new_slots = torch.from_numpy(np.ascontiguousarray(self.slots_np[:, T - 1])).to(dev)
-        self.caches = [[None] * self.L for _ in range(copies)]
+        self.caches = [[None] * self.L for _ in range(self.copies)]
         self.k_new, self.v_new, self.q = [], [], []
         self.out = torch.empty((self.L, B, self.hq, 128), dtype=torch.float32, device=dev)
         self.wsb = nk.decode_workspace_bytes(B, self.hq, hkv, T, split_tokens)
         self.ws = torch.zeros(max(self.wsb, 256), dtype=torch.uint8, device=dev)
+        # sequences whose bf16 inputs are kept on the host for the oracle legs
+        self.sample_b = list(range(B)) if B <= 4 else [0, B - 1]
         self._build()
 
     def _build(self):
         torch, nk, S = self.torch, self.nk, self.S
         c, B, T, hkv = self.c, self.B, self.T, self.hkv
-        chunk = max(1, (1 << 22) // (T * hkv))          # sequences per prefill append call
+        bc = max(1, min(B, (1 << 27) // (T * hkv * 128)))        # sequences per generation chunk
         for l in range(self.L):
-            k = S.make_keys_device(c["kind"], c["cfg"], l, B, T, hkv)
-            v = S.make_values_device(c["cfg"], l, B, T, hkv)
-            kw = torch.cat([S.make_keys_device(c["kind"], c["cfg"], l, 1, c["Tw"], hkv, role=S.ROLE_WIN0 + w)
-                            for w in range(4)])
-            vw = torch.cat([S.make_values_device(c["cfg"], l, 1, c["Tw"], hkv, role=S.ROLE_WIN0 + 4 + w)
-                            for w in range(4)])
+            kw, vw = calib_windows_device(torch, S, c, l)
             s = torch.empty((hkv, 128), dtype=torch.float32, device="cuda")
             r = torch.empty_like(s)
             g = torch.empty(2, dtype=torch.float32, device="cuda")
             nk.calibrate_key_smoothing(kw, vw, 4, c["Tw"], hkv, True, self.flags, s, r, g)
+            layer_caches = []
             for cp in range(self.copies):
                 cache = nk.CacheLayer(self.num_pages, PAGE, hkv, k_fmt=self.k_fmt, k_flags=self.flags)
                 cache.smooth.copy_(s)
                 cache.inv_smooth.copy_(r)
                 cache.gscale.copy_(g)
-                Ls = cache.struct()
-                for b0 in range(0, B, chunk):
-                    b1 = min(B, b0 + chunk)
-                    n = (b1 - b0) * (T - 1)
-                    sl = torch.from_numpy(np.ascontiguousarray(self.slots_np[b0:b1, :T - 1]).reshape(-1)).cuda()
-                    nk.quantize_append_kv(Ls, k[b0:b1, :T - 1].contiguous(), v[b0:b1, :T - 1].contiguous(), sl, n)
-                self.caches[cp][l] = (cache, Ls)
-            self.k_new.append(k[:, T - 1].contiguous())
-            self.v_new.append(v[:, T - 1].contiguous())
+                layer_caches.append((cache, cache.struct()))
+            k_new = torch.empty((B, hkv, 128), dtype=torch.bfloat16, device="cuda")
+            v_new = torch.empty_like(k_new)
+            keep = {}
+            for b0 in range(0, B, bc):
+                b1 = min(B, b0 + bc)
+                k = S.make_keys_device(c["kind"], c["cfg"], l, b1 - b0, T, hkv, seed_index=b0)
+                v = S.make_values_device(c["cfg"], l, b1 - b0, T, hkv, seed_index=b0)
+                n = (b1 - b0) * (T - 1)
+                sl = torch.from_numpy(np.ascontiguousarray(self.slots_np[b0:b1, :T - 1]).reshape(-1)).cuda()
+                kp, vp = k[:, :T - 1].contiguous(), v[:, :T - 1].contiguous()
+                for cache, Ls in layer_caches:
+                    nk.quantize_append_kv(Ls, kp, vp, sl, n)
+                k_new[b0:b1] = k[:, T - 1]
+                v_new[b0:b1] = v[:, T - 1]
+                if l == 0:
+                    for b in self.sample_b:
+                        if b0 <= b < b1:
+                            keep[b] = (k[b - b0].cpu(), v[b - b0].cpu())
+                del k, v, kp, vp
+            for cp in range(self.copies):
+                self.caches[cp][l] = layer_caches[cp]
+            self.k_new.append(k_new)
+            self.v_new.append(v_new)
             self.q.append(S.make_queries_device(c["cfg"], l, B, self.hq))
             if l == 0:
-                self.layer0 = (k.cpu(), v.cpu(), kw.cpu(), vw.cpu())
-            del k, v, kw, vw
+                self.layer0 = (keep, kw.cpu(), vw.cpu())
+            del kw, vw
+            if self.L > 8 and (l + 1) % 6 == 0:
+                torch.cuda.synchronize()
+                print(f"[bench] built layer {l + 1}/{self.L}", file=sys.stderr, flush=True)
         torch.cuda.synchronize()
 
     # one layer of the hot path: append the new token, then attend over the whole cache
@@ -138,14 +186,19 @@ class Workload:
         if not decode_only:
             nk.quantize_append_kv(Ls, self.k_new[l], self.v_new[l], self.new_slots, self.B)
         nk.decode_attention_nvfp4(Ls, self.q[l], self.B, self.hq, self.table, self.pps, self.seq_lens, self.T,
-                                  1.0 / math.sqrt(128), self.out[l], self.ws, self.wsb, self.split_tokens)
+                                  SM_SCALE, self.out[l], self.ws, self.wsb, self.split_tokens)
 
     def step(self, cp):
         for l in range(self.L):
             self.layer_step(cp, l)
 
+    def snapshot(self):
+        return self.out.clone()
+
     # algorithmic bytes (what the method must move)
-    def decode_bytes_per_layer(self):
+    def launch_bytes(self):
+        """One decode_attention_nvfp4 call: every cached K and V row with its scales once, the
+        query (bf16) in and the output (fp32) out."""
         per_tok = row_bytes(self.k_fmt) + 72
         return self.B * self.hkv * self.T * per_tok + self.B * self.hq * (256 + 512)
 
@@ -153,7 +206,182 @@ class Workload:
         return self.B * self.hkv * ((256 + row_bytes(self.k_fmt)) + (256 + 72))
 
     def step_bytes(self):
-        return self.L * (self.decode_bytes_per_layer() + self.append_bytes_per_layer())
+        return self.L * (self.launch_bytes() + self.append_bytes_per_layer())
+
+    def tokens_per_step(self):
+        return self.B
+
+    def launch_times(self, reps):
+        return decode_launch_times(self.torch, self, reps)
+
+    def check(self):
+        return decode_check_against_oracle(self)
+
+    def cpu_baseline(self):
+        return decode_cpu_baseline(self)
+
+    def describe(self):
+        c = self.c
+        return (f"{self.name}: Qwen3-8B-shaped decode step, {c['layers']} layers x {c['hkv']} KV heads x 128, "
+                f"{c['hq']} query heads, batch {c['B']} x {c['T']} context, 16-token paged cache, "
+                f"{self.variant['label']}; per layer append 1 token + split-K decode")
+
+
+class PrefillAppend:
+    """Prefill workload: quantize_append_kv of B x T new tokens into each of the paged layers."""
+
+    metric = "NVFP4-KV quantize/append: achieved HBM GB/s (% of peak) and tokens/s"
+    kernel_label = "k_quantize_append (quantize_append_kv of batch 16 x 8192 new tokens), per layer"
+
+    def __init__(self, name):
+        import torch
+        import nvfp4_bit_kv_amd as nk
+        from synth import kv_inputs as S
+        self.torch, self.nk, self.S = torch, nk, S
+        v = VARIANTS[name]
+        c = S.CONFIGS[v["cfg"]]
+        self.name, self.variant, self.c = name, v, c
+        self.B, self.T, self.hkv, self.L = c["B"], c["T"], c["hkv"], c["layers"]
+        self.flags = v["flags"]
+        self.copies = 1
+        B, T, hkv = self.B, self.T, self.hkv
+        self.pps = T // PAGE
+        self.num_pages = B * self.pps
+        rng = np.random.default_rng(4321)
+        self.table_np = rng.permutation(self.num_pages).reshape(B, self.pps).astype(np.int32)
+        t = np.arange(T)
+        slots = (self.table_np[:, t // PAGE] * PAGE + t % PAGE).astype(np.int32)
+        self.slots = torch.from_numpy(np.ascontiguousarray(slots.reshape(-1))).cuda()
+        self.N = B * T
+        self.caches, self.k, self.v = [], [], []
+        for l in range(self.L):
+            kw, vw = calib_windows_device(torch, S, c, l)
+            cache = nk.CacheLayer(self.num_pages, PAGE, hkv, k_flags=self.flags)
+            nk.calibrate_key_smoothing(kw, vw, 4, c["Tw"], hkv, True, self.flags, cache.smooth,
+                                       cache.inv_smooth, cache.gscale)
+            self.caches.append((cache, cache.struct()))
+            self.k.append(S.make_keys_device(c["kind"], c["cfg"], l, B, T, hkv).reshape(B * T, hkv, 128))
+            self.v.append(S.make_values_device(c["cfg"], l, B, T, hkv).reshape(B * T, hkv, 128))
+            if l == 0:
+                self.layer0 = (kw.cpu(), vw.cpu())
+        torch.cuda.synchronize()
+        self._calib = None
+
+    def step(self, cp):
+        for l in range(self.L):
+            cache, Ls = self.caches[l]
+            self.nk.quantize_append_kv(Ls, self.k[l], self.v[l], self.slots, self.N)
+
+    def snapshot(self):
+        cache, _ = self.caches[0]
+        return self.torch.cat([cache.k_data, cache.k_scales, cache.v_data, cache.v_scales])
+
+    def launch_bytes(self):
+        """One quantize_append_kv call: per (token, KV head) the bf16 K and V rows in
+        (2 x 256 B) and their codes and scales out (2 x 72 B); the slot index per token."""
+        return self.N * (self.hkv * 2 * (256 + 72) + 4)
+
+    def step_bytes(self):
+        return self.L * self.launch_bytes()
+
+    def tokens_per_step(self):
+        return self.N
+
+    def launch_times(self, reps):
+        """Average duration of one quantize_append_kv call: a HIP graph of the calls of all
+        layers is replayed between HIP events on the launch stream, divided by the layer count."""
+        torch = self.torch
+        g = capture(torch, lambda: self.step(0))
+        g.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for r in range(reps):
+            ev[r][0].record(stream)
+            g.replay()
+            ev[r][1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3 / self.L
+
+    def _oracle_calib(self):
+        from oracle import nvfp4_oracle as O
+        if self._calib is None:
+            kw, vw = self.layer0
+            self._calib = O.calibrate(f32_of(self.torch, kw), f32_of(self.torch, vw), True, self.flags)
+        return self._calib
+
+    def _oracle_rows(self, rows):
+        from oracle import nvfp4_oracle as O
+        torch = self.torch
+        s, r, g = self._oracle_calib()
+        k = f32_of(torch, self.k[0][rows].cpu())
+        v = f32_of(torch, self.v[0][rows].cpu())
+        kc, ks = O.quantize_rows(O.key_transform(k, r[None], self.flags), g[0])
+        vc, vs = O.quantize_rows(v, g[1])
+        return kc, ks, vc, vs
+
+    def check(self):
+        """Bit-exact comparison of sampled rows of layer 0 (first and last sequence, read back
+        through the page table) and of the calibrated scales."""
+        torch = self.torch
+        cache, _ = self.caches[0]
+        s, r, g = self._oracle_calib()
+        ok = bool(np.array_equal(cache.inv_smooth.cpu().numpy(), r)
+                  and np.array_equal(cache.gscale.cpu().numpy(), g))
+        n_rows = 0
+        views = (cache.k_data.view(self.num_pages, self.hkv, PAGE, 64),
+                 cache.k_scales.view(self.num_pages, self.hkv, PAGE // 4, 8, 4),
+                 cache.v_data.view(self.num_pages, self.hkv, PAGE, 64),
+                 cache.v_scales.view(self.num_pages, self.hkv, PAGE // 4, 8, 4))
+        t = np.arange(self.T)
+        for b in (0, self.B - 1):
+            want = self._oracle_rows(slice(b * self.T, (b + 1) * self.T))
+            pg = torch.from_numpy(self.table_np[b][t // PAGE].astype(np.int64)).cuda()
+            off = torch.from_numpy((t % PAGE).astype(np.int64)).cuda()
+            got = (views[0][pg, :, off], views[1][pg, :, off // 4, :, off % 4],
+                   views[2][pg, :, off], views[3][pg, :, off // 4, :, off % 4])
+            for gt, w in zip(got, want):
+                ok &= bool(np.array_equal(gt.cpu().numpy(), w))
+            n_rows += 2 * self.T * self.hkv
+        return dict(ok=ok, compared_rows=n_rows,
+                    kind="bit-exact K/V codes and scales of layer 0, sequences 0 and last, and the calibration")
+
+    def cpu_baseline(self, budget_s=12.0):
+        """The oracle's key transform and NVFP4 quantisation of K and V on chunks of layer 0's
+        new tokens (calibration done once beforehand, untimed), one BLAS thread, for a bounded
+        time; the per-layer rate is divided by the layer count."""
+        from threadpoolctl import threadpool_limits
+        chunk = 1024
+        with threadpool_limits(limits=1):
+            self._oracle_calib()
+            rows_done = 0
+            t0 = time.perf_counter()
+            while True:
+                a = rows_done % (self.N - chunk)
+                self._oracle_rows(slice(a, a + chunk))
+                rows_done += chunk
+                el = time.perf_counter() - t0
+                if el >= budget_s:
+                    break
+        tok_s = rows_done / el
+        return dict(value=round(tok_s / self.L, 2), unit="tokens/s", cores=1, kind="oracle",
+                    sample=f"{rows_done} new tokens x {self.hkv} KV heads of layer 0 (key transform + NVFP4 "
+                           f"quantisation of K and V) in {el:.1f} s on 1 core of "
+                           f"{len(os.sched_getaffinity(0))}; per-layer rate divided by {self.L} layers",
+                    oracle_effective_gbs=round(tok_s * self.launch_bytes() / self.N / 1e9, 6))
+
+    def describe(self):
+        c = self.c
+        return (f"{self.name}: quantize_append_kv of batch {c['B']} x {c['T']} new tokens into each of "
+                f"{c['layers']} layers x {c['hkv']} KV heads x 128, 16-token paged cache (shuffled pages), "
+                f"{self.variant['label']}, K and V NVFP4")
+
+
+def capture(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
 
 
 def time_graphs(torch, graphs, steps, warmup):
@@ -170,15 +398,8 @@ def time_graphs(torch, graphs, steps, warmup):
     return e0.elapsed_time(e1)
 
 
-def capture(torch, fn):
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        fn()
-    return g
-
-
 def decode_launch_times(torch, wl, reps):
-    """Average duration of one decode_attention_nvfp4 call (its kernels back to back, no host
+    """Average duration of one decode_attention_nvfp4 call (its kernel back to back, no host
     gaps): a HIP graph of the decode calls of all layers of a cache copy is replayed between
     two HIP events on the launch stream; one sample per replay, divided by the layer count."""
     graphs = [capture(torch, lambda cp=cp: [wl.layer_step(cp, l, decode_only=True) for l in range(wl.L)])
@@ -207,82 +428,98 @@ def sweep_splits(torch, wl, splits):
         d = decode_launch_times(torch, wl, reps=10)
         res[sp] = (float(np.mean(d)) * 1e6, float(np.min(d)) * 1e6)
         print(f"[sweep] split_tokens={sp}: avg {res[sp][0]:.2f} us  min {res[sp][1]:.2f} us  "
-              f"-> {wl.decode_bytes_per_layer() / np.mean(d) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
+              f"-> {wl.launch_bytes() / np.mean(d) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
     wl.split_tokens, wl.wsb, wl.ws = saved
     return res
 
 
-def check_against_oracle(wl):
-    """Sampled parity of the timed configuration: layer 0, every sequence and query head,
-    against the oracle built from the same bf16 inputs (calibration included)."""
+def _oracle_decode_inputs(wl):
+    """Oracle calibration, query and per-sequence codes for layer 0, from the same bf16 inputs
+    as the GPU path; computed once and kept (the codes are row-wise, so the codes of the first
+    T-1 rows are a prefix of those of all T rows)."""
     from oracle import nvfp4_oracle as O
-    torch, S = wl.torch, wl.S
-    k, v, kw, vw = wl.layer0
-    f = lambda t: S.bf16_to_f32(t.view(torch.int16).numpy().view(np.uint16))
-    s, r, g = O.calibrate(f(kw), f(vw), True, wl.flags)
-    B, T, hq = wl.B, wl.T, wl.hq
-    qf = f(wl.q[0].cpu()).astype(np.float64)
+    if getattr(wl, "_oracle", None) is None:
+        torch = wl.torch
+        keep, kw, vw = wl.layer0
+        s, r, g = O.calibrate(f32_of(torch, kw), f32_of(torch, vw), True, wl.flags)
+        qf = f32_of(torch, wl.q[0].cpu()).astype(np.float64)
+        seqs = {}
+        for b in wl.sample_b:
+            kf, vf = f32_of(torch, keep[b][0]), f32_of(torch, keep[b][1])
+            kc = ks = None
+            if wl.k_fmt == 1:
+                kc, ks = O.quantize_rows(O.key_transform(kf, r[None], wl.flags), g[0])
+            vc, vs = O.quantize_rows(vf, g[1])
+            seqs[b] = (kf, vf, (kc, ks, vc, vs))
+        wl._oracle = (s, r, g, qf, seqs)
+    return (O,) + wl._oracle
+
+
+def _oracle_sequence(O, wl, s, r, g, qf, kf, vf, b, codes, append_last):
+    """Oracle decode of one sequence: the codes of its T cached rows (with append_last, the
+    codes of the first T-1 rows plus the appended row quantised here), dequantisation and fp64
+    attention for every query head."""
+    T, hq, hkv = wl.T, wl.hq, wl.hkv
+    kc, ks, vc, vs = codes
+    if append_last:
+        if wl.k_fmt == 1:
+            nkc, nks = O.quantize_rows(O.key_transform(kf[T - 1:], r[None], wl.flags), g[0])
+            kc, ks = np.concatenate([kc[:T - 1], nkc]), np.concatenate([ks[:T - 1], nks])
+        nvc, nvs = O.quantize_rows(vf[T - 1:], g[1])
+        vc, vs = np.concatenate([vc[:T - 1], nvc]), np.concatenate([vs[:T - 1], nvs])
     if wl.k_fmt == 1:
-        kc, ks = O.quantize_rows(O.key_transform(f(k), r[None, None], wl.flags), g[0])
-        khat = [O.dequantize(kc[b], ks[b], g[0]) for b in range(B)]
-        qp = O.query_transform(qf, np.repeat(s, hq // wl.hkv, 0)[None], wl.flags)
+        khat = O.dequantize(kc, ks, g[0])
+        qp = O.query_transform(qf[b:b + 1], np.repeat(s, hq // hkv, 0)[None], wl.flags)
     else:
-        khat = [f(k[b]).astype(np.float64) for b in range(B)]
-        qp = qf
-    vc, vs = O.quantize_rows(f(v), g[1])
-    vhat = [O.dequantize(vc[b], vs[b], g[1]) for b in range(B)]
-    ref = O.attention(qp, khat, vhat, [T] * B, 1.0 / math.sqrt(128))
-    got = wl.out[0].cpu().numpy().astype(np.float64)
-    vmax = max(float(np.abs(x).max()) for x in vhat)
-    err = float(np.abs(got - ref).max())
-    rel = float((np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)).max())
-    ok = err <= 1e-3 * vmax and rel <= 1e-4
-    return dict(ok=bool(ok), max_abs_err=err, tol_abs=1e-3 * vmax, max_rel_l2=rel, tol_rel_l2=1e-4)
+        khat = kf.astype(np.float64)
+        qp = qf[b:b + 1]
+    vhat = O.dequantize(vc, vs, g[1])
+    return O.attention(qp, [khat], [vhat], [T], SM_SCALE)[0], vhat
 
 
-def cpu_baseline(wl, budget_s=12.0):
-    """The oracle as it stands on a bounded sample: per layer and for all B sequences, quantise
-    the new token, dequantise the cache and run fp64 attention for every query head (the oracle
-    needs the cached codes, which it builds itself beforehand, untimed).  BLAS is held to one
-    thread.  Extrapolated to the 36-layer step."""
+def decode_check_against_oracle(wl):
+    """Sampled parity of the timed configuration: layer 0, the sampled sequences, every query
+    head, against the oracle built from the same bf16 inputs (calibration included)."""
+    O, s, r, g, qf, seqs = _oracle_decode_inputs(wl)
+    got_all = wl.out[0].cpu().numpy().astype(np.float64)
+    worst_err = worst_rel = 0.0
+    ok = True
+    for b in wl.sample_b:
+        kf, vf, codes = seqs[b]
+        ref, vhat = _oracle_sequence(O, wl, s, r, g, qf, kf, vf, b, codes, append_last=False)
+        got = got_all[b]
+        err = float(np.abs(got - ref).max())
+        rel = float((np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)).max())
+        ok &= err <= 1e-3 * float(np.abs(vhat).max()) and rel <= 1e-4
+        worst_err, worst_rel = max(worst_err, err), max(worst_rel, rel)
+    return dict(ok=bool(ok), sequences=wl.sample_b, max_abs_err=worst_err, max_rel_l2=worst_rel,
+                tol="max|err| <= 1e-3 max|Vhat|, rel L2 <= 1e-4")
+
+
+def decode_cpu_baseline(wl, budget_s=12.0):
+    """The oracle as it stands on a bounded sample: per (layer-0 sequence) unit, quantise the
+    new token, dequantise the cache and run fp64 attention for every query head (the codes of
+    the T-1 cached rows are built beforehand, untimed).  BLAS is held to one thread.
+    Extrapolated to all sequences and layers of the step."""
     from threadpoolctl import threadpool_limits
-    from oracle import nvfp4_oracle as O
-    torch, S = wl.torch, wl.S
-    k, v, kw, vw = wl.layer0
-    f = lambda t: S.bf16_to_f32(t.view(torch.int16).numpy().view(np.uint16))
     B, T, hq, hkv = wl.B, wl.T, wl.hq, wl.hkv
     with threadpool_limits(limits=1):
-        s, r, g = O.calibrate(f(kw), f(vw), True, wl.flags)
-        kf, vf = f(k), f(v)
-        if wl.k_fmt == 1:
-            kc, ks = O.quantize_rows(O.key_transform(kf[:, :T - 1], r[None, None], wl.flags), g[0])
-        vc, vs = O.quantize_rows(vf[:, :T - 1], g[1])
-        qf = f(wl.q[0].cpu()).astype(np.float64)
-        layers = 0
+        O, s, r, g, qf, seqs = _oracle_decode_inputs(wl)
+        units = 0
         t0 = time.perf_counter()
         while True:
-            if wl.k_fmt == 1:
-                nkc, nks = O.quantize_rows(O.key_transform(kf[:, T - 1:], r[None, None], wl.flags), g[0])
-                khat = [O.dequantize(np.concatenate([kc[b], nkc[b]]), np.concatenate([ks[b], nks[b]]), g[0])
-                        for b in range(B)]
-                qp = O.query_transform(qf, np.repeat(s, hq // hkv, 0)[None], wl.flags)
-            else:
-                khat = [kf[b].astype(np.float64) for b in range(B)]
-                qp = qf
-            nvc, nvs = O.quantize_rows(vf[:, T - 1:], g[1])
-            vhat = [O.dequantize(np.concatenate([vc[b], nvc[b]]), np.concatenate([vs[b], nvs[b]]), g[1])
-                    for b in range(B)]
-            O.attention(qp, khat, vhat, [T] * B, 1.0 / math.sqrt(128))
-            layers += 1
+            for b in wl.sample_b:
+                kf, vf, codes = seqs[b]
+                _oracle_sequence(O, wl, s, r, g, qf, kf, vf, b, codes, append_last=True)
+                units += 1
             el = time.perf_counter() - t0
-            if el >= budget_s or layers >= wl.L:
+            if el >= budget_s or units >= B * wl.L:
                 break
-    per_layer = el / layers
-    step_s = per_layer * wl.L
+    step_s = el / units * B * wl.L
     return dict(value=round(B / step_s, 4), unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{layers} x (layer 0 of {wl.L}, all {B} sequences: append 1 token + dequantise "
-                       f"{T} tokens x {hkv} KV heads + fp64 attention for {hq} query heads), "
-                       f"{el:.1f} s on 1 core of {len(os.sched_getaffinity(0))}, extrapolated x{wl.L} layers",
+                sample=f"{units} x (one sequence of layer 0: append 1 token + dequantise {T} tokens x {hkv} KV "
+                       f"heads + fp64 attention for {hq} query heads), {el:.1f} s on 1 core of "
+                       f"{len(os.sched_getaffinity(0))}, extrapolated to {B} sequences x {wl.L} layers",
                 oracle_step_s=round(step_s, 3),
                 oracle_effective_gbs=round(wl.step_bytes() / step_s / 1e9, 6))
 
@@ -291,44 +528,49 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(sharding design is described in the design notes)"}))
+                                   "(the sharding design is described in the design notes)"}))
         sys.exit(2)
+    if args.workload not in VARIANTS:
+        sys.exit(f"unknown workload {args.workload!r}; choose from {sorted(VARIANTS)}")
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     if args.profile_pass:
         args.steps, args.warmup, args.no_cpu_baseline = min(args.steps, 20), min(args.warmup, 5), True
     print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
-    wl = Workload(args.workload, args.copies, args.split_tokens)
+    if VARIANTS[args.workload]["cfg"] == "prefill":
+        wl = PrefillAppend(args.workload)
+    else:
+        wl = DecodeStep(args.workload, args.copies, args.split_tokens)
 
-    # eager warm-up and reference outputs per copy, then graph capture per copy
+    # eager pass and its result, then one graph per cache copy
     wl.step(0)
     torch.cuda.synchronize()
-    eager0 = wl.out.clone()
+    eager0 = wl.snapshot()
     graphs = [capture(torch, lambda cp=cp: wl.step(cp)) for cp in range(wl.copies)]
     print(f"[bench] captured {len(graphs)} step graphs; timing {args.steps} steps", file=sys.stderr, flush=True)
     ms = time_graphs(torch, graphs, args.steps, args.warmup) / args.steps
-    # replays must reproduce the eager result
-    graphs[0].replay()
+    graphs[0].replay()                       # replays must reproduce the eager result
     torch.cuda.synchronize()
-    replay_ok = bool(torch.equal(wl.out, eager0))
+    replay_ok = bool(torch.equal(wl.snapshot(), eager0))
+    del eager0
 
-    print("[bench] per-launch decode timing", file=sys.stderr, flush=True)
-    durs = decode_launch_times(torch, wl, reps=max(3, min(30, args.steps // 5)))
+    print("[bench] per-launch timing of the dominant kernel", file=sys.stderr, flush=True)
+    durs = wl.launch_times(max(3, min(30, args.steps // 5)))
     avg_launch = float(np.mean(durs))
-    dec_bytes = wl.decode_bytes_per_layer()
-    achieved = dec_bytes / avg_launch / 1e9
+    achieved = wl.launch_bytes() / avg_launch / 1e9
 
-    if args.sweep_splits:
+    if args.sweep_splits and isinstance(wl, DecodeStep):
         sweep_splits(torch, wl, [int(x) for x in args.sweep_splits.split(",")])
-    check = None if args.no_check else check_against_oracle(wl)
-    base = None if args.no_cpu_baseline else cpu_baseline(wl)
+    print("[bench] oracle check / cpu baseline", file=sys.stderr, flush=True)
+    check = None if args.no_check else wl.check()
+    base = None if args.no_cpu_baseline else wl.cpu_baseline()
 
     step_s = ms * 1e-3
     gbs = wl.step_bytes() / step_s / 1e9
     c = wl.c
     line = {
-        "metric": METRIC,
+        "metric": wl.metric,
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -339,19 +581,17 @@ def main():
         "dtype": "nvfp4 cache (e2m1 + e4m3 scales); f16 MFMA on exact operands, f32 accumulate",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.workload}: Qwen3-8B-shaped decode step, {c['layers']} layers x {c['hkv']} KV heads "
-                        f"x 128, {c['hq']} query heads, batch {c['B']} x {c['T']} context, 16-token paged "
-                        f"cache, {wl.v['label']}; per layer append 1 token + split-K decode",
+            "workload": wl.describe(),
             "global_batch": c["B"], "seq_len": c["T"], "layers": c["layers"], "parallelism": "none (1 GPU)",
             "split_tokens": args.split_tokens or "auto",
         },
-        "tokens_per_s": round(c["B"] / step_s, 2),
+        "tokens_per_s": round(wl.tokens_per_step() / step_s, 2),
         "hbm_frac_of_step": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "k_decode (decode_attention_nvfp4: split-K decode + in-kernel cross-split merge), per layer",
-            "bytes_per_launch": dec_bytes, "avg_launch_us": round(avg_launch * 1e6, 3),
+            "kernel": wl.kernel_label,
+            "bytes_per_launch": wl.launch_bytes(), "avg_launch_us": round(avg_launch * 1e6, 3),
             "min_launch_us": round(float(np.min(durs)) * 1e6, 3),
         },
         "cpu_baseline": base,
