@@ -44,6 +44,7 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxWaves = 16;   // wavefronts per workgroup: 4..16 (runtime, blockDim.x / 64)
 constexpr int kIterTok = 32;
@@ -65,6 +66,7 @@ struct DecodeArgs {
   float* ws_ml;               // [B][Hkv][n_splits][4][2]
   unsigned* counters;         // [B][Hkv] arrival counters, zero between calls
   int32_t hkv, hq, page_size, num_pages, max_pages_per_seq, seq_cap;
+  int32_t page_shift;         // log2(page_size) when it is a power of two, else -1
   int32_t split_tokens, n_splits;
   uint32_t k_flags;
   float sm_scale;
@@ -84,19 +86,13 @@ __device__ __forceinline__ float dpp_row_ror8(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));
 }
 
-// Reductions over the four 16-lane rows (lanes l, l^16, l^32, l^48) with the gfx950 row-swap
-// permutes: pure VALU, so they never wait on outstanding scalar loads.
+// Max over the four 16-lane rows (lanes l, l^16, l^32, l^48) with the gfx950 row-swap
+// permutes: pure VALU, so it never waits on outstanding scalar loads.
 __device__ __forceinline__ float rows_max(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
   const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
-}
-__device__ __forceinline__ float rows_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
 __device__ __forceinline__ half2v as_half2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
@@ -120,27 +116,48 @@ __device__ __forceinline__ half8 dequant_dword(uint32_t d, half2v sig2) {
 // E4M3 scale byte (masked to 7 bits) -> fp16 bits of sigma * 2^-8, duplicated in both halves.
 __device__ __forceinline__ half2v scale_pair_same(uint32_t s) { return as_half2((s & 0x7Fu) * 0x00800080u); }
 
+// Per-lane constants: lane (c, g) = (lane & 15, lane >> 4).  All cache loads of an iteration
+// are a wave-uniform base (scalar registers, from the page table) plus one of these
+// loop-invariant 32-bit lane offsets.
+struct Lane {
+  int c, g;
+  uint32_t k_off;       // K codes: token c, dims 32g..32g+31 (16 B); BF16 keys: 64 B
+  uint32_t ks_off;      // K scales: the quad of token c, blocks 2g and 2g+1 (8 B)
+  uint32_t ks_shift;    // bit position of token c's byte in those scale dwords
+  uint32_t v_off;       // V codes: token 4g of the half, dims 8c..8c+7 (4 B; + 64 j for token 4g+j)
+  uint32_t vs_off;      // V scales: quad g of the half, block c >> 1 (4 B)
+};
+
 // Registers of one 32-token iteration, filled by issue_loads() well before they are used.
 template <bool KBF16> struct KLoads;
 template <> struct KLoads<false> {
-  u32x4 kc[2];          // codes of dims 32g..32g+31 of token (half eta, row c)
-  uint32_t ks[2][2];    // scale bytes of blocks 2g, 2g+1 of that token
+  u32x4 kc[2];          // codes of dims 32g..32g+31 of token c of half eta
+  u32x2 ks[2];          // scale dwords of blocks 2g, 2g+1 (4 tokens each) of half eta
 };
 template <> struct KLoads<true> {
-  u32x4 kr[2][4];       // bf16 dims 32g..32g+31 of token (half eta, row c)
+  u32x4 kr[2][4];       // bf16 dims 32g..32g+31 of token c of half eta
 };
 template <bool KBF16> struct IterLoads {
   KLoads<KBF16> k;
-  uint32_t vd[8];       // V code dwords (dims 8c..8c+7) of tokens T(g, e)
-  uint32_t vs[2];       // V scale dwords (4 tokens of quad g of each half, block c>>1)
+  uint32_t vd[8];       // V code dword (dims 8c..8c+7) of token 4g+j of half eta, at [2j + eta]
+  uint32_t vs[2];       // V scale dword of half eta (tokens 4g..4g+3, block c >> 1)
 };
 
-struct HalfAddr {
-  int64_t kv_row;       // (page * Hkv + h) * ps + in-page offset of the half's first token
-  int64_t sc_base;      // byte base of the (page, head) scale array
-  int off16;
-  bool ok;              // page index in range
+// Wave-uniform buffer descriptors of the two 16-token halves of an iteration: base = the
+// half's first token in each cache array, so every load is descriptor + 32-bit lane offset
+// + instruction offset.
+struct HalfBase {
+  __amdgpu_buffer_rsrc_t kc, ks, vc, vs;
+  bool ok;              // page index in range (otherwise page 0 is read and the tokens masked)
 };
+
+// Raw-buffer descriptor word 3 for gfx9-family parts (32-bit data format, no swizzle); the
+// record count is left unbounded because every offset is derived from checked indices.
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, -1, kRsrcWord3);
+}
+constexpr int kNonTemporal = 2;   // cache-policy bit of the buffer-load intrinsics: nt
 
 // Page-table entries of the two 16-token halves of an iteration (scalar loads, issued one
 // iteration before the cache loads that need them).  Tokens at or beyond t_hi are mapped
@@ -150,185 +167,196 @@ struct IterPages {
   int off16[2];
 };
 
-__device__ __forceinline__ IterPages load_pages(const DecodeArgs& a, const int32_t* ptab, int t, int t_hi) {
+// The page table is read-only for the whole kernel: reading it through the constant address
+// space lets the compiler use scalar loads for these wave-uniform entries.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+
+__device__ __forceinline__ IterPages load_pages(const DecodeArgs& a, const_i32_ptr ptab, int t, int t_hi) {
   IterPages r;
 #pragma unroll
   for (int eta = 0; eta < 2; ++eta) {
     int tb = t + 16 * eta;
     if (tb >= t_hi) tb = (t_hi - 1) & ~15;
     if (tb < 0) tb = 0;
-    r.pg[eta] = ptab[tb / a.page_size];
-    r.off16[eta] = tb % a.page_size;
+    if (a.page_shift >= 0) {
+      r.pg[eta] = ptab[tb >> a.page_shift];
+      r.off16[eta] = tb & (a.page_size - 1);
+    } else {
+      r.pg[eta] = ptab[tb / a.page_size];
+      r.off16[eta] = tb % a.page_size;
+    }
   }
   return r;
 }
 
-__device__ __forceinline__ void half_addrs(const DecodeArgs& a, const IterPages& P, int h, HalfAddr (&ha)[2]) {
+template <bool KBF16>
+__device__ __forceinline__ void half_bases(const DecodeArgs& a, const IterPages& P, int h, HalfBase (&hb)[2]) {
 #pragma unroll
   for (int eta = 0; eta < 2; ++eta) {
     const int32_t pg = P.pg[eta];
-    ha[eta].ok = static_cast<uint32_t>(pg) < static_cast<uint32_t>(a.num_pages);
-    const int64_t pgc = ha[eta].ok ? pg : 0;
-    ha[eta].off16 = P.off16[eta];
-    ha[eta].kv_row = (pgc * a.hkv + h) * a.page_size + P.off16[eta];
-    ha[eta].sc_base = (pgc * a.hkv + h) * a.page_size * 8;
+    hb[eta].ok = static_cast<uint32_t>(pg) < static_cast<uint32_t>(a.num_pages);
+    const int64_t ph = static_cast<int64_t>(hb[eta].ok ? pg : 0) * a.hkv + h;   // (page, head) block
+    const int64_t row0 = ph * a.page_size + P.off16[eta];
+    const int64_t sc0 = ph * a.page_size * 8 + (P.off16[eta] >> 2) * 32;
+    hb[eta].kc = make_rsrc(a.k_codes + row0 * (KBF16 ? kHeadDim * 2 : 64));
+    if constexpr (!KBF16) hb[eta].ks = make_rsrc(a.k_scales + sc0);
+    hb[eta].vc = make_rsrc(a.v_codes + row0 * 64);
+    hb[eta].vs = make_rsrc(a.v_scales + sc0);
   }
 }
 
 template <bool KBF16>
-__device__ __forceinline__ void issue_loads(const DecodeArgs& a, const HalfAddr (&ha)[2], int c, int g,
-                                            IterLoads<KBF16>& L) {
+__device__ __forceinline__ void issue_loads(const HalfBase (&hb)[2], const Lane& ln, IterLoads<KBF16>& L) {
 #pragma unroll
   for (int eta = 0; eta < 2; ++eta) {
-    const int64_t row = ha[eta].kv_row + c;
     if constexpr (!KBF16) {
-      L.k.kc[eta] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.k_codes + row * 64 + 16 * g));
-      const int tok = ha[eta].off16 + c;
-      const uint8_t* sb = a.k_scales + ha[eta].sc_base + ((tok >> 2) * 8 + 2 * g) * 4 + (tok & 3);
-      L.k.ks[eta][0] = sb[0];
-      L.k.ks[eta][1] = sb[4];
+      L.k.kc[eta] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hb[eta].kc, ln.k_off, 0, kNonTemporal));
+      L.k.ks[eta] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(hb[eta].ks, ln.ks_off, 0, 0));
     } else {
-      const u32x4* kr = reinterpret_cast<const u32x4*>(a.k_codes + row * (kHeadDim * 2) + 64 * g);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) L.k.kr[eta][u] = __builtin_nontemporal_load(kr + u);
+      for (int u = 0; u < 4; ++u)
+        L.k.kr[eta][u] =
+            __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hb[eta].kc, ln.k_off + 16 * u, 0, kNonTemporal));
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      L.vd[4 * eta + j] = __builtin_nontemporal_load(
-          reinterpret_cast<const uint32_t*>(a.v_codes + (ha[eta].kv_row + 4 * g + j) * 64 + 4 * c));
-    const int quad = (ha[eta].off16 >> 2) + g;
-    L.vs[eta] = *reinterpret_cast<const uint32_t*>(a.v_scales + ha[eta].sc_base + (quad * 8 + (c >> 1)) * 4);
+      L.vd[2 * j + eta] = __builtin_amdgcn_raw_buffer_load_b32(hb[eta].vc, ln.v_off + 64 * j, 0, kNonTemporal);
+    L.vs[eta] = __builtin_amdgcn_raw_buffer_load_b32(hb[eta].vs, ln.vs_off, 0, 0);
   }
 }
 
-// Online-softmax state of one wavefront.
+// Online-softmax state of one wavefront.  Lane (c, g) serves query head g: its running max,
+// its share of the denominator and the PV accumulator rows 4g..4g+3 = (head g, term 0..3).
 struct SoftmaxState {
-  float m_ref;          // lazy running max of the lane's head (base-2 units)
-  float l_acc;          // lane's share of the denominator
-  floatx4 acc[8];       // PV accumulators: rows (head g, term r), column c <-> dim 8c + v
+  float m_ref;          // lazy running max of head g (base-2 units)
+  float l_acc;          // lane's share of head g's denominator
+  floatx4 acc[8];       // PV accumulators: column c <-> dim 8c + v
 };
 
-// PV for dims 8c + 2K and 8c + 2K + 1 (instructions v = 2K, 2K + 1).
+// P transpose buffer of a wavefront in LDS: 16 rows (head i, term t) of 32 fp16 in the PV
+// token order k, row stride kPStride dwords (padded against bank conflicts).
+constexpr int kPStride = 20;
+constexpr int kPWords = 16 * kPStride;
+
+// Per-block nibble interleave of the V codes of two tokens A, B (dims 8c..8c+7 each): byte k
+// of ev holds dim 8c+2k of (A, B), byte k of od holds dim 8c+2k+1 of (A, B), so one FP4 pair
+// convert yields a (token, token) pair of one dim -- the PV B-operand order.
+__device__ __forceinline__ uint32_t nib_even(uint32_t A, uint32_t B) { return (A & 0x0F0F0F0Fu) | ((B << 4) & 0xF0F0F0F0u); }
+__device__ __forceinline__ uint32_t nib_odd(uint32_t A, uint32_t B) { return ((A >> 4) & 0x0F0F0F0Fu) | (B & 0xF0F0F0F0u); }
+
+// PV for dims 8c + 2K (from ev) and 8c + 2K + 1 (from od): instructions v = 2K, 2K + 1.
 template <int K>
-__device__ __forceinline__ void pv_pair(const uint32_t (&vd)[8], const half2v (&sig)[4], const half8& ap,
-                                        SoftmaxState& st) {
-  uint32_t xk[8];
+__device__ __forceinline__ void pv_pair(const uint32_t (&ev)[4], const uint32_t (&od)[4], const half2v (&sig)[4],
+                                        const half8& ap, SoftmaxState& st) {
+  u32x4 be, bo;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) xk[e] = as_u32(fp4_pair_x256<K>(vd[e]));
-#pragma unroll
-  for (int hi = 0; hi < 2; ++hi) {
-    const uint32_t sel = hi ? 0x07060302u : 0x05040100u;   // high or low f16 half of each
-    u32x4 bw;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) bw[p] = as_u32(as_half2(__builtin_amdgcn_perm(xk[2 * p + 1], xk[2 * p], sel)) * sig[p]);
-    st.acc[2 * K + hi] =
-        __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(half8, bw), st.acc[2 * K + hi], 0, 0, 0);
+  for (int p = 0; p < 4; ++p) {
+    be[p] = as_u32(fp4_pair_x256<K>(ev[p]) * sig[p]);
+    bo[p] = as_u32(fp4_pair_x256<K>(od[p]) * sig[p]);
   }
+  st.acc[2 * K] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(half8, be), st.acc[2 * K], 0, 0, 0);
+  st.acc[2 * K + 1] =
+      __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(half8, bo), st.acc[2 * K + 1], 0, 0, 0);
 }
 
+// Sum / max over the 16 lanes of a row (DPP within the row).
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_xor1(x));
+  x = fmaxf(x, dpp_xor2(x));
+  x = fmaxf(x, dpp_row_ror4(x));
+  return fmaxf(x, dpp_row_ror8(x));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_xor1(x);
+  x += dpp_xor2(x);
+  x += dpp_row_ror4(x);
+  return x + dpp_row_ror8(x);
+}
+
+__device__ __forceinline__ void valid_tokens(const HalfBase (&hb)[2], int t0, int t_end, int c, bool (&v)[2]) {
+  v[0] = hb[0].ok && (t0 + c < t_end);
+  v[1] = hb[1].ok && (t0 + 16 + c < t_end);
+}
+
+// One 32-token iteration of a wavefront.  valid[eta]: token c of half eta is inside the split
+// and its page index is in range.
 template <bool KBF16>
-__device__ __forceinline__ void compute_iter(const IterLoads<KBF16>& L, const HalfAddr (&ha)[2], const u32x4 (&qb)[4],
-                                             float descale, int t0, int t_end, int c, int g, SoftmaxState& st) {
-  const int term = c & 3;
-  // ---- QK^T: rows = tokens (c), columns = (head, query term) ----
+__device__ __forceinline__ void compute_iter(const IterLoads<KBF16>& L, const bool (&valid)[2], const u32x4 (&qa)[4],
+                                             float descale, const Lane& ln, SoftmaxState& st, uint32_t* p_w) {
+  // ---- QK: S = Q' Khat^T.  A = Q' (row = (head, term)), B = Khat^T (column = token c of the
+  // half); lane (c, g) receives rows 4g..4g+3 = the query terms of head g for token c ----
   floatx4 sacc[2];
 #pragma unroll
   for (int eta = 0; eta < 2; ++eta) {
     sacc[eta] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (!KBF16) {
-      const half2v s0 = scale_pair_same(L.k.ks[eta][0]);
-      const half2v s1 = scale_pair_same(L.k.ks[eta][1]);
+      const half2v s0 = scale_pair_same(L.k.ks[eta][0] >> ln.ks_shift);
+      const half2v s1 = scale_pair_same(L.k.ks[eta][1] >> ln.ks_shift);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const half8 ak = dequant_dword(L.k.kc[eta][u], u < 2 ? s0 : s1);
-        sacc[eta] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, __builtin_bit_cast(half8, qb[u]), sacc[eta], 0, 0, 0);
+        const half8 bk = dequant_dword(L.k.kc[eta][u], u < 2 ? s0 : s1);
+        sacc[eta] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, qa[u]), bk, sacc[eta], 0, 0, 0);
       }
     } else {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        sacc[eta] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, L.k.kr[eta][u]),
-                                                             __builtin_bit_cast(bf16x8, qb[u]), sacc[eta], 0, 0, 0);
+        sacc[eta] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[u]),
+                                                             __builtin_bit_cast(bf16x8, L.k.kr[eta][u]), sacc[eta],
+                                                             0, 0, 0);
     }
   }
-  // ---- scores: sum the query terms of a head (columns 4i..4i+3), mask ragged tails ----
-  // A wave-uniform flag skips the masking when all 32 tokens are valid.
-  const bool full = (t0 + kIterTok <= t_end) && ha[0].ok && ha[1].ok;
-  float s[8];
-  float bmax = -INFINITY;
+  float s[2];
 #pragma unroll
   for (int eta = 0; eta < 2; ++eta) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float x = sacc[eta][r];
-      x += dpp_xor1(x);
-      x += dpp_xor2(x);
-      if (!full) {
-        const bool ok = (t0 + 16 * eta + 4 * g + r) < t_end && ha[eta].ok;
-        x = ok ? x : -INFINITY;
-      }
-      s[4 * eta + r] = x;
-      bmax = fmaxf(bmax, x);
-    }
+    float x = sacc[eta][0] + sacc[eta][1];       // fp16 queries: terms 2, 3 are zero
+    if constexpr (KBF16) x += sacc[eta][2];      // bf16 queries: three terms
+    s[eta] = valid[eta] ? x : -INFINITY;
   }
-  bmax = rows_max(bmax) * descale;              // descale > 0: max commutes with it
+  const float bmax = row16_max(fmaxf(s[0], s[1])) * descale;   // descale > 0: max commutes with it
   // ---- lazy running max: it moves only when a block max exceeds it by more than 8 ----
   const bool need = bmax > st.m_ref + kLazyMax;
-  if (__any(need)) {
+  if (__builtin_expect(__any(need), 0)) {
     const float m_new = need ? bmax : st.m_ref;
-    const float alpha = exp2f(st.m_ref - m_new);          // 0 on the first block
+    const float alpha = exp2f(st.m_ref - m_new);           // 0 on the first block
     st.m_ref = m_new;
     st.l_acc *= alpha;
-    // PV rows of lane group g belong to head g, whose alpha sits in lane 4g
-    const float al0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0));
-    const float al1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 4));
-    const float al2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 8));
-    const float al3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 12));
-    const float alpha_row = g == 0 ? al0 : (g == 1 ? al1 : (g == 2 ? al2 : al3));
 #pragma unroll
-    for (int v = 0; v < 8; ++v) st.acc[v] *= alpha_row;
+    for (int v = 0; v < 8; ++v) st.acc[v] *= alpha;
   }
   const float neg_m = (st.m_ref == -INFINITY) ? 0.0f : -st.m_ref;   // a fully masked block keeps p = 0
-  // p = 2^(s*descale - m) <= 256; A operand of PV: row term 0 = hi(p), term 1 = lo(p) =
-  // p - hi(p), terms 2, 3 = 0 (hi/lo by round-toward-zero packed converts: |p - hi - lo| <
-  // 2^-20 p).
-  u32x4 apw;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * k], descale, neg_m));
-    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * k + 1], descale, neg_m));
-    st.l_acc += p0 + p1;
-    const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0, p1));
-    const half2v lo = __builtin_bit_cast(
-        half2v, __builtin_amdgcn_cvt_pkrtz(p0 - static_cast<float>(hi[0]), p1 - static_cast<float>(hi[1])));
-    apw[k] = term == 0 ? as_u32(hi) : (term == 1 ? as_u32(lo) : 0u);
-  }
-  const half8 ap = __builtin_bit_cast(half8, apw);
-  // ---- V: zero masked tokens, dequantise, PV ----
-  // xk[e] = (dims 8c+2k, 8c+2k+1) of token T(g, e) as value * 2^8; instruction v = 2k + hi
-  // takes dim 8c + v of tokens (2p, 2p+1) and multiplies by their scale pair sig[p].
-  uint32_t vd[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    uint32_t d = L.vd[e];
-    if (!full) {
-      const int eta = e >> 2;
-      const bool ok = (t0 + 16 * eta + 4 * g + (e & 3)) < t_end && ha[eta].ok;
-      d = ok ? d : 0u;
-    }
-    vd[e] = d;
-  }
+  // p = 2^(s*descale - m) <= 256, split into hi + lo fp16 terms by round-toward-zero packed
+  // converts (|p - hi - lo| < 2^-20 p); PV rows (head, 0) take hi, (head, 1) lo.
+  const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0], descale, neg_m));
+  const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[1], descale, neg_m));
+  st.l_acc += p0 + p1;
+  const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+  const half2v lo = __builtin_bit_cast(
+      half2v, __builtin_amdgcn_cvt_pkrtz(p0 - static_cast<float>(hi[0]), p1 - static_cast<float>(hi[1])));
+  // ---- P: scores layout (lane = token) -> PV A-operand layout (lane = row, 8 tokens) through
+  // the wavefront's LDS rows.  PV token order k = 2c + eta, i.e. k = 8g' + e is token
+  // 16 (e & 1) + 4 g' + (e >> 1). ----
+  // (LDS operations of one wavefront complete in issue order, and the compiler keeps the
+  // read after the possibly aliasing writes.)
+  p_w[(4 * ln.g + 0) * kPStride + ln.c] = as_u32(hi);
+  p_w[(4 * ln.g + 1) * kPStride + ln.c] = as_u32(lo);
+  const half8 ap = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(p_w + ln.c * kPStride + 4 * ln.g));
+  // ---- V: B operand column c <-> dim 8c + v, k = 8g + e <-> token T(g, e) as above.  The
+  // scale pair of (k = 8g+2p, 8g+2p+1) is (half 0, half 1) token 4g+p, block c >> 1.
+  // Masked tokens need no zeroing: p = 0 there and every code and scale decodes finite. ----
+  const uint32_t w0 = L.vs[0] & 0x7F7F7F7Fu, w1 = L.vs[1] & 0x7F7F7F7Fu;
   half2v sig[4];
+  uint32_t ev[4], od[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const uint32_t w = L.vs[p >> 1] & 0x7F7F7F7Fu;
-    const int j0 = 2 * (p & 1);
-    const uint32_t sel = 0x0Cu | (uint32_t(j0) << 8) | (0x0Cu << 16) | (uint32_t(j0 + 1) << 24);
-    sig[p] = as_half2(__builtin_amdgcn_perm(w, w, sel) >> 1);
+    const uint32_t sel = 0x0Cu | (uint32_t(p) << 8) | (0x0Cu << 16) | (uint32_t(4 + p) << 24);
+    sig[p] = as_half2(__builtin_amdgcn_perm(w1, w0, sel) >> 1);
+    ev[p] = nib_even(L.vd[2 * p], L.vd[2 * p + 1]);
+    od[p] = nib_odd(L.vd[2 * p], L.vd[2 * p + 1]);
   }
-  pv_pair<0>(vd, sig, ap, st);
-  pv_pair<1>(vd, sig, ap, st);
-  pv_pair<2>(vd, sig, ap, st);
-  pv_pair<3>(vd, sig, ap, st);
+  pv_pair<0>(ev, od, sig, ap, st);
+  pv_pair<1>(ev, od, sig, ap, st);
+  pv_pair<2>(ev, od, sig, ap, st);
+  pv_pair<3>(ev, od, sig, ap, st);
 }
 
 // Device-coherent 64-bit store / load (relaxed, device scope): they bypass the
@@ -398,8 +426,17 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
+  Lane ln;
+  ln.c = c;
+  ln.g = g;
+  ln.k_off = KBF16 ? static_cast<uint32_t>(c * kHeadDim * 2 + 64 * g) : static_cast<uint32_t>(c * 64 + 16 * g);
+  ln.ks_off = static_cast<uint32_t>((c >> 2) * 32 + 8 * g);
+  ln.ks_shift = static_cast<uint32_t>(8 * (c & 3));
+  ln.v_off = static_cast<uint32_t>(256 * g + 4 * c);
+  ln.vs_off = static_cast<uint32_t>(32 * g + 4 * (c >> 1));
 
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[4][4][kHeadDim];   // [head][term][dim]
+  __shared__ __attribute__((aligned(16))) uint32_t p_lds[kMaxWaves][kPWords];
   __shared__ float q_descale[4];
   __shared__ float red_m[kMaxWaves][4], red_l[kMaxWaves][4];
   __shared__ __attribute__((aligned(16))) float red_o[kMaxWaves][4][kHeadDim];
@@ -407,7 +444,7 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   __shared__ int mrg_last;
 
   const int64_t unit = static_cast<int64_t>(b) * a.hkv + h;
-  const int32_t* ptab = a.page_table + static_cast<int64_t>(b) * a.max_pages_per_seq;
+  const const_i32_ptr ptab = __builtin_bit_cast(const_i32_ptr, a.page_table) + static_cast<int64_t>(b) * a.max_pages_per_seq;
 
   // ---- start every independent memory access first: query row, sequence length, pages ----
   const bool q_wave = wave < 4;                 // wavefronts 0..3 prepare query heads 4h..4h+3
@@ -429,14 +466,14 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   const int step = kIterTok * nw;
   int t0 = t_begin + kIterTok * wave;
   IterLoads<KBF16> buf0, buf1;
-  HalfAddr ha0[2], ha1[2];
+  HalfBase hb0[2], hb1[2];
   if (t0 < t_lim) {
-    half_addrs(a, load_pages(a, ptab, t0, t_lim), h, ha0);
-    issue_loads<KBF16>(a, ha0, c, g, buf0);
+    half_bases<KBF16>(a, load_pages(a, ptab, t0, t_lim), h, hb0);
+    issue_loads<KBF16>(hb0, ln, buf0);
   }
   if (PIPE2 && t0 + step < t_lim) {
-    half_addrs(a, load_pages(a, ptab, t0 + step, t_lim), h, ha1);
-    issue_loads<KBF16>(a, ha1, c, g, buf1);
+    half_bases<KBF16>(a, load_pages(a, ptab, t0 + step, t_lim), h, hb1);
+    issue_loads<KBF16>(hb1, ln, buf1);
   }
   IterPages pnext = load_pages(a, ptab, t0 + (PIPE2 ? 2 : 1) * step, t_lim > 0 ? t_lim : 1);
 
@@ -507,51 +544,58 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   for (int v = 0; v < 8; ++v) st.acc[v] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
   if (!empty) {
-    // B operand of QK (Q'^T): lane (c, g) = column c = (head c>>2, term c&3); instruction u,
-    // item e <-> dim 32g + 8u + e.
-    u32x4 qb[4];
+    // A operand of QK (Q'): lane (c, g) = row c = (head c>>2, term c&3); instruction u, item
+    // e <-> dim 32g + 8u + e (the same dim order as the key codes a lane loads).
+    u32x4 qa[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      qb[u] = *reinterpret_cast<const u32x4*>(&q_lds[c >> 2][c & 3][32 * g + 8 * u]);
-    const float descale = q_descale[c >> 2];
+      qa[u] = *reinterpret_cast<const u32x4*>(&q_lds[c >> 2][c & 3][32 * g + 8 * u]);
+    const float descale = q_descale[g];        // the lane's scores belong to head g
+    // P rows (head, term 2 or 3) stay zero
+    uint32_t* p_w = p_lds[wave];
+    for (int i = lane; i < kPWords; i += 64) p_w[i] = 0u;
+    bool vm[2];
 
     // Software pipeline: two register buffers hold the next two iterations' cache data and
     // the page entries of the iteration after them are already loaded, so neither the
     // vector loads nor the page lookups sit on the critical path.
     if constexpr (!PIPE2) {
       while (t0 < t_end) {
-        compute_iter<KBF16>(buf0, ha0, qb, descale, t0, t_end, c, g, st);
+        valid_tokens(hb0, t0, t_end, c, vm);
+        compute_iter<KBF16>(buf0, vm, qa, descale, ln, st, p_w);
         t0 += step;
         if (t0 >= t_end) break;
-        half_addrs(a, pnext, h, ha0);
-        issue_loads<KBF16>(a, ha0, c, g, buf0);
+        half_bases<KBF16>(a, pnext, h, hb0);
+        issue_loads<KBF16>(hb0, ln, buf0);
         pnext = load_pages(a, ptab, t0 + step, t_end);
       }
     }
     while (PIPE2 && t0 < t_end) {
-      compute_iter<KBF16>(buf0, ha0, qb, descale, t0, t_end, c, g, st);
+      valid_tokens(hb0, t0, t_end, c, vm);
+        compute_iter<KBF16>(buf0, vm, qa, descale, ln, st, p_w);
       t0 += step;
       if (t0 >= t_end) break;
       if (t0 + step < t_end) {
-        half_addrs(a, pnext, h, ha0);
-        issue_loads<KBF16>(a, ha0, c, g, buf0);
+        half_bases<KBF16>(a, pnext, h, hb0);
+        issue_loads<KBF16>(hb0, ln, buf0);
         pnext = load_pages(a, ptab, t0 + 2 * step, t_end);
       }
-      compute_iter<KBF16>(buf1, ha1, qb, descale, t0, t_end, c, g, st);
+      valid_tokens(hb1, t0, t_end, c, vm);
+      compute_iter<KBF16>(buf1, vm, qa, descale, ln, st, p_w);
       t0 += step;
       if (t0 + step < t_end) {
-        half_addrs(a, pnext, h, ha1);
-        issue_loads<KBF16>(a, ha1, c, g, buf1);
+        half_bases<KBF16>(a, pnext, h, hb1);
+        issue_loads<KBF16>(hb1, ln, buf1);
         pnext = load_pages(a, ptab, t0 + 2 * step, t_end);
       }
     }
   }
 
   // ---------------- wavefront partials -> LDS -> workgroup partial ----------------
-  const float l_tot = rows_sum(st.l_acc);
-  if (g == 0 && (c & 3) == 0) {
-    red_m[wave][c >> 2] = st.m_ref;
-    red_l[wave][c >> 2] = l_tot;
+  const float l_tot = row16_sum(st.l_acc);
+  if (c == 0) {
+    red_m[wave][g] = st.m_ref;
+    red_l[wave][g] = l_tot;
   }
   {
     float4* dst = reinterpret_cast<float4*>(&red_o[wave][g][8 * c]);
@@ -681,6 +725,7 @@ hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, int32_t B, int3
   a.hkv = L.num_kv_heads;
   a.hq = Hq;
   a.page_size = L.page_size;
+  a.page_shift = (L.page_size & (L.page_size - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(L.page_size)) : -1;
   a.num_pages = L.num_pages;
   a.max_pages_per_seq = max_pages_per_seq;
   const int64_t cap_pages = static_cast<int64_t>(max_pages_per_seq) * L.page_size;
