@@ -329,9 +329,11 @@ class PrefillAppend:
         ok = bool(np.array_equal(cache.inv_smooth.cpu().numpy(), r)
                   and np.array_equal(cache.gscale.cpu().numpy(), g))
         n_rows = 0
+        # keys row-major; values quad-interleaved (word w of token t at ((t/4)*16 + w)*16 + (t%4)*4)
+        vq = cache.v_data.view(self.num_pages, self.hkv, PAGE // 4, 16, 4, 4).permute(0, 1, 2, 4, 3, 5)
         views = (cache.k_data.view(self.num_pages, self.hkv, PAGE, 64),
                  cache.k_scales.view(self.num_pages, self.hkv, PAGE // 4, 8, 4),
-                 cache.v_data.view(self.num_pages, self.hkv, PAGE, 64),
+                 vq.reshape(self.num_pages, self.hkv, PAGE, 64),
                  cache.v_scales.view(self.num_pages, self.hkv, PAGE // 4, 8, 4))
         t = np.arange(self.T)
         for b in (0, self.B - 1):

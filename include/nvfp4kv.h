@@ -39,9 +39,15 @@
  *
  * Cache layout of one layer (page_size tokens per page, multiple of 16; a contiguous cache is
  * num_pages = batch with one page of max-context tokens per sequence):
- *   NVFP4 codes   u8  [num_pages][Hkv][page_size][64]    (K and V alike)
- *                 byte k of a row = element 2k in the low nibble | element 2k+1 in the high
- *                 nibble; nibble = sign<<3 | E2M1 magnitude code.
+ *   NVFP4 codes   64 bytes per (token, head): byte k = element 2k in the low nibble |
+ *                 element 2k+1 in the high nibble; nibble = sign<<3 | E2M1 magnitude code.
+ *                 Word w (4 bytes, elements 8w..8w+7) of token t of a page:
+ *                   keys   u8 [num_pages][Hkv][page_size][64]: byte 64t + 4w of the
+ *                          (page, head) block (row-major);
+ *                   values u8 [num_pages][Hkv][page_size/4][16][4][4]: byte
+ *                          ((t/4)*16 + w)*16 + (t%4)*4 of the block (quad-interleaved: the
+ *                          four tokens of a quad side by side per word, so a decode lane
+ *                          reads one word of four tokens with one 16-byte load).
  *   NVFP4 scales  u8  [num_pages][Hkv][page_size/4][8][4] (K and V alike)
  *                 the E4M3FN scale of block b (elements 16b..16b+15) of token t of a page is
  *                 byte ((t/4)*8 + b)*4 + t%4 of that (page, head).

@@ -20,8 +20,9 @@
 //       (query head i, term t) with p split into hi + lo fp16 terms.
 // The score layout produced by QK (lane (c, g) holds tokens 4g..4g+3 of each 16-token half
 // for column c) is exactly the A-operand layout PV needs, so no transpose is required.
-// V codes are read token-major: lane (c, g) fetches the dword of dims 8c..8c+7 of its 8
-// tokens and serves column c of PV instruction v as dim 8c + v.
+// V codes are stored quad-interleaved (the four tokens of a quad side by side per 8-dim
+// word), so lane (c, g) fetches word c of its four tokens of each half with one 16-byte load
+// and serves column c of PV instruction v as dim 8c + v.
 // Dequantisation: nibble -> fp16 (value * 2^8) with the gfx950 scaled FP4 convert (it
 // applies only the exponent of its scale operand, so the scale is 2^8), E4M3 scale -> fp16
 // (sigma * 2^-8) by a bit shift, one v_pk_mul_f16 per element pair; the product is the exact
@@ -124,7 +125,7 @@ struct Lane {
   uint32_t k_off;       // K codes: token c, dims 32g..32g+31 (16 B); BF16 keys: 64 B
   uint32_t ks_off;      // K scales: the quad of token c, blocks 2g and 2g+1 (8 B)
   uint32_t ks_shift;    // bit position of token c's byte in those scale dwords
-  uint32_t v_off;       // V codes: token 4g of the half, dims 8c..8c+7 (4 B; + 64 j for token 4g+j)
+  uint32_t v_off;       // V codes: words c (dims 8c..8c+7) of tokens 4g..4g+3 of the half (16 B)
   uint32_t vs_off;      // V scales: quad g of the half, block c >> 1 (4 B)
 };
 
@@ -218,9 +219,9 @@ __device__ __forceinline__ void issue_loads(const HalfBase (&hb)[2], const Lane&
         L.k.kr[eta][u] =
             __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hb[eta].kc, ln.k_off + 16 * u, 0, kNonTemporal));
     }
+    const u32x4 v4 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hb[eta].vc, ln.v_off, 0, kNonTemporal));
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      L.vd[2 * j + eta] = __builtin_amdgcn_raw_buffer_load_b32(hb[eta].vc, ln.v_off + 64 * j, 0, kNonTemporal);
+    for (int j = 0; j < 4; ++j) L.vd[2 * j + eta] = v4[j];
     L.vs[eta] = __builtin_amdgcn_raw_buffer_load_b32(hb[eta].vs, ln.vs_off, 0, 0);
   }
 }
@@ -432,7 +433,7 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   ln.k_off = KBF16 ? static_cast<uint32_t>(c * kHeadDim * 2 + 64 * g) : static_cast<uint32_t>(c * 64 + 16 * g);
   ln.ks_off = static_cast<uint32_t>((c >> 2) * 32 + 8 * g);
   ln.ks_shift = static_cast<uint32_t>(8 * (c & 3));
-  ln.v_off = static_cast<uint32_t>(256 * g + 4 * c);
+  ln.v_off = static_cast<uint32_t>(16 * (16 * g + c));
   ln.vs_off = static_cast<uint32_t>(32 * g + 4 * (c >> 1));
 
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[4][4][kHeadDim];   // [head][term][dim]

@@ -30,6 +30,7 @@ struct AppendArgs {
   const float* gscale;        // &g_K or &g_V
   uint32_t flags;             // key transform flags (0 for V)
   int32_t fmt;                // NVKV_FMT_*
+  int32_t quad_words;         // 1: codes in the quad-interleaved word layout (NVFP4 values)
 };
 
 struct AppendPair {
@@ -69,7 +70,15 @@ __global__ void __launch_bounds__(256) k_quantize_append(AppendPair p) {
 
   uint32_t lo, hi;
   const uint32_t S = encode_block(y, gsc, lo, hi);
-  *reinterpret_cast<uint2*>(a.codes + row_index * 64 + blk * 8) = make_uint2(lo, hi);
+  if (!a.quad_words) {
+    *reinterpret_cast<uint2*>(a.codes + row_index * 64 + blk * 8) = make_uint2(lo, hi);
+  } else {
+    // words 2blk, 2blk+1 of token `off`: byte ((off/4)*16 + w)*16 + (off%4)*4 of the
+    // (page, head) block, which starts at the same place as in the row-major layout
+    uint8_t* wq = a.codes + (row_index - (off & 3)) * 64 + 32 * blk + 4 * (off & 3);
+    *reinterpret_cast<uint32_t*>(wq) = lo;
+    *reinterpret_cast<uint32_t*>(wq + 16) = hi;
+  }
   const int64_t sbase = (static_cast<int64_t>(page) * a.hkv + h) * a.page_size * 8;
   a.scales[sbase + ((off >> 2) * 8 + blk) * 4 + (off & 3)] = static_cast<uint8_t>(S);
 }
@@ -164,10 +173,10 @@ hipError_t launch_quantize_append(const nvkv_layer& L, const uint16_t* k_new, co
   const int64_t max_slot = static_cast<int64_t>(L.num_pages) * L.page_size;
   p.a[0] = AppendArgs{k_new, slots, rows, L.num_kv_heads, L.page_size, max_slot,
                       static_cast<uint8_t*>(L.k_data), L.k_scales, L.k_inv_smooth,
-                      L.global_scale + 0, L.k_fmt == NVKV_FMT_NVFP4 ? L.k_flags : 0u, L.k_fmt};
+                      L.global_scale + 0, L.k_fmt == NVKV_FMT_NVFP4 ? L.k_flags : 0u, L.k_fmt, 0};
   p.a[1] = AppendArgs{v_new, slots, rows, L.num_kv_heads, L.page_size, max_slot,
                       static_cast<uint8_t*>(L.v_data), L.v_scales, nullptr,
-                      L.global_scale + 1, 0u, L.v_fmt};
+                      L.global_scale + 1, 0u, L.v_fmt, 1};
   const int wg = (rows + kRowsPerWg - 1) / kRowsPerWg;
   p.wg_k = wg;
   hipLaunchKernelGGL(k_quantize_append, dim3(2 * wg), dim3(256), 0, stream, p);

@@ -43,10 +43,21 @@ class Pages:
         return int(self.table[b, t // self.page_size]), t % self.page_size
 
 
-def rows_from_cache(codes_u8: np.ndarray, scales_u8: np.ndarray, pages: Pages, hkv: int, b: int, T: int):
+def codes_view(codes_u8: np.ndarray, pages: Pages, hkv: int, values: bool) -> np.ndarray:
+    """Codes of one layer as [page][head][token in page][64] (header layout: keys row-major,
+    values quad-interleaved: word w of token t at ((t/4)*16 + w)*16 + (t%4)*4)."""
+    ps = pages.page_size
+    if not values:
+        return codes_u8.reshape(pages.num_pages, hkv, ps, 64)
+    q = codes_u8.reshape(pages.num_pages, hkv, ps // 4, 16, 4, 4)        # [pg][h][quad][w][j][byte]
+    return q.transpose(0, 1, 2, 4, 3, 5).reshape(pages.num_pages, hkv, ps, 64)
+
+
+def rows_from_cache(codes_u8: np.ndarray, scales_u8: np.ndarray, pages: Pages, hkv: int, b: int, T: int,
+                    values: bool = False):
     """Logical rows of sequence b, tokens [0, T): codes [T][Hkv][64], scales [T][Hkv][8]."""
     ps = pages.page_size
-    codes = codes_u8.reshape(pages.num_pages, hkv, ps, 64)
+    codes = codes_view(codes_u8, pages, hkv, values)
     sc = scales_u8.reshape(pages.num_pages, hkv, ps // 4, 8, 4)
     out_c = np.empty((T, hkv, 64), np.uint8)
     out_s = np.empty((T, hkv, 8), np.uint8)
@@ -57,10 +68,11 @@ def rows_from_cache(codes_u8: np.ndarray, scales_u8: np.ndarray, pages: Pages, h
     return out_c, out_s
 
 
-def rows_from_cache_vec(codes_u8: np.ndarray, scales_u8: np.ndarray, pages: Pages, hkv: int, b: int, T: int):
+def rows_from_cache_vec(codes_u8: np.ndarray, scales_u8: np.ndarray, pages: Pages, hkv: int, b: int, T: int,
+                        values: bool = False):
     """Vectorised rows_from_cache for long sequences."""
     ps = pages.page_size
-    codes = codes_u8.reshape(pages.num_pages, hkv, ps, 64)
+    codes = codes_view(codes_u8, pages, hkv, values)
     sc = scales_u8.reshape(pages.num_pages, hkv, ps // 4, 8, 4)
     t = np.arange(T)
     pg = pages.table[b, t // ps]

@@ -89,7 +89,7 @@ def test_quantize_bit_exact(lib, name, flags, paged):
         gc, gs = P.rows_from_cache_vec(kd, ksd, pages, c["hkv"], b, c["T"])
         assert np.array_equal(gs, ks[b]), f"K scales differ, seq {b}"
         assert np.array_equal(gc, kc[b]), f"K codes differ, seq {b}"
-        gc, gs = P.rows_from_cache_vec(vd, vsd, pages, c["hkv"], b, c["T"])
+        gc, gs = P.rows_from_cache_vec(vd, vsd, pages, c["hkv"], b, c["T"], values=True)
         assert np.array_equal(gs, vs[b]), f"V scales differ, seq {b}"
         assert np.array_equal(gc, vc[b]), f"V codes differ, seq {b}"
 
@@ -195,7 +195,7 @@ def test_bf16_keys_nvfp4_values(lib, paged):
     for b in range(c["B"]):
         assert np.array_equal(P.bf16_rows_from_cache(kd, pages, c["hkv"], b, c["T"]), k[b])
         gc, gs = P.rows_from_cache_vec(cache.v_data.cpu().numpy(), cache.v_scales.cpu().numpy(), pages,
-                                       c["hkv"], b, c["T"])
+                                       c["hkv"], b, c["T"], values=True)
         assert np.array_equal(gc, vc[b]) and np.array_equal(gs, vs[b])
     seq = [c["T"], 1000, 17, 2048]
     ref, vmax = oracle_decode(q, so, 0, kc, ks, vc, vs, go, seq, c["hkv"], k_bf16=k)
@@ -236,7 +236,8 @@ def test_special_rows_bit_exact(lib):
     torch.cuda.synchronize()
     gc, gs = P.rows_from_cache_vec(cache.k_data.cpu().numpy(), cache.k_scales.cpu().numpy(), pages, hkv, 0, N)
     assert np.array_equal(gs, ks) and np.array_equal(gc, kc)
-    gc, gs = P.rows_from_cache_vec(cache.v_data.cpu().numpy(), cache.v_scales.cpu().numpy(), pages, hkv, 0, N)
+    gc, gs = P.rows_from_cache_vec(cache.v_data.cpu().numpy(), cache.v_scales.cpu().numpy(), pages, hkv, 0, N,
+                                   values=True)
     assert np.array_equal(gs, vs) and np.array_equal(gc, vc)
     assert 0 in ks[:, 0, 0] and 0x7E in ks[:, 0, 0] and np.any((ks > 0) & (ks < 8))
 
@@ -262,10 +263,10 @@ def test_append_canaries_and_skipped_slots(lib):
     after = [t.cpu().numpy() for t in (cache.k_data, cache.k_scales, cache.v_data, cache.v_scales)]
     written = set(int(x) for i, x in enumerate(slots) if i not in (3, 7, 8))
     ps = pages.page_size
-    for arr_b, arr_a, row_bytes, is_scale in zip(before, after, (64, 8, 64, 8), (False, True, False, True)):
-        if not is_scale:
-            b3 = arr_b.reshape(pages.num_pages, hkv, ps, row_bytes)
-            a3 = arr_a.reshape(pages.num_pages, hkv, ps, row_bytes)
+    for idx, (arr_b, arr_a) in enumerate(zip(before, after)):
+        if idx in (0, 2):                                   # K codes, V codes (their layouts)
+            b3 = P.codes_view(arr_b, pages, hkv, values=idx == 2)
+            a3 = P.codes_view(arr_a, pages, hkv, values=idx == 2)
             for pg in range(pages.num_pages):
                 for off in range(ps):
                     same = np.array_equal(b3[pg, :, off], a3[pg, :, off])
@@ -278,6 +279,38 @@ def test_append_canaries_and_skipped_slots(lib):
                     same = np.array_equal(b5[pg, :, off // 4, :, off % 4], a5[pg, :, off // 4, :, off % 4])
                     if (pg * ps + off) not in written:
                         assert same
+
+
+def test_cache_byte_positions(lib):
+    """Codes and scales sit where the header's layout formulas put them, checked byte by byte
+    with the formulas written out (keys row-major, values quad-interleaved, scales
+    [quad][block][token in quad]) for tokens at every position in a quad and page."""
+    rng = np.random.default_rng(31)
+    hkv, N = 2, 37
+    pages = P.Pages(3, 32, True, spare=1)
+    cache = lib.CacheLayer(pages.num_pages, pages.page_size, hkv, k_flags=0, fill=0)
+    cache.gscale.fill_(0.02)
+    k = S.bf16_round(rng.standard_normal((N, hkv, 128)).astype(np.float32))
+    v = S.bf16_round(rng.standard_normal((N, hkv, 128)).astype(np.float32))
+    slots = np.concatenate([pages.slots(0, 0, 20), pages.slots(2, 3, 20)])
+    lib.quantize_append_kv(cache.struct(), P.to_dev_u16(k), P.to_dev_u16(v), P.to_dev_i32(slots), N)
+    torch.cuda.synchronize()
+    kc, ks = O.quantize_rows(S.bf16_to_f32(k), np.float32(0.02))
+    vc, vs = O.quantize_rows(S.bf16_to_f32(v), np.float32(0.02))
+    kd, vd = cache.k_data.cpu().numpy(), cache.v_data.cpu().numpy()
+    ksd, vsd = cache.k_scales.cpu().numpy(), cache.v_scales.cpu().numpy()
+    ps = pages.page_size
+    for n, slot in enumerate(slots):
+        pg, t = int(slot) // ps, int(slot) % ps
+        for h in range(hkv):
+            blk = (pg * hkv + h) * ps                     # tokens before this (page, head) block
+            for w in range(16):
+                for by in range(4):
+                    assert kd[blk * 64 + 64 * t + 4 * w + by] == kc[n, h, 4 * w + by]
+                    assert vd[blk * 64 + ((t // 4) * 16 + w) * 16 + (t % 4) * 4 + by] == vc[n, h, 4 * w + by]
+            for b8 in range(8):
+                assert ksd[blk * 8 + ((t // 4) * 8 + b8) * 4 + t % 4] == ks[n, h, b8]
+                assert vsd[blk * 8 + ((t // 4) * 8 + b8) * 4 + t % 4] == vs[n, h, b8]
 
 
 def test_error_paths_on_gpu_host(lib):
