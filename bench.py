@@ -5,10 +5,11 @@ Default workload ("step36"): one decode step of a Qwen3-8B-shaped attention cach
   - shape: 36 layers x 8 KV heads x head_dim 128, 32 query heads, batch 4 x 2304 cached
     tokens, 16-token pages with a shuffled page table;
   - cache: keys and values NVFP4, static per-channel key smoothing;
-  - a step runs, for every layer, quantize_append_kv of the new token of each sequence and
-    then decode_attention_nvfp4 over all 2304 tokens: quantise -> pack -> split-K decode ->
-    merge;
-  - steps replay HIP graphs over 3 rotating copies of the 36-layer cache (1.15 GB, beyond the
+  - a step runs, for every layer, one decode_append_attention_nvfp4 call: the new token of
+    each sequence is quantised and packed into the cache and attention runs over all 2304
+    tokens (quantise -> pack -> split-K decode -> merge) in one launch; --separate times the
+    same step as quantize_append_kv + decode_attention_nvfp4 per layer (also reported);
+  - steps replay HIP graphs over 4 rotating copies of the 36-layer cache (1.5 GB, beyond the
     256 MB last-level cache).
 Other workloads (run by hand with --workload):
   - step36-vonly, step36-hadamard, step36-had-smooth: the same step with other cache formats;
@@ -59,14 +60,17 @@ def parse():
                     help="comma-separated split sizes: report the decode launch time of each")
     ap.add_argument("--profile-pass", action="store_true",
                     help="short run for rocprofv3: few steps, no CPU baseline")
+    ap.add_argument("--separate", action="store_true",
+                    help="decode step as two calls per layer (quantize_append_kv, then "
+                         "decode_attention_nvfp4) instead of the fused decode_append_attention_nvfp4")
     return ap.parse_args()
 
 
 VARIANTS = {
-    "step36": dict(cfg="step36", k_fmt=1, flags=1, copies=3, label="K+V NVFP4, K smoothed"),
-    "step36-vonly": dict(cfg="step36", k_fmt=0, flags=0, copies=3, label="K bf16, V NVFP4"),
-    "step36-hadamard": dict(cfg="step36", k_fmt=1, flags=2, copies=3, label="K+V NVFP4, K Hadamard-128"),
-    "step36-had-smooth": dict(cfg="step36", k_fmt=1, flags=3, copies=3,
+    "step36": dict(cfg="step36", k_fmt=1, flags=1, copies=4, label="K+V NVFP4, K smoothed"),
+    "step36-vonly": dict(cfg="step36", k_fmt=0, flags=0, copies=4, label="K bf16, V NVFP4"),
+    "step36-hadamard": dict(cfg="step36", k_fmt=1, flags=2, copies=4, label="K+V NVFP4, K Hadamard-128"),
+    "step36-had-smooth": dict(cfg="step36", k_fmt=1, flags=3, copies=4,
                               label="K+V NVFP4, K smoothed + Hadamard-128"),
     "long": dict(cfg="long", k_fmt=1, flags=1, copies=1, label="K+V NVFP4, K smoothed"),
     "prefill": dict(cfg="prefill", k_fmt=1, flags=1, copies=1, label="K smoothed"),
@@ -96,9 +100,8 @@ class DecodeStep:
     """Decode-step workloads: per layer, append the new token of every sequence, then attend."""
 
     metric = METRIC
-    kernel_label = "k_decode (decode_attention_nvfp4: split-K decode + in-kernel cross-split merge), per layer"
 
-    def __init__(self, name, copies, split_tokens):
+    def __init__(self, name, copies, split_tokens, fused=True):
         import torch
         import nvfp4_bit_kv_amd as nk
         from synth import kv_inputs as S
@@ -110,6 +113,11 @@ class DecodeStep:
         self.k_fmt, self.flags = v["k_fmt"], v["flags"]
         self.copies = copies or v["copies"]
         self.split_tokens = split_tokens
+        self.mode = "fused" if fused else "separate"
+        self.kernel_label = (
+            "k_decode<append> (decode_append_attention_nvfp4: new-token quantise/append + split-K decode + "
+            "in-kernel cross-split merge, one launch), per layer" if fused else
+            "k_decode (decode_attention_nvfp4: split-K decode + in-kernel cross-split merge), per layer")
         B, T, hkv = self.B, self.T, self.hkv
         self.pps = (T + PAGE - 1) // PAGE
         self.num_pages = B * self.pps
@@ -180,27 +188,40 @@ class DecodeStep:
         torch.cuda.synchronize()
 
     # one layer of the hot path: append the new token, then attend over the whole cache
-    def layer_step(self, cp, l, decode_only=False):
+    # mode "fused": one decode_append_attention_nvfp4 call; "separate": quantize_append_kv of
+    # the new token, then decode_attention_nvfp4; "decode": decode_attention_nvfp4 only
+    def layer_step(self, cp, l, mode=None):
         nk = self.nk
+        mode = mode or self.mode
         cache, Ls = self.caches[cp][l]
-        if not decode_only:
+        if mode == "fused":
+            nk.decode_append_attention_nvfp4(Ls, self.q[l], self.k_new[l], self.v_new[l], self.B, self.hq, self.table,
+                                             self.pps, self.seq_lens, self.T, SM_SCALE, self.out[l], self.ws,
+                                             self.wsb, self.split_tokens)
+            return
+        if mode == "separate":
             nk.quantize_append_kv(Ls, self.k_new[l], self.v_new[l], self.new_slots, self.B)
         nk.decode_attention_nvfp4(Ls, self.q[l], self.B, self.hq, self.table, self.pps, self.seq_lens, self.T,
                                   SM_SCALE, self.out[l], self.ws, self.wsb, self.split_tokens)
 
-    def step(self, cp):
+    def step(self, cp, mode=None):
         for l in range(self.L):
-            self.layer_step(cp, l)
+            self.layer_step(cp, l, mode)
 
     def snapshot(self):
         return self.out.clone()
 
     # algorithmic bytes (what the method must move)
-    def launch_bytes(self):
-        """One decode_attention_nvfp4 call: every cached K and V row with its scales once, the
-        query (bf16) in and the output (fp32) out."""
+    def decode_bytes(self):
+        """One decode over the cache: every cached K and V row with its scales once, the query
+        (bf16) in and the output (fp32) out."""
         per_tok = row_bytes(self.k_fmt) + 72
         return self.B * self.hkv * self.T * per_tok + self.B * self.hq * (256 + 512)
+
+    def launch_bytes(self):
+        """Bytes of one launch of the dominant kernel: the fused call also appends the new
+        token (bf16 K and V rows in, their codes and scales out)."""
+        return self.decode_bytes() + (self.append_bytes_per_layer() if self.mode == "fused" else 0)
 
     def append_bytes_per_layer(self):
         return self.B * self.hkv * ((256 + row_bytes(self.k_fmt)) + (256 + 72))
@@ -212,7 +233,7 @@ class DecodeStep:
         return self.B
 
     def launch_times(self, reps):
-        return decode_launch_times(self.torch, self, reps)
+        return decode_launch_times(self.torch, self, reps, self.mode if self.mode == "fused" else "decode")
 
     def check(self):
         return decode_check_against_oracle(self)
@@ -400,11 +421,11 @@ def time_graphs(torch, graphs, steps, warmup):
     return e0.elapsed_time(e1)
 
 
-def decode_launch_times(torch, wl, reps):
-    """Average duration of one decode_attention_nvfp4 call (its kernel back to back, no host
-    gaps): a HIP graph of the decode calls of all layers of a cache copy is replayed between
-    two HIP events on the launch stream; one sample per replay, divided by the layer count."""
-    graphs = [capture(torch, lambda cp=cp: [wl.layer_step(cp, l, decode_only=True) for l in range(wl.L)])
+def decode_launch_times(torch, wl, reps, mode="decode"):
+    """Average duration of one decode launch (the kernel back to back, no host gaps): a HIP
+    graph of the calls of all layers of a cache copy is replayed between two HIP events on
+    the launch stream; one sample per replay, divided by the layer count."""
+    graphs = [capture(torch, lambda cp=cp: [wl.layer_step(cp, l, mode) for l in range(wl.L)])
               for cp in range(wl.copies)]
     for gr in graphs:
         gr.replay()
@@ -427,7 +448,7 @@ def sweep_splits(torch, wl, splits):
         wl.split_tokens = sp
         wl.wsb = wl.nk.decode_workspace_bytes(wl.B, wl.hq, wl.hkv, wl.T, sp)
         wl.ws = torch.zeros(max(wl.wsb, 256), dtype=torch.uint8, device="cuda")
-        d = decode_launch_times(torch, wl, reps=10)
+        d = decode_launch_times(torch, wl, reps=10, mode=wl.mode if wl.mode == "fused" else "decode")
         res[sp] = (float(np.mean(d)) * 1e6, float(np.min(d)) * 1e6)
         print(f"[sweep] split_tokens={sp}: avg {res[sp][0]:.2f} us  min {res[sp][1]:.2f} us  "
               f"-> {wl.launch_bytes() / np.mean(d) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
@@ -543,7 +564,7 @@ def main():
     if VARIANTS[args.workload]["cfg"] == "prefill":
         wl = PrefillAppend(args.workload)
     else:
-        wl = DecodeStep(args.workload, args.copies, args.split_tokens)
+        wl = DecodeStep(args.workload, args.copies, args.split_tokens, fused=not args.separate)
 
     # eager pass and its result, then one graph per cache copy
     wl.step(0)
@@ -556,6 +577,18 @@ def main():
     torch.cuda.synchronize()
     replay_ok = bool(torch.equal(wl.snapshot(), eager0))
     del eager0
+    # the pages' timing protocol: 3 repetitions x 30 runs; median and spread per step
+    reps = []
+    for _ in range(3):
+        reps.append(time_graphs(torch, graphs, 30, 3) / 30)
+    protocol = {"repetitions": 3, "runs": 30, "median_ms": round(float(np.median(reps)), 5),
+                "min_ms": round(float(np.min(reps)), 5), "max_ms": round(float(np.max(reps)), 5)}
+    # the same decode step as two calls per layer, for comparison
+    separate_ms = None
+    if isinstance(wl, DecodeStep) and wl.mode == "fused":
+        sgraphs = [capture(torch, lambda cp=cp: wl.step(cp, "separate")) for cp in range(wl.copies)]
+        separate_ms = round(time_graphs(torch, sgraphs, max(10, args.steps // 4), 3) / max(10, args.steps // 4), 5)
+        del sgraphs
 
     print("[bench] per-launch timing of the dominant kernel", file=sys.stderr, flush=True)
     durs = wl.launch_times(max(3, min(30, args.steps // 5)))
@@ -598,6 +631,8 @@ def main():
         },
         "cpu_baseline": base,
         "graph_replay_matches_eager": replay_ok,
+        "timing_protocol": protocol,
+        "separate_calls_ms_per_step": separate_ms,
         "oracle_check": check,
     }
     print(json.dumps(line), flush=True)

@@ -136,7 +136,8 @@ NVKV_API nvkv_status nvkv_quantize_append_kv(const nvkv_layer *layer,
                                     const int32_t *slot_mapping, int32_t N, void *stream);
 
 /*
- * Workspace needed by nvkv_decode_attention_nvfp4 for the same (B, Hq, Hkv, max_seq_len,
+ * Workspace needed by nvkv_decode_attention_nvfp4 (and by
+ * nvkv_decode_append_attention_nvfp4) for the same (B, Hq, Hkv, max_seq_len,
  * split_tokens).  split_tokens = 0 selects the library's own split size; otherwise it must
  * be a positive multiple of 32 (tokens handled by one workgroup).  Returns 0 for invalid arguments.
  */
@@ -166,6 +167,32 @@ NVKV_API size_t nvkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, 
  */
 NVKV_API nvkv_status nvkv_decode_attention_nvfp4(const nvkv_layer *layer,
                                         const uint16_t *q, int32_t B, int32_t Hq,
+                                        const int32_t *page_table, int32_t max_pages_per_seq,
+                                        const int32_t *seq_lens, int32_t max_seq_len,
+                                        float sm_scale, float *out,
+                                        void *workspace, size_t workspace_bytes,
+                                        int32_t split_tokens, void *stream);
+
+/*
+ * One decode step with the new token appended in the same launch: exactly the effect of
+ * nvkv_quantize_append_kv of k_new/v_new at position n-1, followed by
+ * nvkv_decode_attention_nvfp4 over [0, n), where n = min(seq_lens[b], max_seq_len,
+ * max_pages_per_seq * page_size) is the length INCLUDING the new token.  The quantisation
+ * is the one of nvkv_quantize_append_kv ([cache post] opening paragraph and cache-config
+ * table; [OSFP4] sections 1 and 3), the attention the one of nvkv_decode_attention_nvfp4.
+ *   k_new, v_new: bf16 [B][Hkv][128], device: the new token's post-RoPE key and value.
+ *   The slot is taken from the page table (page page_table[b][(n-1) / page_size], offset
+ *   (n-1) % page_size); an out-of-range page index writes nothing and leaves the new token
+ *   out of the attention, as the two separate calls would.  Sequences with n = 0 append
+ *   nothing and get a zero output row.
+ *   Other arguments, the workspace rules and the output are those of
+ *   nvkv_decode_attention_nvfp4 (same nvkv_decode_workspace_bytes).  The workgroup that
+ *   owns position n-1 encodes the row while the others stream the cache, which saves the
+ *   separate append launch of a decode step.
+ */
+NVKV_API nvkv_status nvkv_decode_append_attention_nvfp4(const nvkv_layer *layer,
+                                        const uint16_t *q, const uint16_t *k_new,
+                                        const uint16_t *v_new, int32_t B, int32_t Hq,
                                         const int32_t *page_table, int32_t max_pages_per_seq,
                                         const int32_t *seq_lens, int32_t max_seq_len,
                                         float sm_scale, float *out,

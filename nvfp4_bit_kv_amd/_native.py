@@ -21,7 +21,7 @@ PART_CODES, PART_SCALES = 0, 1
 HEAD_DIM = 128
 
 EXPORTED = ["nvkv_calibrate_key_smoothing", "nvkv_quantize_append_kv", "nvkv_decode_workspace_bytes",
-            "nvkv_decode_attention_nvfp4", "nvkv_cache_array_bytes", "nvkv_cache_bytes_per_token",
+            "nvkv_decode_attention_nvfp4", "nvkv_decode_append_attention_nvfp4", "nvkv_cache_array_bytes", "nvkv_cache_bytes_per_token",
             "nvkv_status_string", "nvkv_last_error"]
 
 
@@ -68,6 +68,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.nvkv_decode_attention_nvfp4.argtypes = [ctypes.POINTER(Layer), vp, i32, i32, vp, i32, vp, i32, f32, vp,
                                                 vp, sz, i32, vp]
     lib.nvkv_decode_attention_nvfp4.restype = ctypes.c_int
+    lib.nvkv_decode_append_attention_nvfp4.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, i32, i32, vp, i32, vp, i32,
+                                                       f32, vp, vp, sz, i32, vp]
+    lib.nvkv_decode_append_attention_nvfp4.restype = ctypes.c_int
     lib.nvkv_cache_array_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.nvkv_cache_array_bytes.restype = sz
     lib.nvkv_cache_bytes_per_token.argtypes = [i32, i32, i32, i32]
@@ -125,6 +128,16 @@ def decode_attention_nvfp4(layer: Layer, q, B: int, Hq: int, page_table, max_pag
                                               max_pages_per_seq, _ptr(seq_lens), max_seq_len, sm_scale, _ptr(out),
                                               _ptr(workspace), workspace_bytes, split_tokens, _stream(stream)),
            "nvkv_decode_attention_nvfp4")
+
+
+def decode_append_attention_nvfp4(layer: Layer, q, k_new, v_new, B: int, Hq: int, page_table,
+                                  max_pages_per_seq: int, seq_lens, max_seq_len: int, sm_scale: float, out,
+                                  workspace, workspace_bytes: int, split_tokens: int = 0, stream=None) -> None:
+    _check(load().nvkv_decode_append_attention_nvfp4(ctypes.byref(layer), _ptr(q), _ptr(k_new), _ptr(v_new), B, Hq,
+                                                     _ptr(page_table), max_pages_per_seq, _ptr(seq_lens),
+                                                     max_seq_len, sm_scale, _ptr(out), _ptr(workspace),
+                                                     workspace_bytes, split_tokens, _stream(stream)),
+           "nvkv_decode_append_attention_nvfp4")
 
 
 def cache_array_bytes(fmt: int, part: int, num_pages: int, Hkv: int, page_size: int) -> int:

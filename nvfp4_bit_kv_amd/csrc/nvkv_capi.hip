@@ -111,35 +111,57 @@ nvkv_status nvkv_quantize_append_kv(const nvkv_layer* layer, const uint16_t* k_n
 
 size_t nvkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len, int32_t split_tokens) {
   if (B < 1 || Hkv < 1 || Hq != 4 * Hkv || max_seq_len < 0 || split_tokens < 0 || split_tokens % 32 != 0) return 0;
-  const nvkv::DecodePlan plan = nvkv::plan_decode(B, Hkv, max_seq_len, split_tokens);
+  const nvkv::DecodePlan plan = nvkv::plan_decode(B, Hkv, max_seq_len, split_tokens, false);
   if (plan.n_splits <= 1) return 0;
   return nvkv::decode_workspace_bytes(B, Hkv, plan);
 }
 
-nvkv_status nvkv_decode_attention_nvfp4(const nvkv_layer* layer, const uint16_t* q, int32_t B, int32_t Hq,
-                                        const int32_t* page_table, int32_t max_pages_per_seq,
-                                        const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, float* out,
-                                        void* workspace, size_t workspace_bytes, int32_t split_tokens,
-                                        void* stream) {
+namespace {
+nvkv_status decode_common(const nvkv_layer* layer, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                          bool append, int32_t B, int32_t Hq, const int32_t* page_table, int32_t max_pages_per_seq,
+                          const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, float* out, void* workspace,
+                          size_t workspace_bytes, int32_t split_tokens, void* stream) {
   const nvkv_status st = check_layer(layer);
   if (st != NVKV_OK) return st;
   if (!q || !page_table || !seq_lens || !out) return fail(NVKV_ERR_NULL, "input/output pointer is NULL");
+  if (append && (!k_new || !v_new)) return fail(NVKV_ERR_NULL, "k_new / v_new is NULL");
   if (B < 1 || B > kMaxGridYZ) return fail(NVKV_ERR_SHAPE, "B must be in [1, 65535]");
   if (Hq < 1 || Hq % layer->num_kv_heads != 0) return fail(NVKV_ERR_SHAPE, "Hq must be a multiple of Hkv");
   if (Hq != 4 * layer->num_kv_heads) return fail(NVKV_ERR_UNSUPPORTED, "only 4 query heads per KV head");
   if (max_pages_per_seq < 1 || max_seq_len < 0) return fail(NVKV_ERR_SHAPE, "max_pages_per_seq >= 1, max_seq_len >= 0");
   if (split_tokens < 0 || split_tokens % 32 != 0) return fail(NVKV_ERR_SHAPE, "split_tokens must be a multiple of 32");
   if (!std::isfinite(sm_scale)) return fail(NVKV_ERR_SHAPE, "sm_scale must be finite");
-  const nvkv::DecodePlan plan = nvkv::plan_decode(B, layer->num_kv_heads, max_seq_len, split_tokens);
+  const nvkv::DecodePlan plan = nvkv::plan_decode(B, layer->num_kv_heads, max_seq_len, split_tokens, append);
   if (plan.n_splits > 1) {
     const size_t need = nvkv::decode_workspace_bytes(B, layer->num_kv_heads, plan);
     if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
       return fail(NVKV_ERR_WORKSPACE, "workspace missing, too small or not 256-byte aligned");
   }
   (void)hipGetLastError();
-  return hip_status(nvkv::launch_decode(*layer, q, B, Hq, page_table, max_pages_per_seq, seq_lens, max_seq_len,
-                                        sm_scale, out, workspace, plan, static_cast<hipStream_t>(stream)),
-                    "decode launch");
+  return hip_status(nvkv::launch_decode(*layer, q, append ? k_new : nullptr, append ? v_new : nullptr, B, Hq,
+                                        page_table, max_pages_per_seq, seq_lens, max_seq_len, sm_scale, out,
+                                        workspace, plan, static_cast<hipStream_t>(stream)),
+                    append ? "decode-append launch" : "decode launch");
+}
+}  // namespace
+
+nvkv_status nvkv_decode_attention_nvfp4(const nvkv_layer* layer, const uint16_t* q, int32_t B, int32_t Hq,
+                                        const int32_t* page_table, int32_t max_pages_per_seq,
+                                        const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, float* out,
+                                        void* workspace, size_t workspace_bytes, int32_t split_tokens,
+                                        void* stream) {
+  return decode_common(layer, q, nullptr, nullptr, false, B, Hq, page_table, max_pages_per_seq, seq_lens,
+                       max_seq_len, sm_scale, out, workspace, workspace_bytes, split_tokens, stream);
+}
+
+nvkv_status nvkv_decode_append_attention_nvfp4(const nvkv_layer* layer, const uint16_t* q, const uint16_t* k_new,
+                                               const uint16_t* v_new, int32_t B, int32_t Hq,
+                                               const int32_t* page_table, int32_t max_pages_per_seq,
+                                               const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                                               float* out, void* workspace, size_t workspace_bytes,
+                                               int32_t split_tokens, void* stream) {
+  return decode_common(layer, q, k_new, v_new, true, B, Hq, page_table, max_pages_per_seq, seq_lens, max_seq_len,
+                       sm_scale, out, workspace, workspace_bytes, split_tokens, stream);
 }
 
 }  // extern "C"

@@ -36,6 +36,7 @@
 // issued at kernel start, before the sequence length is known; later iterations are
 // software-pipelined two deep.
 #include "nvkv_device.hpp"
+#include "nvkv_encode.hpp"
 #include "nvkv_internal.hpp"
 
 namespace nvkv {
@@ -71,6 +72,15 @@ struct DecodeArgs {
   int32_t split_tokens, n_splits;
   uint32_t k_flags;
   float sm_scale;
+  // fused append (k_decode<.., .., true>): the new token of sequence b, at position
+  // seq_len - 1, is quantised into the cache and attended from registers
+  const uint16_t* k_new;      // bf16 [B][Hkv][128]
+  const uint16_t* v_new;      // bf16 [B][Hkv][128]
+  const float* inv_smooth;    // r [Hkv][128] (key smoothing)
+  uint8_t* k_codes_w;         // writable views of the cache arrays
+  uint8_t* k_scales_w;
+  uint8_t* v_codes_w;
+  uint8_t* v_scales_w;
 };
 
 __device__ __forceinline__ float dpp_xor1(float x) {
@@ -418,10 +428,187 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs& a, int64_t unit, 
       make_float2(o0 * f, o1 * f);
 }
 
+// ---------------------------------------------------------------------------------------
+// Fused append of the new token
+// ---------------------------------------------------------------------------------------
+// The new token as token 0 of a (page, head) block in the cache layouts (only the bytes of
+// token 0), in LDS.
+struct NewTokenStage {
+  uint8_t kc[kHeadDim * 2];        // key row (64 B NVFP4 or 256 B bf16)
+  uint8_t ks[32];                  // key scales: block b at byte 4b (token 0 of its quad)
+  uint8_t vc[256];                 // value words: word w at byte 16w (quad-interleaved)
+  uint8_t vs[32];                  // value scales: block b at byte 4b
+};
+
+// Registers of the encoding wavefront: the whole wavefront encodes the new token, lane L
+// holding elements 4(L & 31) .. 4(L & 31) + 3 of the key row (L < 32) or the value row
+// (L >= 32), i.e. quarter L & 3 of block (L >> 2) & 7.  Loaded at kernel start.
+struct NewTokenRegs {
+  uint2 raw;            // 4 bf16 elements
+  float4 r;             // key smoothing factors of those elements (key lanes, smoothing on)
+  float g;              // tensor scale of the lane's row
+};
+
+template <bool KBF16>
+__device__ __forceinline__ void new_token_load(const DecodeArgs& a, int b, int h, int lane, NewTokenRegs& R) {
+  const bool is_v = lane >= 32;
+  const int64_t row = (static_cast<int64_t>(b) * a.hkv + h) * kHeadDim;
+  R.raw = reinterpret_cast<const uint2*>((is_v ? a.v_new : a.k_new) + row)[lane & 31];
+  R.g = a.gscale[is_v ? 1 : 0];
+  R.r = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+  if (!KBF16 && !is_v && (a.k_flags & NVKV_K_SMOOTH))
+    R.r = reinterpret_cast<const float4*>(a.inv_smooth + h * kHeadDim)[lane & 31];
+}
+
+// One Hadamard stage across lanes: element i of this lane pairs with element i of lane
+// (lane ^ m), the lower lane keeping the sum, the upper the difference (lower - upper).
+__device__ __forceinline__ void had_cross(float (&y)[4], int lane, int m) {
+  const bool upper = (lane & m) != 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p = __shfl_xor(y[i], m, 64);
+    y[i] = upper ? (p - y[i]) : (y[i] + p);
+  }
+}
+
+// Encode the new token (the transform and encoder of quantize_append_kv, four elements per
+// lane): the LDS stage receives it as token 0 of a 16-token block in the cache layouts, and
+// the cache slot too when its page is in range (page pg, offset off).
+template <bool KBF16>
+__device__ __forceinline__ void new_token_encode(const DecodeArgs& a, int h, int lane, const NewTokenRegs& R,
+                                                 int32_t pg, int off, bool ok, NewTokenStage& st) {
+  const bool is_v = lane >= 32;
+  const int blk = (lane >> 2) & 7, qtr = lane & 3;
+  const int64_t ph = static_cast<int64_t>(ok ? pg : 0) * a.hkv + h;
+  const int64_t row_index = ph * a.page_size + off;
+  if (KBF16 && !is_v) {                                   // bf16 keys: plain copy of the row
+    *reinterpret_cast<uint2*>(st.kc + 8 * (lane & 31)) = R.raw;
+    if (ok) *reinterpret_cast<uint2*>(a.k_codes_w + row_index * (kHeadDim * 2) + 8 * (lane & 31)) = R.raw;
+    return;
+  }
+  float y[4] = {bf16_to_f32(R.raw.x & 0xFFFFu), bf16_to_f32(R.raw.x >> 16), bf16_to_f32(R.raw.y & 0xFFFFu),
+                bf16_to_f32(R.raw.y >> 16)};
+  if (!is_v && (a.k_flags & NVKV_K_SMOOTH)) {             // y_j = fl32(x_j * r_j)
+    y[0] = y[0] * R.r.x;
+    y[1] = y[1] * R.r.y;
+    y[2] = y[2] * R.r.z;
+    y[3] = y[3] * R.r.w;
+  }
+  if (!is_v && (a.k_flags & NVKV_K_HADAMARD)) {           // stages h = 1, 2, ..., 64 in order
+    float t0 = y[0] + y[1], t1 = y[0] - y[1], t2 = y[2] + y[3], t3 = y[2] - y[3];
+    y[0] = t0 + t2;
+    y[2] = t0 - t2;
+    y[1] = t1 + t3;
+    y[3] = t1 - t3;
+    had_cross(y, lane, 1);                                // h = 4
+    had_cross(y, lane, 2);                                // h = 8
+    had_cross(y, lane, 4);                                // h = 16
+    had_cross(y, lane, 8);                                // h = 32
+    had_cross(y, lane, 16);                               // h = 64
+  }
+  // block absmax over the block's four lanes, scale code, E2M1 nibbles
+  float A = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
+  A = fmaxf(A, __shfl_xor(A, 1, 64));
+  A = fmaxf(A, __shfl_xor(A, 2, 64));
+  const uint32_t S = e4m3_scale_code(A, R.g);
+  const float sigma = e4m3_value(S);
+  uint32_t bits = 0u;
+  if (sigma > 0.0f) {
+    const E2m1Thresholds t(sigma);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bits |= e2m1_nibble(y[i], t, R.g) << (4 * i);
+  }
+  // word w = 2 blk + (qtr >> 1) holds elements 8w..8w+7: even quarters take the odd
+  // neighbour's 16 bits as their high half
+  const uint32_t hi16 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(bits), 1, 64));
+  const uint32_t word = bits | (hi16 << 16);
+  const int w = 2 * blk + (qtr >> 1);
+  const int64_t sc = ph * a.page_size * 8 + ((off >> 2) * 8 + blk) * 4 + (off & 3);
+  if ((qtr & 1) == 0) {
+    if (!is_v) {
+      *reinterpret_cast<uint32_t*>(st.kc + 4 * w) = word;
+      if (ok) *reinterpret_cast<uint32_t*>(a.k_codes_w + row_index * 64 + 4 * w) = word;
+    } else {
+      *reinterpret_cast<uint32_t*>(st.vc + 16 * w) = word;
+      if (ok) *reinterpret_cast<uint32_t*>(a.v_codes_w + (row_index - (off & 3)) * 64 + 16 * w + 4 * (off & 3)) = word;
+    }
+  }
+  if (qtr == 0) {
+    (is_v ? st.vs : st.ks)[4 * blk] = static_cast<uint8_t>(S);
+    if (ok) (is_v ? a.v_scales_w : a.k_scales_w)[sc] = static_cast<uint8_t>(S);
+  }
+}
+
+// Add the staged new token to a wavefront's softmax state (a single-token update instead of
+// an MFMA iteration).  Scores: lane L takes dims 2L, 2L+1 of the four query heads (terms hi +
+// lo from the query LDS image, exact in fp32) against the staged key (code * sigma, exact in
+// fp16) and the sums are reduced over the wavefront.  Lane (c, g) then updates head g: the
+// lazy max, the denominator (one lane per head) and row (g, term 0) of the accumulators with
+// p * value(dims 8c..8c+7) in fp32.
+template <bool KBF16>
+__device__ __forceinline__ void new_token_update(const NewTokenStage& st, const uint16_t (*q_lds)[4][kHeadDim],
+                                                 const float* q_descale, int lane, const Lane& ln,
+                                                 SoftmaxState& sm) {
+  float kx, ky;
+  if constexpr (!KBF16) {
+    const uint32_t kw = *reinterpret_cast<const uint32_t*>(st.kc + 4 * (lane >> 2));
+    const uint32_t byte_sel = static_cast<uint32_t>(lane & 3);
+    const uint32_t kb = (kw >> (8 * byte_sel)) & 0xFFu;
+    const half2v kv = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(kb, 256.0f, 0)) *
+                      scale_pair_same(st.ks[4 * (lane >> 3)]);
+    kx = static_cast<float>(kv[0]);
+    ky = static_cast<float>(kv[1]);
+  } else {
+    const uint32_t kb = *reinterpret_cast<const uint32_t*>(st.kc + 4 * lane);
+    kx = bf16_to_f32(kb & 0xFFFFu);
+    ky = bf16_to_f32(kb >> 16);
+  }
+  float sc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t hi = reinterpret_cast<const uint32_t*>(q_lds[i][0])[lane];
+    const uint32_t lo = reinterpret_cast<const uint32_t*>(q_lds[i][1])[lane];
+    float q0, q1;
+    if constexpr (!KBF16) {
+      const half2v h2 = as_half2(hi), l2 = as_half2(lo);
+      q0 = static_cast<float>(h2[0]) + static_cast<float>(l2[0]);
+      q1 = static_cast<float>(h2[1]) + static_cast<float>(l2[1]);
+    } else {
+      const uint32_t t2 = reinterpret_cast<const uint32_t*>(q_lds[i][2])[lane];
+      q0 = (bf16_to_f32(hi & 0xFFFFu) + bf16_to_f32(lo & 0xFFFFu)) + bf16_to_f32(t2 & 0xFFFFu);
+      q1 = (bf16_to_f32(hi >> 16) + bf16_to_f32(lo >> 16)) + bf16_to_f32(t2 >> 16);
+    }
+    float x = q0 * kx + q1 * ky;
+    x = row16_sum(x);
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    sc[i] = (__uint_as_float(t[0]) + __uint_as_float(t[1])) * q_descale[i];
+  }
+  const float s = ln.g == 0 ? sc[0] : (ln.g == 1 ? sc[1] : (ln.g == 2 ? sc[2] : sc[3]));
+  if (s > sm.m_ref + kLazyMax) {                   // per row of lanes, as in the iterations
+    const float alpha = exp2f(sm.m_ref - s);
+    sm.m_ref = s;
+    sm.l_acc *= alpha;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) sm.acc[v] *= alpha;
+  }
+  const float p = __builtin_amdgcn_exp2f(s - sm.m_ref);
+  if (ln.c == 0) sm.l_acc += p;
+  const uint32_t vw = *reinterpret_cast<const uint32_t*>(st.vc + 16 * ln.c);
+  const half8 vv = dequant_dword(vw, scale_pair_same(st.vs[4 * (ln.c >> 1)]));
+#pragma unroll
+  for (int v = 0; v < 8; ++v) sm.acc[v][0] = __builtin_fmaf(p, static_cast<float>(vv[v]), sm.acc[v][0]);
+}
+
 // PIPE2: two register buffers and up to 8 wavefronts per workgroup (long splits, several
 // iterations per wavefront); otherwise one buffer and few enough registers for 16
 // wavefronts per workgroup (short splits, about one iteration per wavefront).
-template <bool KBF16, bool PIPE2>
+// APPEND: one extra wavefront per workgroup reads no cache.  In the workgroup whose split
+// holds position seq_len - 1 it quantises the new token into its cache slot and an LDS stage
+// once the query prologue is done and adds the token to its own softmax state; the cache
+// wavefronts read the split without that position.
+template <bool KBF16, bool PIPE2, bool APPEND>
 __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -442,7 +629,10 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   __shared__ float red_m[kMaxWaves][4], red_l[kMaxWaves][4];
   __shared__ __attribute__((aligned(16))) float red_o[kMaxWaves][4][kHeadDim];
   const int nw = static_cast<int>(blockDim.x) >> 6;
+  const int nwc = APPEND ? nw - 1 : nw;                     // wavefronts that read the cache
+  const bool app_wave = APPEND && wave == nw - 1;
   __shared__ int mrg_last;
+  __shared__ __attribute__((aligned(16))) NewTokenStage nt_stage;
 
   const int64_t unit = static_cast<int64_t>(b) * a.hkv + h;
   const const_i32_ptr ptab = __builtin_bit_cast(const_i32_ptr, a.page_table) + static_cast<int64_t>(b) * a.max_pages_per_seq;
@@ -454,18 +644,35 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   float2 sv = make_float2(1.0f, 1.0f);
   if (!KBF16 && (a.k_flags & NVKV_K_SMOOTH)) sv = reinterpret_cast<const float2*>(a.smooth + h * kHeadDim)[lane];
   const float gk = KBF16 ? 1.0f : a.gscale[0];
+  NewTokenRegs nreg;
+  if (app_wave) new_token_load<KBF16>(a, b, h, lane, nreg);
   int seq_len = a.seq_lens[b];
   seq_len = seq_len < 0 ? 0 : (seq_len > a.seq_cap ? a.seq_cap : seq_len);
   const int t_begin = split * a.split_tokens;
   const int t_end = min(t_begin + a.split_tokens, seq_len);
   const bool empty = t_begin >= t_end;                      // uniform across the workgroup
+  // APPEND: the new token is position t_new = seq_len - 1
+  const int t_new = seq_len - 1;
+  const bool owns_new = APPEND && !empty && t_new >= t_begin && t_new < t_begin + a.split_tokens;
+  const int t_read = APPEND ? min(t_end, t_new) : t_end;  // the cache wavefronts skip t_new
+  int32_t new_pg = 0;
+  int new_off = 0;
+  if (owns_new && app_wave) {
+    if (a.page_shift >= 0) {
+      new_pg = ptab[t_new >> a.page_shift];
+      new_off = t_new & (a.page_size - 1);
+    } else {
+      new_pg = ptab[t_new / a.page_size];
+      new_off = t_new % a.page_size;
+    }
+  }
 
   // First two iterations of this wavefront: addresses and loads are issued before the
   // sequence length arrives, bounded by the kernel arguments only (t_lim >= t_end), so the
   // cache traffic overlaps the query prologue; tokens in [t_end, t_lim) are masked later.
   const int t_lim = min(t_begin + a.split_tokens, a.seq_cap);
-  const int step = kIterTok * nw;
-  int t0 = t_begin + kIterTok * wave;
+  const int step = kIterTok * nwc;
+  int t0 = app_wave ? INT_MAX / 2 : t_begin + kIterTok * wave;   // the append wavefront reads no cache
   IterLoads<KBF16> buf0, buf1;
   HalfBase hb0[2], hb1[2];
   if (t0 < t_lim) {
@@ -561,34 +768,39 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
     // the page entries of the iteration after them are already loaded, so neither the
     // vector loads nor the page lookups sit on the critical path.
     if constexpr (!PIPE2) {
-      while (t0 < t_end) {
-        valid_tokens(hb0, t0, t_end, c, vm);
+      while (t0 < t_read) {
+        valid_tokens(hb0, t0, t_read, c, vm);
         compute_iter<KBF16>(buf0, vm, qa, descale, ln, st, p_w);
         t0 += step;
-        if (t0 >= t_end) break;
+        if (t0 >= t_read) break;
         half_bases<KBF16>(a, pnext, h, hb0);
         issue_loads<KBF16>(hb0, ln, buf0);
-        pnext = load_pages(a, ptab, t0 + step, t_end);
+        pnext = load_pages(a, ptab, t0 + step, t_read);
       }
     }
-    while (PIPE2 && t0 < t_end) {
-      valid_tokens(hb0, t0, t_end, c, vm);
-        compute_iter<KBF16>(buf0, vm, qa, descale, ln, st, p_w);
+    while (PIPE2 && t0 < t_read) {
+      valid_tokens(hb0, t0, t_read, c, vm);
+      compute_iter<KBF16>(buf0, vm, qa, descale, ln, st, p_w);
       t0 += step;
-      if (t0 >= t_end) break;
-      if (t0 + step < t_end) {
+      if (t0 >= t_read) break;
+      if (t0 + step < t_read) {
         half_bases<KBF16>(a, pnext, h, hb0);
         issue_loads<KBF16>(hb0, ln, buf0);
-        pnext = load_pages(a, ptab, t0 + 2 * step, t_end);
+        pnext = load_pages(a, ptab, t0 + 2 * step, t_read);
       }
-      valid_tokens(hb1, t0, t_end, c, vm);
+      valid_tokens(hb1, t0, t_read, c, vm);
       compute_iter<KBF16>(buf1, vm, qa, descale, ln, st, p_w);
       t0 += step;
-      if (t0 + step < t_end) {
+      if (t0 + step < t_read) {
         half_bases<KBF16>(a, pnext, h, hb1);
         issue_loads<KBF16>(hb1, ln, buf1);
-        pnext = load_pages(a, ptab, t0 + 2 * step, t_end);
+        pnext = load_pages(a, ptab, t0 + 2 * step, t_read);
       }
+    }
+    if (owns_new && app_wave) {
+      const bool ok = static_cast<uint32_t>(new_pg) < static_cast<uint32_t>(a.num_pages);
+      new_token_encode<KBF16>(a, h, lane, nreg, new_pg, new_off, ok, nt_stage);
+      if (ok) new_token_update<KBF16>(nt_stage, q_lds, q_descale, lane, ln, st);
     }
   }
 
@@ -657,8 +869,9 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
 // ---------------------------------------------------------------------------------------
 // Split plan and launcher
 // ---------------------------------------------------------------------------------------
-DecodePlan plan_decode(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t split_tokens) {
+DecodePlan plan_decode(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t split_tokens, bool append) {
   DecodePlan p{};
+  p.append = append;
   const int32_t len = max_seq_len > 0 ? max_seq_len : 1;
   const int64_t iters = (len + kIterTok - 1) / kIterTok;          // 32-token iterations
   int64_t per;                                                    // iterations per split
@@ -680,12 +893,14 @@ DecodePlan plan_decode(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t spli
   if (per < 1) per = 1;
   p.split_tokens = static_cast<int32_t>(per * kIterTok);
   p.n_splits = static_cast<int32_t>((len + p.split_tokens - 1) / p.split_tokens);
-  if (per <= kMaxWaves) {
+  // the fused append adds one wavefront (the append wavefront) to every workgroup
+  const int64_t max_cache_waves = append ? kMaxWaves - 1 : kMaxWaves;
+  if (per <= max_cache_waves) {
     p.pipe2 = false;
-    p.waves = static_cast<int32_t>(per < 4 ? 4 : per);
+    p.waves = static_cast<int32_t>((per < 4 ? 4 : per) + (append ? 1 : 0));
   } else {
     p.pipe2 = true;
-    p.waves = 8;
+    p.waves = 8;                 // with the append wavefront: 7 cache wavefronts + 1
   }
   return p;
 }
@@ -703,10 +918,18 @@ size_t decode_workspace_bytes(int32_t B, int32_t Hkv, const DecodePlan& plan) {
          align256(slots * kHeadDim * sizeof(float));
 }
 
-hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, int32_t B, int32_t Hq, const int32_t* page_table,
-                         int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
-                         float* out, void* workspace, const DecodePlan& plan, hipStream_t stream) {
+hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                         int32_t B, int32_t Hq, const int32_t* page_table, int32_t max_pages_per_seq,
+                         const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, float* out, void* workspace,
+                         const DecodePlan& plan, hipStream_t stream) {
   DecodeArgs a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.inv_smooth = L.k_inv_smooth;
+  a.k_codes_w = static_cast<uint8_t*>(L.k_data);
+  a.k_scales_w = L.k_scales;
+  a.v_codes_w = static_cast<uint8_t*>(L.v_data);
+  a.v_scales_w = L.v_scales;
   a.k_codes = static_cast<const uint8_t*>(L.k_data);
   a.k_scales = L.k_scales;
   a.v_codes = static_cast<const uint8_t*>(L.v_data);
@@ -737,12 +960,23 @@ hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, int32_t B, int3
   a.sm_scale = sm_scale;
   const dim3 grid(plan.n_splits, L.num_kv_heads, B);
   const dim3 block(64 * plan.waves);
-  if (L.k_fmt == NVKV_FMT_BF16) {
-    if (plan.pipe2) hipLaunchKernelGGL((k_decode<true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((k_decode<true, false>), grid, block, 0, stream, a);
+  const bool bf = L.k_fmt == NVKV_FMT_BF16;
+  if (plan.append) {
+    if (bf) {
+      if (plan.pipe2) hipLaunchKernelGGL((k_decode<true, true, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((k_decode<true, false, true>), grid, block, 0, stream, a);
+    } else {
+      if (plan.pipe2) hipLaunchKernelGGL((k_decode<false, true, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((k_decode<false, false, true>), grid, block, 0, stream, a);
+    }
   } else {
-    if (plan.pipe2) hipLaunchKernelGGL((k_decode<false, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((k_decode<false, false>), grid, block, 0, stream, a);
+    if (bf) {
+      if (plan.pipe2) hipLaunchKernelGGL((k_decode<true, true, false>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((k_decode<true, false, false>), grid, block, 0, stream, a);
+    } else {
+      if (plan.pipe2) hipLaunchKernelGGL((k_decode<false, true, false>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((k_decode<false, false, false>), grid, block, 0, stream, a);
+    }
   }
   return hipGetLastError();
 }

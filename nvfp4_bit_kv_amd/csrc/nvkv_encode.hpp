@@ -1,7 +1,7 @@
-// NVFP4 encoder and key transform, one lane per 16-element block (8 lanes per 128-wide row,
-// 8 rows per wavefront).  Included only by translation units compiled with
-// -ffp-contract=off: the key transform is part of the bit-exact encoding and every fp32
-// multiply and add below must round on its own.
+// NVFP4 encoder and key transform, one lane per 16-element block (8 lanes per 128-wide row).
+// The key transform is part of the bit-exact encoding: every fp32 multiply and add below
+// must round on its own, so the whole header is compiled with floating-point contraction
+// off (scoped with push/pop, so an including unit keeps its own setting).
 //
 // Sources: [cache post] = rstation.ai post "NVFP4 attention cache on W4A4 Qwen3-8B: static
 // key smoothing is near-lossless, key rotations hurt" (cache-config table: per-channel
@@ -9,9 +9,11 @@
 // arXiv 2610.08231v1 (section 1: 16-entry groups, E4M3 scales, FP4 max 6, absmax-to-6;
 // section 3: absmax-to-6 per 16-entry group with a calibration-based global scale).
 #pragma once
-#pragma clang fp contract(off)
 
 #include "nvkv_device.hpp"
+
+#pragma float_control(push)
+#pragma clang fp contract(off)
 
 namespace nvkv {
 
@@ -57,23 +59,34 @@ __device__ __forceinline__ void hadamard_row(float (&y)[kBlock], int blk) {
   }
 }
 
+// Is the midpoint between E4M3 codes k and k+1 (k <= 125) passed by the exact quotient
+// A/(6g)?  6 * midpoint = 3 * (v_k + v_{k+1}) is exact in fp32, and the sign of the fused
+// A - t6*g is that of the exact difference; at an exact midpoint the even code wins.
+__device__ __forceinline__ bool e4m3_mid_passed(uint32_t k, float A, float g) {
+  const float t6 = 3.0f * (e4m3_value(k) + e4m3_value(k + 1));
+  const float d = __builtin_fmaf(-t6, g, A);
+  return (d > 0.0f) || (d == 0.0f && ((k + 1) & 1u) == 0u);
+}
+
 // E4M3 block-scale code: round-to-nearest-even of the exact A/(6g), saturating at 448
-// (code 0x7E).  Counts the midpoints between consecutive codes that the quotient passes
-// (binary search over the 126 midpoints); at an exact midpoint the even code wins.
+// (code 0x7E); g > 0.  A candidate is the code nearest to the rounded fp32 quotient (its
+// error is a few ulp, far below the 1/16 relative spacing of the codes, so the exact answer
+// is the candidate or a neighbour); the exact midpoint tests on both sides settle it.
 __device__ __forceinline__ uint32_t e4m3_scale_code(float A, float g) {
-  uint32_t c = 0;
-#pragma unroll
-  for (uint32_t step = 64; step >= 1; step >>= 1) {
-    const uint32_t k = c + step - 1;
-    if (k <= 125u) {
-      // 6 * midpoint(k, k+1) = 3 * (v_k + v_{k+1}): exact in fp32
-      const float t6 = 3.0f * (e4m3_value(k) + e4m3_value(k + 1));
-      const float d = __builtin_fmaf(-t6, g, A);
-      const bool pass = (d > 0.0f) || (d == 0.0f && ((k + 1) & 1u) == 0u);
-      if (pass) c += step;
-    }
+  if (A == 0.0f) return 0u;                                          // all-zero block
+  const float x = A * __builtin_amdgcn_rcpf(6.0f * g);
+  int c;
+  if (x < 0.015625f) {
+    c = static_cast<int>(__builtin_rintf(x * 512.0f));               // subnormal codes: x * 2^9
+  } else {
+    // normal codes: (exponent field - 120) * 8 + 3 mantissa bits, rounded at mantissa bit 20
+    const uint32_t r = (__float_as_uint(x) + 0x80000u) >> 20;
+    c = r > 1086u ? 126 : static_cast<int>(r) - 960;                // also catches inf
   }
-  return c;
+  c = c > 126 ? 126 : c;
+  const bool up = c < 126 && e4m3_mid_passed(static_cast<uint32_t>(c), A, g);
+  const bool down = !up && c > 0 && !e4m3_mid_passed(static_cast<uint32_t>(c > 0 ? c - 1 : 0), A, g);
+  return static_cast<uint32_t>(c + (up ? 1 : 0) - (down ? 1 : 0));
 }
 
 // Per-block E2M1 thresholds P_k = t_k * sigma (exact), t = midpoints of the magnitude grid
@@ -135,3 +148,5 @@ __device__ __forceinline__ void load_block_bf16(const uint16_t* __restrict__ src
 }
 
 }  // namespace nvkv
+
+#pragma float_control(pop)

@@ -20,12 +20,15 @@ struct DecodePlan {
   int32_t n_splits;       // workgroups per (sequence, KV head)
   int32_t waves;          // wavefronts per workgroup (4..16)
   bool pipe2;             // two-deep software pipeline (several iterations per wavefront)
+  bool append;            // fused append of the new token (one extra wavefront)
 };
-DecodePlan plan_decode(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t split_tokens);
+DecodePlan plan_decode(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t split_tokens, bool append);
 size_t decode_workspace_bytes(int32_t B, int32_t Hkv, const DecodePlan& plan);
 
-hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, int32_t B, int32_t Hq, const int32_t* page_table,
-                         int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
-                         float* out, void* workspace, const DecodePlan& plan, hipStream_t stream);
+// k_new / v_new non-null: fused append of the new token of each sequence (plan.append).
+hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                         int32_t B, int32_t Hq, const int32_t* page_table, int32_t max_pages_per_seq,
+                         const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, float* out, void* workspace,
+                         const DecodePlan& plan, hipStream_t stream);
 
 }  // namespace nvkv

@@ -28,7 +28,7 @@ def clib():
 
 def test_every_declared_symbol_is_exported(clib):
     decl = _declared_symbols()
-    assert len(decl) == 8, decl
+    assert len(decl) == 9, decl
     assert sorted(decl) == sorted(nk.EXPORTED)
     for name in decl:
         assert hasattr(clib, name), name
@@ -113,6 +113,24 @@ def test_decode_argument_errors(clib):
     assert nk.decode_workspace_bytes(4, 32, 8, 64, 64) == 0     # single split: none needed
     assert nk.decode_workspace_bytes(4, 30, 8, 64, 0) == 0      # invalid
     assert f(None, 0x10, 4, 32, 0x10, 4, 0x10, 64, 0.1, 0x10, None, 0, 0, None) == 1
+
+
+def test_decode_append_argument_errors(clib):
+    """The fused append+decode entry point validates like decode, plus k_new / v_new."""
+    L = _layer()
+    f = clib.nvkv_decode_append_attention_nvfp4
+    ok = dict(q=0x10, kn=0x10, vn=0x10, B=4, Hq=32, pt=0x10, mp=4, sl=0x10, msl=64, sm=0.1, out=0x10, ws=0x1000,
+              wsb=1 << 30, sp=0)
+    def call(lay=L, **kw):
+        a = dict(ok, **kw)
+        return f(ctypes.byref(lay) if lay is not None else None, a["q"], a["kn"], a["vn"], a["B"], a["Hq"], a["pt"],
+                 a["mp"], a["sl"], a["msl"], a["sm"], a["out"], a["ws"], a["wsb"], a["sp"], None)
+    assert call(lay=None) == 1
+    assert call(kn=None) == 1 and call(vn=None) == 1 and call(q=None) == 1 and call(out=None) == 1
+    assert call(B=0) == 2 and call(Hq=16) == 3 and call(sp=48) == 2 and call(sm=float("nan")) == 2
+    need = nk.decode_workspace_bytes(4, 32, 8, 4096, 32)
+    assert call(msl=4096, sp=32, wsb=need - 1) == 4
+    assert call(lay=_layer(k_fmt=7)) == 3
 
 
 def test_calibrate_argument_errors(clib):

@@ -242,6 +242,48 @@ def test_special_rows_bit_exact(lib):
     assert 0 in ks[:, 0, 0] and 0x7E in ks[:, 0, 0] and np.any((ks > 0) & (ks < 8))
 
 
+def test_scale_code_at_every_e4m3_midpoint(lib):
+    """Block absmax exactly at 6*g times each of the 126 E4M3 midpoints (ties: the even code
+    wins), and one bf16 step above and below each, for two tensor scales; codes and scales
+    bit-exact against the oracle."""
+    grid = O.E4M3_GRID
+    mids6 = 3.0 * (grid[:-1] + grid[1:])                      # 6 * midpoint, exact
+    hkv = 1
+    for g_val in (np.float32(2.0 ** -9), np.float32(0.0390625)):   # power of two, and 5 * 2^-7
+        amax = []
+        for m6 in mids6:
+            t = np.float32(m6 * np.float64(g_val))
+            b = S.bf16_round(np.array([t], np.float32))[0]
+            for d in (-1, 0, 1):
+                amax.append(S.bf16_to_f32(np.array([int(b) + d], np.uint16))[0])
+        amax = np.array(amax, np.float32)
+        N = len(amax)
+        rows = np.zeros((N, hkv, 128), np.float32)
+        rng = np.random.default_rng(5)
+        for blk in range(8):
+            rows[:, 0, 16 * blk] = amax * (1 if blk % 2 == 0 else -1)
+            rows[:, 0, 16 * blk + 1: 16 * blk + 16] = amax[:, None] * rng.uniform(-1, 1, (N, 15))
+        bits = S.bf16_round(rows)
+        r32 = S.bf16_to_f32(bits)
+        g = np.array([g_val, g_val], np.float32)
+        kc, ks = O.quantize_rows(r32, g[0])
+        pages = P.Pages(1, N, True)
+        cache = lib.CacheLayer(pages.num_pages, pages.page_size, hkv, k_flags=0)
+        cache.gscale.copy_(torch.from_numpy(g))
+        lib.quantize_append_kv(cache.struct(), P.to_dev_u16(bits), P.to_dev_u16(bits),
+                               P.to_dev_i32(pages.slots(0, 0, N)), N)
+        torch.cuda.synchronize()
+        gc, gs = P.rows_from_cache_vec(cache.k_data.cpu().numpy(), cache.k_scales.cpu().numpy(), pages, hkv, 0, N)
+        assert np.array_equal(gs, ks), np.argwhere(gs != ks)[:5]
+        assert np.array_equal(gc, kc)
+        gc, gs = P.rows_from_cache_vec(cache.v_data.cpu().numpy(), cache.v_scales.cpu().numpy(), pages, hkv, 0, N,
+                                       values=True)
+        assert np.array_equal(gs, ks) and np.array_equal(gc, kc)
+        # the ties really are ties for the power-of-two scale: every code 1..126 is hit
+        if g_val == np.float32(2.0 ** -9):
+            assert set(np.unique(ks[:, 0, 0])) >= set(range(1, 127))
+
+
 def test_append_canaries_and_skipped_slots(lib):
     """Only the addressed slots change; negative and out-of-range slots write nothing."""
     rng = np.random.default_rng(12)
