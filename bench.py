@@ -60,6 +60,9 @@ def parse():
                     help="comma-separated split sizes: report the decode launch time of each")
     ap.add_argument("--profile-pass", action="store_true",
                     help="short run for rocprofv3: few steps, no CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (5 times): the reference kernel for scaling "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counts to bytes")
     ap.add_argument("--separate", action="store_true",
                     help="decode step as two calls per layer (quantize_append_kv, then "
                          "decode_attention_nvfp4) instead of the fused decode_append_attention_nvfp4")
@@ -547,6 +550,50 @@ def decode_cpu_baseline(wl, budget_s=12.0):
                 oracle_effective_gbs=round(wl.step_bytes() / step_s / 1e9, 6))
 
 
+COPY_BYTES = 256 << 20
+
+
+def copy_calibration(torch):
+    """A plain device-to-device copy of 256 MiB, five times (reference kernel for the HBM
+    byte counters: it reads and writes exactly COPY_BYTES per dispatch)."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] copy calibration: 5 x {COPY_BYTES} B device copies", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    """sha256 over the sources of the decode/append kernels (the traffic figures in profiles/
+    hold for this exact source)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "nvfp4_bit_kv_amd", "csrc")
+    for name in ("nvkv_decode.hip", "nvkv_encode.hpp", "nvkv_device.hpp", "nvkv_quantize.hip"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_per_launch(wl):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 FETCH_SIZE +
+    WRITE_SIZE summary of this workload, or None when there is none or the kernel sources
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        text = f.read()
+    if "```json" not in text:
+        return None
+    rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    if rec.get("kernel_source_sha256") != kernel_source_hash() or rec.get("kernel") != wl.kernel_label:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -578,14 +625,16 @@ def main():
     replay_ok = bool(torch.equal(wl.snapshot(), eager0))
     del eager0
     # the pages' timing protocol: 3 repetitions x 30 runs; median and spread per step
-    reps = []
-    for _ in range(3):
-        reps.append(time_graphs(torch, graphs, 30, 3) / 30)
-    protocol = {"repetitions": 3, "runs": 30, "median_ms": round(float(np.median(reps)), 5),
-                "min_ms": round(float(np.min(reps)), 5), "max_ms": round(float(np.max(reps)), 5)}
+    protocol = None
+    if not args.profile_pass:
+        reps = []
+        for _ in range(3):
+            reps.append(time_graphs(torch, graphs, 30, 3) / 30)
+        protocol = {"repetitions": 3, "runs": 30, "median_ms": round(float(np.median(reps)), 5),
+                    "min_ms": round(float(np.min(reps)), 5), "max_ms": round(float(np.max(reps)), 5)}
     # the same decode step as two calls per layer, for comparison
     separate_ms = None
-    if isinstance(wl, DecodeStep) and wl.mode == "fused":
+    if isinstance(wl, DecodeStep) and wl.mode == "fused" and not args.profile_pass:
         sgraphs = [capture(torch, lambda cp=cp: wl.step(cp, "separate")) for cp in range(wl.copies)]
         separate_ms = round(time_graphs(torch, sgraphs, max(10, args.steps // 4), 3) / max(10, args.steps // 4), 5)
         del sgraphs
@@ -597,6 +646,8 @@ def main():
 
     if args.sweep_splits and isinstance(wl, DecodeStep):
         sweep_splits(torch, wl, [int(x) for x in args.sweep_splits.split(",")])
+    if args.copy_calibration:
+        copy_calibration(torch)
     print("[bench] oracle check / cpu baseline", file=sys.stderr, flush=True)
     check = None if args.no_check else wl.check()
     base = None if args.no_cpu_baseline else wl.cpu_baseline()
@@ -624,7 +675,7 @@ def main():
         "hbm_frac_of_step": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_per_launch(wl),
             "kernel": wl.kernel_label,
             "bytes_per_launch": wl.launch_bytes(), "avg_launch_us": round(avg_launch * 1e6, 3),
             "min_launch_us": round(float(np.min(durs)) * 1e6, 3),
