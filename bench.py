@@ -119,7 +119,8 @@ class DecodeStep:
         self.mode = "fused" if fused else "separate"
         self.kernel_label = (
             "k_decode<append> (decode_append_attention_nvfp4: new-token quantise/append + split-K decode + "
-            "in-kernel cross-split merge, one launch), per layer" if fused else
+            "in-kernel cross-split merge, one launch; for long splits the library issues k_quantize_append "
+            "of the new tokens + k_decode), per layer" if fused else
             "k_decode (decode_attention_nvfp4: split-K decode + in-kernel cross-split merge), per layer")
         B, T, hkv = self.B, self.T, self.hkv
         self.pps = (T + PAGE - 1) // PAGE

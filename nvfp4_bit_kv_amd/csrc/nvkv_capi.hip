@@ -138,9 +138,24 @@ nvkv_status decode_common(const nvkv_layer* layer, const uint16_t* q, const uint
       return fail(NVKV_ERR_WORKSPACE, "workspace missing, too small or not 256-byte aligned");
   }
   (void)hipGetLastError();
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (append && plan.pipe2) {
+    // Long splits: the decode dominates and the fused kernel would give up a cache
+    // wavefront, so the new tokens go in with the append kernel first (same effect).
+    const int64_t cap_pages = static_cast<int64_t>(max_pages_per_seq) * layer->page_size;
+    const int32_t seq_cap = static_cast<int32_t>(cap_pages < max_seq_len ? cap_pages : max_seq_len);
+    const nvkv_status s1 = hip_status(nvkv::launch_quantize_append_rows(*layer, k_new, v_new, nullptr, B, page_table,
+                                                                        seq_lens, max_pages_per_seq, seq_cap, hs),
+                                      "decode-append: append launch");
+    if (s1 != NVKV_OK) return s1;
+    nvkv::DecodePlan dplan = nvkv::plan_decode(B, layer->num_kv_heads, max_seq_len, split_tokens, false);
+    return hip_status(nvkv::launch_decode(*layer, q, nullptr, nullptr, B, Hq, page_table, max_pages_per_seq,
+                                          seq_lens, max_seq_len, sm_scale, out, workspace, dplan, hs),
+                      "decode-append: decode launch");
+  }
   return hip_status(nvkv::launch_decode(*layer, q, append ? k_new : nullptr, append ? v_new : nullptr, B, Hq,
                                         page_table, max_pages_per_seq, seq_lens, max_seq_len, sm_scale, out,
-                                        workspace, plan, static_cast<hipStream_t>(stream)),
+                                        workspace, plan, hs),
                     append ? "decode-append launch" : "decode launch");
 }
 }  // namespace

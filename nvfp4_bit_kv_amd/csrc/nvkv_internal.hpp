@@ -9,6 +9,12 @@ namespace nvkv {
 
 hipError_t launch_quantize_append(const nvkv_layer& L, const uint16_t* k_new, const uint16_t* v_new,
                                   const int32_t* slots, int32_t N, hipStream_t stream);
+// slots == nullptr: row n is the new token of sequence n, at position
+// min(seq_lens[n], seq_cap) - 1 taken through the page table.
+hipError_t launch_quantize_append_rows(const nvkv_layer& L, const uint16_t* k_new, const uint16_t* v_new,
+                                       const int32_t* slots, int32_t N, const int32_t* page_table,
+                                       const int32_t* seq_lens, int32_t max_pages_per_seq, int32_t seq_cap,
+                                       hipStream_t stream);
 
 hipError_t launch_calibrate(const uint16_t* k_win, const uint16_t* v_win, int32_t W, int32_t T, int32_t hkv,
                             int32_t exclude_pos0, uint32_t k_flags, float* s_out, float* r_out, float* g_out,

@@ -31,6 +31,12 @@ struct AppendArgs {
   uint32_t flags;             // key transform flags (0 for V)
   int32_t fmt;                // NVKV_FMT_*
   int32_t quad_words;         // 1: codes in the quad-interleaved word layout (NVFP4 values)
+  // slots == nullptr: row n is the new token of sequence n, at position min(seq_lens[n],
+  // seq_cap) - 1 of the paged sequence (nothing is written when that length is 0)
+  const int32_t* page_table;  // [B][max_pages_per_seq]
+  const int32_t* seq_lens;    // [B]
+  int32_t max_pages_per_seq;
+  int32_t seq_cap;
 };
 
 struct AppendPair {
@@ -52,7 +58,18 @@ __global__ void __launch_bounds__(256) k_quantize_append(AppendPair p) {
   float y[kBlock];
   uint4 raw0, raw1;
   load_block_bf16(a.src + static_cast<int64_t>(row) * kHeadDim + blk * kBlock, y, raw0, raw1);
-  const int32_t slot = a.slots[n];
+  int32_t slot;
+  if (a.slots) {
+    slot = a.slots[n];
+  } else {
+    int32_t len = a.seq_lens[n];
+    len = len > a.seq_cap ? a.seq_cap : len;
+    if (len <= 0) return;
+    const int32_t pos = len - 1;
+    const int64_t pg = a.page_table[static_cast<int64_t>(n) * a.max_pages_per_seq + pos / a.page_size];
+    const int64_t s64 = pg * a.page_size + pos % a.page_size;
+    slot = (pg < 0 || s64 >= a.max_slot) ? -1 : static_cast<int32_t>(s64);
+  }
   const float gsc = a.fmt == 0 ? 1.0f : *a.gscale;
   if (slot < 0 || static_cast<int64_t>(slot) >= a.max_slot) return;
   const int32_t page = slot / a.page_size;
@@ -168,15 +185,23 @@ __global__ void k_calib_finalize_g(float* g_out, int do_k, int do_v) {
 // ---------------------------------------------------------------------------------------
 hipError_t launch_quantize_append(const nvkv_layer& L, const uint16_t* k_new, const uint16_t* v_new,
                                   const int32_t* slots, int32_t N, hipStream_t stream) {
+  return launch_quantize_append_rows(L, k_new, v_new, slots, N, nullptr, nullptr, 0, 0, stream);
+}
+
+hipError_t launch_quantize_append_rows(const nvkv_layer& L, const uint16_t* k_new, const uint16_t* v_new,
+                                       const int32_t* slots, int32_t N, const int32_t* page_table,
+                                       const int32_t* seq_lens, int32_t max_pages_per_seq, int32_t seq_cap,
+                                       hipStream_t stream) {
   AppendPair p{};
   const int32_t rows = N * L.num_kv_heads;
   const int64_t max_slot = static_cast<int64_t>(L.num_pages) * L.page_size;
   p.a[0] = AppendArgs{k_new, slots, rows, L.num_kv_heads, L.page_size, max_slot,
                       static_cast<uint8_t*>(L.k_data), L.k_scales, L.k_inv_smooth,
-                      L.global_scale + 0, L.k_fmt == NVKV_FMT_NVFP4 ? L.k_flags : 0u, L.k_fmt, 0};
+                      L.global_scale + 0, L.k_fmt == NVKV_FMT_NVFP4 ? L.k_flags : 0u, L.k_fmt, 0,
+                      page_table, seq_lens, max_pages_per_seq, seq_cap};
   p.a[1] = AppendArgs{v_new, slots, rows, L.num_kv_heads, L.page_size, max_slot,
                       static_cast<uint8_t*>(L.v_data), L.v_scales, nullptr,
-                      L.global_scale + 1, 0u, L.v_fmt, 1};
+                      L.global_scale + 1, 0u, L.v_fmt, 1, page_table, seq_lens, max_pages_per_seq, seq_cap};
   const int wg = (rows + kRowsPerWg - 1) / kRowsPerWg;
   p.wg_k = wg;
   hipLaunchKernelGGL(k_quantize_append, dim3(2 * wg), dim3(256), 0, stream, p);
