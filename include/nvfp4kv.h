@@ -158,9 +158,10 @@ NVKV_API size_t nvkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, 
  *   Query head hq reads KV head hq / (Hq / Hkv); Hq must be 4 * Hkv.
  *   out:        fp32 [B][Hq][128] = softmax(sm_scale * q' . k_hat) v_hat.
  *   workspace:  device scratch of at least nvkv_decode_workspace_bytes(...) bytes, 256-byte
- *               aligned (NULL allowed when that size is 0).  Its first B*Hkv 32-bit words are
- *               arrival counters, the rest holds the per-split partials.  Zero-fill it before
- *               its first use (and again if a later call has a larger B*Hkv); every completed
+ *               aligned (NULL allowed when that size is 0).  Its first 256*B*Hkv bytes hold
+ *               one arrival counter per (sequence, KV head), 256 bytes apart; the rest holds
+ *               the per-split partials.  Zero-fill it before its first use (and again if a
+ *               later call has a larger B*Hkv); every completed
  *               call leaves the counters at zero, so the workspace can be reused by calls with
  *               other split counts or lengths without clearing.  Calls that may run
  *               concurrently must not share a workspace.
