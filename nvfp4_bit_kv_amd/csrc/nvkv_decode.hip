@@ -466,6 +466,7 @@ __device__ __forceinline__ void new_token_load(const DecodeArgs& a, int b, int h
 // One Hadamard stage across lanes: element i of this lane pairs with element i of lane
 // (lane ^ m), the lower lane keeping the sum, the upper the difference (lower - upper).
 __device__ __forceinline__ void had_cross(float (&y)[4], int lane, int m) {
+#pragma clang fp contract(off)   // part of the bit-exact key transform
   const bool upper = (lane & m) != 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -480,6 +481,7 @@ __device__ __forceinline__ void had_cross(float (&y)[4], int lane, int m) {
 template <bool KBF16>
 __device__ __forceinline__ void new_token_encode(const DecodeArgs& a, int h, int lane, const NewTokenRegs& R,
                                                  int32_t pg, int off, bool ok, NewTokenStage& st) {
+#pragma clang fp contract(off)   // part of the bit-exact key transform
   const bool is_v = lane >= 32;
   const int blk = (lane >> 2) & 7, qtr = lane & 3;
   const int64_t ph = static_cast<int64_t>(ok ? pg : 0) * a.hkv + h;

@@ -1,7 +1,7 @@
 // NVFP4 encoder and key transform, one lane per 16-element block (8 lanes per 128-wide row).
 // The key transform is part of the bit-exact encoding: every fp32 multiply and add below
-// must round on its own, so the whole header is compiled with floating-point contraction
-// off (scoped with push/pop, so an including unit keeps its own setting).
+// must round on its own, so each function turns floating-point contraction off for its own
+// body (the including unit keeps its setting for everything else).
 //
 // Sources: [cache post] = rstation.ai post "NVFP4 attention cache on W4A4 Qwen3-8B: static
 // key smoothing is near-lossless, key rotations hurt" (cache-config table: per-channel
@@ -12,8 +12,6 @@
 
 #include "nvkv_device.hpp"
 
-#pragma float_control(push)
-#pragma clang fp contract(off)
 
 namespace nvkv {
 
@@ -22,6 +20,7 @@ __device__ __forceinline__ float xor_lanes(float v, int mask) { return __shfl_xo
 
 // Smoothing: y_j = fl32(x_j * r_j) for the 16 elements of this lane's block.
 __device__ __forceinline__ void smooth_block(float (&y)[kBlock], const float* __restrict__ r16) {
+#pragma clang fp contract(off)
   const float4* rp = reinterpret_cast<const float4*>(r16);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -37,6 +36,7 @@ __device__ __forceinline__ void smooth_block(float (&y)[kBlock], const float* __
 // order; a stage maps the pair (i, i+h) with (i & h) == 0 to (y_i + y_{i+h}, y_i - y_{i+h}).
 // Stages 1..8 stay inside a lane's block; stages 16, 32, 64 pair block b with b ^ 1, 2, 4.
 __device__ __forceinline__ void hadamard_row(float (&y)[kBlock], int blk) {
+#pragma clang fp contract(off)
 #pragma unroll
   for (int h = 1; h < kBlock; h <<= 1) {
 #pragma unroll
@@ -63,6 +63,7 @@ __device__ __forceinline__ void hadamard_row(float (&y)[kBlock], int blk) {
 // A/(6g)?  6 * midpoint = 3 * (v_k + v_{k+1}) is exact in fp32, and the sign of the fused
 // A - t6*g is that of the exact difference; at an exact midpoint the even code wins.
 __device__ __forceinline__ bool e4m3_mid_passed(uint32_t k, float A, float g) {
+#pragma clang fp contract(off)
   const float t6 = 3.0f * (e4m3_value(k) + e4m3_value(k + 1));
   const float d = __builtin_fmaf(-t6, g, A);
   return (d > 0.0f) || (d == 0.0f && ((k + 1) & 1u) == 0u);
@@ -73,6 +74,7 @@ __device__ __forceinline__ bool e4m3_mid_passed(uint32_t k, float A, float g) {
 // error is a few ulp, far below the 1/16 relative spacing of the codes, so the exact answer
 // is the candidate or a neighbour); the exact midpoint tests on both sides settle it.
 __device__ __forceinline__ uint32_t e4m3_scale_code(float A, float g) {
+#pragma clang fp contract(off)
   if (A == 0.0f) return 0u;                                          // all-zero block
   const float x = A * __builtin_amdgcn_rcpf(6.0f * g);
   int c;
@@ -102,6 +104,7 @@ struct E2m1Thresholds {
 // round-to-nearest (ties to the even code) of the exact |y|/(sigma g), saturating at 6;
 // a zero magnitude is stored as code 0.  Three exact comparisons (binary search).
 __device__ __forceinline__ uint32_t e2m1_nibble(float y, const E2m1Thresholds& t, float g) {
+#pragma clang fp contract(off)
   const float a = fabsf(y);
   const bool b2 = __builtin_fmaf(-t.p3, g, a) >= 0.0f;            // 1.75: tie -> code 4
   const float t1 = b2 ? t.p5 : t.p1;                               // 3.5 / 0.75: tie -> up
@@ -117,6 +120,7 @@ __device__ __forceinline__ uint32_t e2m1_nibble(float y, const E2m1Thresholds& t
 // (byte k = nibble 2k | nibble 2k+1 << 4).
 __device__ __forceinline__ uint32_t encode_block(const float (&y)[kBlock], float g, uint32_t& lo,
                                                  uint32_t& hi) {
+#pragma clang fp contract(off)
   float A = 0.0f;
 #pragma unroll
   for (int i = 0; i < kBlock; ++i) A = fmaxf(A, fabsf(y[i]));
@@ -136,6 +140,7 @@ __device__ __forceinline__ uint32_t encode_block(const float (&y)[kBlock], float
 // Load this lane's 16 bf16 elements as fp32.
 __device__ __forceinline__ void load_block_bf16(const uint16_t* __restrict__ src, float (&y)[kBlock],
                                                 uint4& raw0, uint4& raw1) {
+#pragma clang fp contract(off)
   const uint4* p = reinterpret_cast<const uint4*>(src);
   raw0 = p[0];
   raw1 = p[1];
@@ -149,4 +154,3 @@ __device__ __forceinline__ void load_block_bf16(const uint16_t* __restrict__ src
 
 }  // namespace nvkv
 
-#pragma float_control(pop)
