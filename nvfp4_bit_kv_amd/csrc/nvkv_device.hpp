@@ -32,10 +32,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Value of a non-negative E4M3FN code 0..126, exact in fp32.
+// Value of a non-negative E4M3FN code 0..126, exact in fp32: (m/8 + [e > 0]) * 2^(max(e,1) - 7)
+// (one formula for normal and subnormal codes, so it compiles to straight-line code).
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
   const uint32_t e = c >> 3, m = c & 7u;
-  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : static_cast<float>(m) * 0x1p-9f;
+  const float frac = static_cast<float>(m) * 0.125f + (e ? 1.0f : 0.0f);
+  return __builtin_ldexpf(frac, static_cast<int>(e ? e : 1u) - 7);
 }
 
 // Neighbours of a positive finite fp32 value (bit-pattern steps).

@@ -7,23 +7,27 @@
 // (cache-config table).  [OSFP4] = paperlayer.ai summary of arXiv 2610.08231v1: the global
 // scale is static and calibration-based so blocks can be quantised as they arrive (section 3).
 //
-// Thread layout of every row kernel: 8 lanes per 128-element row, one 16-element block per
-// lane, 8 rows per wavefront, 4 wavefronts (32 rows) per workgroup.  Rows are independent;
-// the only cross-lane traffic is the Hadamard butterfly's three block-pair stages.
+// Every lane handles one 16-element block of a 128-element row.  The append kernel puts the
+// 8 blocks of a row 8 lanes apart (lane = 8 * block + token); the calibration kernels put
+// them in 8 consecutive lanes (8 rows per wavefront, 32 per workgroup).  The only cross-lane
+// traffic is the Hadamard butterfly's three block-pair stages.
 #include "nvkv_encode.hpp"
 #include "nvkv_internal.hpp"
 
 namespace nvkv {
 
-constexpr int kRowsPerWg = 32;
+// Append layout: a wavefront takes 8 consecutive new tokens of one KV head per pass, lane
+// = 8 * block + token, and makes kPasses passes; a workgroup is 4 wavefronts.  The
+// smoothing factors of a lane's block are loaded once and serve every pass.  Adjacent lanes
+// hold adjacent tokens, so the scale bytes and value words of a token quad are written by
+// adjacent lanes to adjacent bytes.
+constexpr int kTokPerPass = 8;
+constexpr int kPasses = 4;
+constexpr int kAppendWaves = 4;
+constexpr int kTokPerWg = kTokPerPass * kPasses * kAppendWaves;
 
 struct AppendArgs {
   const uint16_t* src;        // bf16 [N][Hkv][128]
-  const int32_t* slots;       // [N]
-  int32_t n_rows;             // N * Hkv
-  int32_t hkv;
-  int32_t page_size;
-  int64_t max_slot;           // num_pages * page_size
   uint8_t* codes;             // NVFP4 codes or BF16 rows
   uint8_t* scales;            // NVFP4 scales (unused for BF16)
   const float* inv_smooth;    // r [Hkv][128]
@@ -31,74 +35,104 @@ struct AppendArgs {
   uint32_t flags;             // key transform flags (0 for V)
   int32_t fmt;                // NVKV_FMT_*
   int32_t quad_words;         // 1: codes in the quad-interleaved word layout (NVFP4 values)
-  // slots == nullptr: row n is the new token of sequence n, at position min(seq_lens[n],
+};
+
+struct AppendPair {
+  AppendArgs a[2];            // [0] = keys, [1] = values
+  const int32_t* slots;       // [N]; nullptr: see below
+  // slots == nullptr: token n is the new token of sequence n, at position min(seq_lens[n],
   // seq_cap) - 1 of the paged sequence (nothing is written when that length is 0)
   const int32_t* page_table;  // [B][max_pages_per_seq]
   const int32_t* seq_lens;    // [B]
   int32_t max_pages_per_seq;
   int32_t seq_cap;
+  int32_t n_tokens;           // N
+  int32_t hkv;
+  int32_t page_size;
+  int64_t max_slot;           // num_pages * page_size
 };
 
-struct AppendPair {
-  AppendArgs a[2];            // [0] = keys, [1] = values
-  int32_t wg_k;               // workgroups that serve keys
-};
-
-__global__ void __launch_bounds__(256) k_quantize_append(AppendPair p) {
-  const int which = (static_cast<int>(blockIdx.x) >= p.wg_k) ? 1 : 0;
-  const AppendArgs a = which ? p.a[1] : p.a[0];   // uniform select, no dynamic indexing
-  const int wg = static_cast<int>(blockIdx.x) - (which ? p.wg_k : 0);
-  const int lane = threadIdx.x & 63;
-  const int blk = lane & 7;
-  const int row = wg * kRowsPerWg + (threadIdx.x >> 3);
-  if (row >= a.n_rows) return;                      // whole 8-lane row groups leave together
-  const int n = row / a.hkv;
-  const int h = row - n * a.hkv;
-  // independent loads first (row data, slot, tensor scale); the slot check comes after
-  float y[kBlock];
-  uint4 raw0, raw1;
-  load_block_bf16(a.src + static_cast<int64_t>(row) * kHeadDim + blk * kBlock, y, raw0, raw1);
-  int32_t slot;
-  if (a.slots) {
-    slot = a.slots[n];
-  } else {
-    int32_t len = a.seq_lens[n];
-    len = len > a.seq_cap ? a.seq_cap : len;
-    if (len <= 0) return;
-    const int32_t pos = len - 1;
-    const int64_t pg = a.page_table[static_cast<int64_t>(n) * a.max_pages_per_seq + pos / a.page_size];
-    const int64_t s64 = pg * a.page_size + pos % a.page_size;
-    slot = (pg < 0 || s64 >= a.max_slot) ? -1 : static_cast<int32_t>(s64);
-  }
-  const float gsc = a.fmt == 0 ? 1.0f : *a.gscale;
-  if (slot < 0 || static_cast<int64_t>(slot) >= a.max_slot) return;
-  const int32_t page = slot / a.page_size;
-  const int32_t off = slot - page * a.page_size;
-  const int64_t row_index = (static_cast<int64_t>(page) * a.hkv + h) * a.page_size + off;
-
-  if (a.fmt == 0) {  // BF16 keys: plain copy of the row
-    uint4* dst = reinterpret_cast<uint4*>(a.codes + row_index * (kHeadDim * 2) + blk * 32);
-    dst[0] = raw0;
-    dst[1] = raw1;
-    return;
-  }
-  if (a.flags & 1u) smooth_block(y, a.inv_smooth + h * kHeadDim + blk * kBlock);
-  if (a.flags & 2u) hadamard_row(y, blk);
-
-  uint32_t lo, hi;
-  const uint32_t S = encode_block(y, gsc, lo, hi);
-  if (!a.quad_words) {
-    *reinterpret_cast<uint2*>(a.codes + row_index * 64 + blk * 8) = make_uint2(lo, hi);
-  } else {
-    // words 2blk, 2blk+1 of token `off`: byte ((off/4)*16 + w)*16 + (off%4)*4 of the
-    // (page, head) block, which starts at the same place as in the row-major layout
-    uint8_t* wq = a.codes + (row_index - (off & 3)) * 64 + 32 * blk + 4 * (off & 3);
-    *reinterpret_cast<uint32_t*>(wq) = lo;
-    *reinterpret_cast<uint32_t*>(wq + 16) = hi;
-  }
-  const int64_t sbase = (static_cast<int64_t>(page) * a.hkv + h) * a.page_size * 8;
-  a.scales[sbase + ((off >> 2) * 8 + blk) * 4 + (off & 3)] = static_cast<uint8_t>(S);
+__device__ __forceinline__ int32_t append_slot(const AppendPair& p, int n) {
+  if (p.slots) return p.slots[n];
+  int32_t len = p.seq_lens[n];
+  len = len > p.seq_cap ? p.seq_cap : len;
+  if (len <= 0) return -1;
+  const int32_t pos = len - 1;
+  const int64_t pg = p.page_table[static_cast<int64_t>(n) * p.max_pages_per_seq + pos / p.page_size];
+  const int64_t s64 = pg * p.page_size + pos % p.page_size;
+  return (pg < 0 || s64 >= p.max_slot) ? -1 : static_cast<int32_t>(s64);
 }
+
+// grid: x = token chunks of kTokPerWg, y = KV head (y < Hkv: keys, else values)
+__global__ void __launch_bounds__(256) k_quantize_append(AppendPair p) {
+  const int which = static_cast<int>(blockIdx.y) >= p.hkv ? 1 : 0;
+  const AppendArgs a = which ? p.a[1] : p.a[0];   // uniform select, no dynamic indexing
+  const int h = static_cast<int>(blockIdx.y) - (which ? p.hkv : 0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int blk = lane >> 3, tok = lane & 7;
+  const bool smooth = a.fmt != NVKV_FMT_BF16 && (a.flags & 1u);
+  float r[kBlock];
+  if (smooth) {
+    const float4* rp = reinterpret_cast<const float4*>(a.inv_smooth + h * kHeadDim + blk * kBlock);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = rp[q];
+      r[4 * q] = v.x;
+      r[4 * q + 1] = v.y;
+      r[4 * q + 2] = v.z;
+      r[4 * q + 3] = v.w;
+    }
+  }
+  const float gsc = a.fmt == NVKV_FMT_BF16 ? 1.0f : *a.gscale;
+  const int n_wave = static_cast<int>(blockIdx.x) * kTokPerWg + wave * (kTokPerPass * kPasses);
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {   // unrolled: a pass's loads overlap the previous encode
+    const int n0 = n_wave + pass * kTokPerPass;
+    if (n0 >= p.n_tokens) break;                        // uniform
+    // tokens past the end compute on a clamped copy (every lane takes part in the
+    // cross-lane steps) and store nothing
+    const int n = n0 + tok < p.n_tokens ? n0 + tok : p.n_tokens - 1;
+    const bool live = n0 + tok < p.n_tokens;
+    // independent loads first (row block, slot); the slot check comes after
+    float y[kBlock];
+    uint4 raw0, raw1;
+    load_block_bf16(a.src + (static_cast<int64_t>(n) * p.hkv + h) * kHeadDim + blk * kBlock, y, raw0, raw1);
+    const int32_t slot = append_slot(p, n);
+    const bool ok = live && slot >= 0 && static_cast<int64_t>(slot) < p.max_slot;
+    const int32_t page = ok ? slot / p.page_size : 0;
+    const int32_t off = ok ? slot - page * p.page_size : 0;
+    const int64_t row_index = (static_cast<int64_t>(page) * p.hkv + h) * p.page_size + off;
+    if (a.fmt == NVKV_FMT_BF16) {  // BF16 keys: plain copy of the row
+      if (ok) {
+        uint4* dst = reinterpret_cast<uint4*>(a.codes + row_index * (kHeadDim * 2) + blk * 32);
+        dst[0] = raw0;
+        dst[1] = raw1;
+      }
+      continue;
+    }
+    if (smooth) {
+#pragma unroll
+      for (int i = 0; i < kBlock; ++i) y[i] = y[i] * r[i];
+    }
+    if (a.flags & 2u) hadamard_row<8>(y, blk);
+    uint32_t lo, hi;
+    const uint32_t S = encode_block(y, gsc, lo, hi);
+    if (!ok) continue;
+    if (!a.quad_words) {
+      *reinterpret_cast<uint2*>(a.codes + row_index * 64 + blk * 8) = make_uint2(lo, hi);
+    } else {
+      // words 2blk, 2blk+1 of token `off`: byte ((off/4)*16 + w)*16 + (off%4)*4 of the
+      // (page, head) block, which starts at the same place as in the row-major layout
+      uint8_t* wq = a.codes + (row_index - (off & 3)) * 64 + 32 * blk + 4 * (off & 3);
+      *reinterpret_cast<uint32_t*>(wq) = lo;
+      *reinterpret_cast<uint32_t*>(wq + 16) = hi;
+    }
+    const int64_t sbase = (static_cast<int64_t>(page) * p.hkv + h) * p.page_size * 8;
+    a.scales[sbase + ((off >> 2) * 8 + blk) * 4 + (off & 3)] = static_cast<uint8_t>(S);
+  }
+}
+
+constexpr int kRowsPerWg = 32;   // calibration kernels: rows per workgroup
 
 // ---------------------------------------------------------------------------------------
 // Calibration.  Max reductions over non-negative fp32 use unsigned atomicMax on the bit
@@ -193,18 +227,21 @@ hipError_t launch_quantize_append_rows(const nvkv_layer& L, const uint16_t* k_ne
                                        const int32_t* seq_lens, int32_t max_pages_per_seq, int32_t seq_cap,
                                        hipStream_t stream) {
   AppendPair p{};
-  const int32_t rows = N * L.num_kv_heads;
-  const int64_t max_slot = static_cast<int64_t>(L.num_pages) * L.page_size;
-  p.a[0] = AppendArgs{k_new, slots, rows, L.num_kv_heads, L.page_size, max_slot,
-                      static_cast<uint8_t*>(L.k_data), L.k_scales, L.k_inv_smooth,
-                      L.global_scale + 0, L.k_fmt == NVKV_FMT_NVFP4 ? L.k_flags : 0u, L.k_fmt, 0,
-                      page_table, seq_lens, max_pages_per_seq, seq_cap};
-  p.a[1] = AppendArgs{v_new, slots, rows, L.num_kv_heads, L.page_size, max_slot,
-                      static_cast<uint8_t*>(L.v_data), L.v_scales, nullptr,
-                      L.global_scale + 1, 0u, L.v_fmt, 1, page_table, seq_lens, max_pages_per_seq, seq_cap};
-  const int wg = (rows + kRowsPerWg - 1) / kRowsPerWg;
-  p.wg_k = wg;
-  hipLaunchKernelGGL(k_quantize_append, dim3(2 * wg), dim3(256), 0, stream, p);
+  p.a[0] = AppendArgs{k_new, static_cast<uint8_t*>(L.k_data), L.k_scales, L.k_inv_smooth, L.global_scale + 0,
+                      L.k_fmt == NVKV_FMT_NVFP4 ? L.k_flags : 0u, L.k_fmt, 0};
+  p.a[1] = AppendArgs{v_new, static_cast<uint8_t*>(L.v_data), L.v_scales, nullptr, L.global_scale + 1, 0u,
+                      L.v_fmt, 1};
+  p.slots = slots;
+  p.page_table = page_table;
+  p.seq_lens = seq_lens;
+  p.max_pages_per_seq = max_pages_per_seq;
+  p.seq_cap = seq_cap;
+  p.n_tokens = N;
+  p.hkv = L.num_kv_heads;
+  p.page_size = L.page_size;
+  p.max_slot = static_cast<int64_t>(L.num_pages) * L.page_size;
+  const dim3 grid((N + kTokPerWg - 1) / kTokPerWg, 2 * L.num_kv_heads);
+  hipLaunchKernelGGL(k_quantize_append, grid, dim3(64 * kAppendWaves), 0, stream, p);
   return hipGetLastError();
 }
 
