@@ -184,19 +184,29 @@ typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 
 __device__ __forceinline__ IterPages load_pages(const DecodeArgs& a, const_i32_ptr ptab, int t, int t_hi) {
   IterPages r;
+  int tb[2], idx[2];
 #pragma unroll
   for (int eta = 0; eta < 2; ++eta) {
-    int tb = t + 16 * eta;
-    if (tb >= t_hi) tb = (t_hi - 1) & ~15;
-    if (tb < 0) tb = 0;
-    if (a.page_shift >= 0) {
-      r.pg[eta] = ptab[tb >> a.page_shift];
-      r.off16[eta] = tb & (a.page_size - 1);
-    } else {
-      r.pg[eta] = ptab[tb / a.page_size];
-      r.off16[eta] = tb % a.page_size;
+    tb[eta] = t + 16 * eta;
+    if (tb[eta] >= t_hi) tb[eta] = (t_hi - 1) & ~15;
+    if (tb[eta] < 0) tb[eta] = 0;
+  }
+  // one branch for both halves
+  if (a.page_shift >= 0) {
+#pragma unroll
+    for (int eta = 0; eta < 2; ++eta) {
+      idx[eta] = tb[eta] >> a.page_shift;
+      r.off16[eta] = tb[eta] & (a.page_size - 1);
+    }
+  } else {
+#pragma unroll
+    for (int eta = 0; eta < 2; ++eta) {
+      idx[eta] = tb[eta] / a.page_size;
+      r.off16[eta] = tb[eta] % a.page_size;
     }
   }
+  r.pg[0] = ptab[idx[0]];
+  r.pg[1] = ptab[idx[1]];
   return r;
 }
 
@@ -386,22 +396,22 @@ __device__ __forceinline__ float2 load_coherent_f2(const float* p) {
 constexpr int kWaitVmcnt0 = 0x0F70;
 
 // Cross-split log-sum-exp merge run by the last workgroup of (b, h): wavefront w owns query
-// head 4h + w, lane l its dims 2l, 2l+1.  Splits are read 16 at a time with device-coherent
+// head 4h + w, lane l its dims 2l, 2l+1.  Splits are read G at a time with device-coherent
 // loads, all loads of a group independent (one memory round trip per group), and folded in
 // with a running max.
 constexpr int kMaxSplits = 1024;
 // Arrival counters sit 256 bytes apart: the device-scope atomics of all workgroups would
 // otherwise queue on one or two cache lines (measured: 0.8 us per launch at 4 x 2304).
 constexpr int kCounterStride = 64;
-constexpr int kMergeGroup = 16;
 
-__device__ __forceinline__ void merge_splits(const DecodeArgs& a, int64_t unit, int i, int d0) {
+template <int G>
+__device__ __forceinline__ void merge_splits(const DecodeArgs& a, int64_t unit, int i, int d0, float gv) {
   const int n = a.n_splits;
   float M = -INFINITY, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  for (int s0 = 0; s0 < n; s0 += kMergeGroup) {
-    float2 ml[kMergeGroup], o[kMergeGroup];
+  for (int s0 = 0; s0 < n; s0 += G) {
+    float2 ml[G], o[G];
 #pragma unroll
-    for (int k = 0; k < kMergeGroup; ++k) {
+    for (int k = 0; k < G; ++k) {
       const int sp = s0 + k < n ? s0 + k : n - 1;
       const int64_t slot = (unit * n + sp) * 4 + i;
       ml[k] = load_coherent_f2(a.ws_ml + slot * 2);
@@ -410,14 +420,14 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs& a, int64_t unit, 
     }
     float mx = M;
 #pragma unroll
-    for (int k = 0; k < kMergeGroup; ++k) mx = ml[k].y > 0.0f ? fmaxf(mx, ml[k].x) : mx;
+    for (int k = 0; k < G; ++k) mx = ml[k].y > 0.0f ? fmaxf(mx, ml[k].x) : mx;
     if (mx == -INFINITY) continue;                     // nothing in this group or before
     const float sc = exp2f(M - mx);                    // 0 while M is still -inf
     L *= sc;
     o0 *= sc;
     o1 *= sc;
 #pragma unroll
-    for (int k = 0; k < kMergeGroup; ++k) {
+    for (int k = 0; k < G; ++k) {
       const float w = ml[k].y > 0.0f ? exp2f(ml[k].x - mx) : 0.0f;
       L += w * ml[k].y;
       o0 += w * o[k].x;
@@ -425,7 +435,7 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs& a, int64_t unit, 
     }
     M = mx;
   }
-  const float f = L > 0.0f ? a.gscale[1] / L : 0.0f;
+  const float f = L > 0.0f ? gv / L : 0.0f;
   const int b = static_cast<int>(unit / a.hkv), h = static_cast<int>(unit % a.hkv);
   *reinterpret_cast<float2*>(a.out + (static_cast<int64_t>(b) * a.hq + 4 * h + i) * kHeadDim + d0) =
       make_float2(o0 * f, o1 * f);
@@ -649,28 +659,12 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   float2 sv = make_float2(1.0f, 1.0f);
   if (!KBF16 && (a.k_flags & NVKV_K_SMOOTH)) sv = reinterpret_cast<const float2*>(a.smooth + h * kHeadDim)[lane];
   const float gk = KBF16 ? 1.0f : a.gscale[0];
+  const float gv = a.gscale[1];                // value tensor scale, applied to the output
   NewTokenRegs nreg;
   if (app_wave) new_token_load<KBF16>(a, b, h, lane, nreg);
-  int seq_len = a.seq_lens[b];
-  seq_len = seq_len < 0 ? 0 : (seq_len > a.seq_cap ? a.seq_cap : seq_len);
+  // the value is first needed after the loads of the first iterations have been issued
+  const int seq_len_in = a.seq_lens[b];
   const int t_begin = split * a.split_tokens;
-  const int t_end = min(t_begin + a.split_tokens, seq_len);
-  const bool empty = t_begin >= t_end;                      // uniform across the workgroup
-  // APPEND: the new token is position t_new = seq_len - 1
-  const int t_new = seq_len - 1;
-  const bool owns_new = APPEND && !empty && t_new >= t_begin && t_new < t_begin + a.split_tokens;
-  const int t_read = APPEND ? min(t_end, t_new) : t_end;  // the cache wavefronts skip t_new
-  int32_t new_pg = 0;
-  int new_off = 0;
-  if (owns_new && app_wave) {
-    if (a.page_shift >= 0) {
-      new_pg = ptab[t_new >> a.page_shift];
-      new_off = t_new & (a.page_size - 1);
-    } else {
-      new_pg = ptab[t_new / a.page_size];
-      new_off = t_new % a.page_size;
-    }
-  }
 
   // First two iterations of this wavefront: addresses and loads are issued before the
   // sequence length arrives, bounded by the kernel arguments only (t_lim >= t_end), so the
@@ -689,6 +683,25 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
     issue_loads<KBF16>(hb1, ln, buf1);
   }
   IterPages pnext = load_pages(a, ptab, t0 + (PIPE2 ? 2 : 1) * step, t_lim > 0 ? t_lim : 1);
+
+  const int seq_len = seq_len_in < 0 ? 0 : (seq_len_in > a.seq_cap ? a.seq_cap : seq_len_in);
+  const int t_end = min(t_begin + a.split_tokens, seq_len);
+  const bool empty = t_begin >= t_end;                      // uniform across the workgroup
+  // APPEND: the new token is position t_new = seq_len - 1
+  const int t_new = seq_len - 1;
+  const bool owns_new = APPEND && !empty && t_new >= t_begin && t_new < t_begin + a.split_tokens;
+  const int t_read = APPEND ? min(t_end, t_new) : t_end;  // the cache wavefronts skip t_new
+  int32_t new_pg = 0;
+  int new_off = 0;
+  if (owns_new && app_wave) {
+    if (a.page_shift >= 0) {
+      new_pg = ptab[t_new >> a.page_shift];
+      new_off = t_new & (a.page_size - 1);
+    } else {
+      new_pg = ptab[t_new / a.page_size];
+      new_off = t_new % a.page_size;
+    }
+  }
 
   // ---------------- query prologue: wavefront w < 4 prepares query head 4h + w ----------------
   if (!empty && q_wave) {
@@ -831,19 +844,38 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   const int d0 = 2 * (tid & 63);
   float M = -INFINITY, Lw = 0.0f, o0 = 0.0f, o1 = 0.0f;
   if (owner) {
-    for (int w = 0; w < nw; ++w) M = fmaxf(M, red_l[w][i] > 0.0f ? red_m[w][i] : -INFINITY);
-    for (int w = 0; w < nw; ++w) {
-      if (red_l[w][i] > 0.0f) {
-        const float wt = exp2f(red_m[w][i] - M);
-        Lw += wt * red_l[w][i];
-        o0 += wt * red_o[w][i][d0];
-        o1 += wt * red_o[w][i][d0 + 1];
-      }
+    // Every wavefront's entries are read at once and without branches (a loop of dependent
+    // LDS reads costs a round trip per read); entries of wavefronts >= nw are replaced.
+    constexpr int kRed = PIPE2 ? 8 : kMaxWaves;
+    float mw[kRed], lw[kRed];
+    float2 ow[kRed];
+#pragma unroll
+    for (int w = 0; w < kRed; ++w) {
+      mw[w] = red_m[w][i];
+      lw[w] = red_l[w][i];
+      ow[w] = *reinterpret_cast<const float2*>(&red_o[w][i][d0]);
+    }
+    __builtin_amdgcn_sched_barrier(0);      // keep the reads together, ahead of the arithmetic
+#pragma unroll
+    for (int w = 0; w < kRed; ++w) {
+      const bool in = w < nw;
+      mw[w] = (in && lw[w] > 0.0f) ? mw[w] : -INFINITY;
+      lw[w] = in ? lw[w] : 0.0f;
+      ow[w] = in ? ow[w] : make_float2(0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int w = 0; w < kRed; ++w) M = fmaxf(M, mw[w]);
+#pragma unroll
+    for (int w = 0; w < kRed; ++w) {
+      const float wt = lw[w] > 0.0f ? exp2f(mw[w] - M) : 0.0f;
+      Lw += wt * lw[w];
+      o0 += wt * ow[w].x;
+      o1 += wt * ow[w].y;
     }
   }
   if (a.n_splits == 1) {
     if (owner) {
-      const float f = Lw > 0.0f ? a.gscale[1] / Lw : 0.0f;
+      const float f = Lw > 0.0f ? gv / Lw : 0.0f;
       float* out_row = a.out + (static_cast<int64_t>(b) * a.hq + 4 * h + i) * kHeadDim + d0;
       *reinterpret_cast<float2*>(out_row) = make_float2(o0 * f, o1 * f);
     }
@@ -868,7 +900,11 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   }
   __syncthreads();
   if (!mrg_last || !owner) return;
-  merge_splits(a, unit, i, d0);
+  // groups of 8 splits when that covers them all (16-entry groups would be half padding)
+  if (a.n_splits <= 8)
+    merge_splits<8>(a, unit, i, d0, gv);
+  else
+    merge_splits<16>(a, unit, i, d0, gv);
   if (tid == 0) __hip_atomic_store(a.counters + unit * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
