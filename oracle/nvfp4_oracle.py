@@ -25,6 +25,8 @@ What the oracle computes (plain, slow, obviously correct; NumPy, fp64 unless not
   * dequantize          -- code value * block scale * tensor scale, in fp64 (exact).
   * query_transform     -- q*s, optionally H(q*s)/128, in fp64.
   * attention           -- textbook softmax attention over the dequantised cache, fp64.
+  * causal_attention    -- the same for a block of query positions with the causal mask
+                           (teacher-forced evaluation over the cache), fp64.
 
 Readings taken where the pages leave a step open (each is repeated in the design notes):
   - tensor scale g = amax / (6*448), from calibration windows, over ALL positions of the
@@ -38,6 +40,8 @@ Readings taken where the pages leave a step open (each is repeated in the design
   - Hadamard is the Sylvester +-1 matrix applied to keys unnormalised (stages h=1..64,
     (a,b) -> (a+b, a-b), each rounded to fp32); the query side carries the exact 1/128.
   - smoothing is applied before the Hadamard basis when both are selected.
+  - a block of Tq queries of a sequence holding n cached tokens sits at positions
+    n-Tq .. n-1 (the block's own keys are in the cache); position p sees keys 0..p.
 
 Every function here is pinned by a CPU test against something other than itself
 (brute-force nearest search with exact rationals, closed forms printed on the pages,
@@ -281,6 +285,38 @@ def attention(qp: np.ndarray, k_hat: list, v_hat: list, seq_lens, sm_scale: floa
             p = np.exp(e - e.max())
             p /= p.sum()
             out[b, hq] = p @ V[:, h, :]
+    return out
+
+
+def causal_attention(qp: np.ndarray, k_hat: list, v_hat: list, seq_lens, sm_scale: float):
+    """Textbook causal GQA attention of a block of query positions over the dequantised
+    cache, in fp64 ([cache post] opening paragraph: the model is evaluated teacher-forced over
+    full windows, with attention reading the fake-quantised post-RoPE cache; the mask is the
+    causal mask of a decoder, each position attending to itself and earlier positions).
+
+    qp: [B][Tq][Hq][128] transformed queries.  Query i of sequence b sits at position
+    p = seq_lens[b] - Tq + i and attends to keys 0..p of k_hat[b], v_hat[b] ([n_b][Hkv][128],
+    n_b >= seq_lens[b]); a row with p < 0 has no keys and is zero.  Query head hq reads KV
+    head hq // (Hq/Hkv).  Output [B][Tq][Hq][128]."""
+    qp = np.asarray(qp, dtype=np.float64)
+    B, Tq, Hq, D = qp.shape
+    out = np.zeros((B, Tq, Hq, D), dtype=np.float64)
+    for b in range(B):
+        n = int(seq_lens[b])
+        K = np.asarray(k_hat[b], dtype=np.float64)
+        V = np.asarray(v_hat[b], dtype=np.float64)
+        Hkv = K.shape[1]
+        grp = Hq // Hkv
+        for i in range(Tq):
+            p = n - Tq + i
+            if p < 0:
+                continue
+            for hq in range(Hq):
+                h = hq // grp
+                e = sm_scale * (K[:p + 1, h, :] @ qp[b, i, hq])
+                w = np.exp(e - e.max())
+                w /= w.sum()
+                out[b, i, hq] = w @ V[:p + 1, h, :]
     return out
 
 

@@ -74,6 +74,35 @@ def _attention_wrong_group(qp, k_hat, v_hat, seq_lens, sm_scale):
     return out
 
 
+def _causal_sees_one_less(qp, k_hat, v_hat, seq_lens, sm_scale):
+    """Off-by-one mask: position p attends to keys 0..p-1 (p = 0 then sees key 0)."""
+    qp = np.asarray(qp, np.float64)
+    B, Tq, Hq, D = qp.shape
+    out = np.zeros((B, Tq, Hq, D))
+    for b in range(B):
+        n = int(seq_lens[b])
+        K = np.asarray(k_hat[b], np.float64)
+        V = np.asarray(v_hat[b], np.float64)
+        grp = Hq // K.shape[1]
+        for i in range(Tq):
+            p = n - Tq + i
+            if p < 0:
+                continue
+            last = max(p, 1)
+            for hq in range(Hq):
+                e = sm_scale * (K[:last, hq // grp] @ qp[b, i, hq])
+                w = np.exp(e - e.max())
+                out[b, i, hq] = (w / w.sum()) @ V[:last, hq // grp]
+    return out
+
+
+def _causal_wrong_offset(qp, k_hat, v_hat, seq_lens, sm_scale):
+    """Queries placed at positions 0..Tq-1 instead of n-Tq..n-1."""
+    qp = np.asarray(qp, np.float64)
+    Tq = qp.shape[1]
+    return ORIG_CA(qp, k_hat, v_hat, [min(int(n), Tq) for n in seq_lens], sm_scale)
+
+
 def _dequant_drop_g(codes, scales, g):
     return ORIG_DQ(codes, scales, 1.0)
 
@@ -82,6 +111,7 @@ ORIG_Q = O.quantize_rows
 ORIG_KT = O.key_transform
 ORIG_CAL = O.calibrate
 ORIG_DQ = O.dequantize
+ORIG_CA = O.causal_attention
 
 CASES = [
     ("rne_grid_index", _ties_to_odd, [C.test_e4m3_block_scale_vs_fraction_brute_force,
@@ -94,6 +124,9 @@ CASES = [
     ("calibrate", _calibrate_keep_pos0, [T.test_calibrate_excludes_position0_and_rounds_exactly]),
     ("attention", _attention_wrong_group, [T.test_attention_matches_torch_sdpa_fp64]),
     ("dequantize", _dequant_drop_g, [C.test_dequantize_exact_and_roundtrip_error_bound]),
+    ("causal_attention", _causal_sees_one_less, [T.test_causal_attention_matches_torch_sdpa_fp64,
+                                                 T.test_causal_attention_special_cases]),
+    ("causal_attention", _causal_wrong_offset, [T.test_causal_attention_matches_torch_sdpa_fp64]),
 ]
 
 

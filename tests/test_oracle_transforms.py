@@ -10,6 +10,9 @@
   square root (checked with exact rationals), g = amax/2688 over transformed keys.
 * attention: torch's scaled_dot_product_attention in fp64 as a library reference, and the
   special cases n = 1, zero query, identical keys, empty sequence.
+* causal attention: torch's scaled_dot_product_attention in fp64 with an explicit
+  position-offset causal mask, and closed forms: position 0 returns v_0; identical keys give
+  the running mean of V; rows before the sequence start are zero.
 * sizes printed on the pages (tests/golden/page_facts.json).
 """
 import json
@@ -146,6 +149,59 @@ def test_attention_special_cases():
     Ksame = [np.repeat(K[0][:1], 6, axis=0)]
     assert np.allclose(O.attention(q, Ksame, V, [6], 0.1)[0], V[0][:, 0].mean(0))  # same keys
     assert np.all(O.attention(q, K, V, [0], 0.1) == 0)                               # empty
+
+
+def _sdpa_causal_ref(qp, K, V, n, Hq):
+    """Library reference: torch SDPA in fp64, GQA by repeating KV heads, boolean mask with
+    query i at position n - Tq + i seeing keys 0..n-Tq+i."""
+    Tq = qp.shape[0]
+    Hkv = K.shape[1]
+    kk = torch.from_numpy(K[:n]).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)     # [Hq][n][D]
+    vv = torch.from_numpy(V[:n]).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+    qq = torch.from_numpy(qp).permute(1, 0, 2)                                           # [Hq][Tq][D]
+    pos = n - Tq + np.arange(Tq)
+    mask = torch.from_numpy(np.arange(n)[None, :] <= pos[:, None])                       # [Tq][n]
+    return qq, kk, vv, mask, pos
+
+
+def test_causal_attention_matches_torch_sdpa_fp64():
+    rng = np.random.default_rng(14)
+    B, Tq, Hq, Hkv = 3, 9, 8, 2
+    seq = [23, 9, 40]
+    qp = rng.standard_normal((B, Tq, Hq, 128))
+    K = [rng.standard_normal((n + 3, Hkv, 128)) for n in seq]
+    V = [rng.standard_normal((n + 3, Hkv, 128)) for n in seq]
+    out = O.causal_attention(qp, K, V, seq, 0.11)
+    for b, n in enumerate(seq):
+        qq, kk, vv, mask, pos = _sdpa_causal_ref(qp[b], K[b], V[b], n, Hq)
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask, scale=0.11)
+        assert np.allclose(out[b], ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_causal_attention_special_cases():
+    rng = np.random.default_rng(15)
+    n, Tq = 12, 12
+    K = [rng.standard_normal((n, 1, 128))]
+    V = [rng.standard_normal((n, 1, 128))]
+    q = rng.standard_normal((1, Tq, 4, 128))
+    out = O.causal_attention(q, K, V, [n], 0.2)
+    # full window: position 0 sees only itself
+    assert np.allclose(out[0, 0], np.broadcast_to(V[0][0, 0], (4, 128)), rtol=0, atol=1e-15)
+    # identical keys: uniform weights, so row i is the running mean of v_0..v_i
+    Ksame = [np.repeat(K[0][:1], n, axis=0)]
+    run_mean = np.cumsum(V[0][:, 0], axis=0) / np.arange(1, n + 1)[:, None]
+    out_same = O.causal_attention(q, Ksame, V, [n], 0.2)
+    for hq in range(4):
+        assert np.allclose(out_same[0, :, hq], run_mean, rtol=1e-12, atol=1e-12)
+    # more queries than cached tokens: the first Tq - n rows come before the sequence start
+    q2 = rng.standard_normal((1, 5, 4, 128))
+    out2 = O.causal_attention(q2, K, V, [3], 0.2)
+    assert np.all(out2[0, :2] == 0)
+    assert np.allclose(out2[0, 2], np.broadcast_to(V[0][0, 0], (4, 128)), rtol=0, atol=1e-15)
+    # two keys: the weight of key 1 is the logistic function of the score difference
+    e0, e1 = 0.2 * (K[0][0, 0] @ q[0, 1, 0]), 0.2 * (K[0][1, 0] @ q[0, 1, 0])
+    w1 = 1.0 / (1.0 + np.exp(e0 - e1))
+    assert np.allclose(out[0, 1, 0], (1 - w1) * V[0][0, 0] + w1 * V[0][1, 0], rtol=1e-12, atol=1e-12)
 
 
 def test_sizes_printed_on_the_pages():
