@@ -572,7 +572,7 @@ def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nvfp4_bit_kv_amd", "csrc")
-    for name in ("nvkv_decode.hip", "nvkv_encode.hpp", "nvkv_device.hpp", "nvkv_quantize.hip"):
+    for name in ("nvkv_decode.hip", "nvkv_encode.hpp", "nvkv_device.hpp", "nvkv_quantize.hip", "nvkv_tiles.hpp"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
