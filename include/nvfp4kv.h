@@ -200,6 +200,30 @@ NVKV_API nvkv_status nvkv_decode_append_attention_nvfp4(const nvkv_layer *layer,
                                         void *workspace, size_t workspace_bytes,
                                         int32_t split_tokens, void *stream);
 
+/*
+ * Causal multi-query attention over the packed cache: the last Tq positions of each sequence
+ * attend to the cached keys up to and including their own position ([cache post] opening
+ * paragraph: models are scored teacher-forced over full windows while attention reads the
+ * quantised post-RoPE cache; the same call serves a prefill chunk whose keys and values were
+ * appended with nvkv_quantize_append_kv just before).
+ *   q:          bf16 [B][Tq][Hq][128], post-RoPE, untransformed (the library applies q*s and
+ *               the 1/128-normalised Hadamard as layer->k_flags select, as in decode).
+ *   seq_lens:   int32 [B], device; n_b = tokens in the cache INCLUDING the Tq query positions,
+ *               clamped to min(max_seq_len, max_pages_per_seq * page_size).  Query i of
+ *               sequence b sits at position p = n_b - Tq + i and attends to tokens [0, p];
+ *               rows with p < 0 (a sequence shorter than Tq) are zero.
+ *   page_table: as for decode.  Hq must be 4 * Hkv.
+ *   out:        fp32 [B][Tq][Hq][128] = softmax(sm_scale * q' . k_hat, causal) v_hat.
+ *   No workspace: the split of a tile's keys over its workgroup is merged in LDS.
+ *   Tq = 0 returns NVKV_OK without a launch.  Errors as for decode (NVKV_ERR_NULL,
+ *   NVKV_ERR_SHAPE, NVKV_ERR_UNSUPPORTED for Hq != 4 Hkv, NVKV_ERR_HIP for a failed launch).
+ */
+NVKV_API nvkv_status nvkv_prefill_attention_nvfp4(const nvkv_layer *layer,
+                                        const uint16_t *q, int32_t B, int32_t Tq, int32_t Hq,
+                                        const int32_t *page_table, int32_t max_pages_per_seq,
+                                        const int32_t *seq_lens, int32_t max_seq_len,
+                                        float sm_scale, float *out, void *stream);
+
 /* Bytes of one cache array of one layer: fmt NVKV_FMT_*, part NVKV_PART_*; 0 if invalid
  * (including a BF16 scales array, which does not exist). */
 NVKV_API size_t nvkv_cache_array_bytes(int32_t fmt, int32_t part, int32_t num_pages, int32_t Hkv,

@@ -22,7 +22,7 @@ HEAD_DIM = 128
 
 EXPORTED = ["nvkv_calibrate_key_smoothing", "nvkv_quantize_append_kv", "nvkv_decode_workspace_bytes",
             "nvkv_decode_attention_nvfp4", "nvkv_decode_append_attention_nvfp4", "nvkv_cache_array_bytes", "nvkv_cache_bytes_per_token",
-            "nvkv_status_string", "nvkv_last_error"]
+            "nvkv_status_string", "nvkv_last_error", "nvkv_prefill_attention_nvfp4"]
 
 
 class NvkvError(RuntimeError):
@@ -71,6 +71,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.nvkv_decode_append_attention_nvfp4.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, i32, i32, vp, i32, vp, i32,
                                                        f32, vp, vp, sz, i32, vp]
     lib.nvkv_decode_append_attention_nvfp4.restype = ctypes.c_int
+    lib.nvkv_prefill_attention_nvfp4.argtypes = [ctypes.POINTER(Layer), vp, i32, i32, i32, vp, i32, vp, i32, f32,
+                                                 vp, vp]
+    lib.nvkv_prefill_attention_nvfp4.restype = ctypes.c_int
     lib.nvkv_cache_array_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.nvkv_cache_array_bytes.restype = sz
     lib.nvkv_cache_bytes_per_token.argtypes = [i32, i32, i32, i32]
@@ -138,6 +141,14 @@ def decode_append_attention_nvfp4(layer: Layer, q, k_new, v_new, B: int, Hq: int
                                                      max_seq_len, sm_scale, _ptr(out), _ptr(workspace),
                                                      workspace_bytes, split_tokens, _stream(stream)),
            "nvkv_decode_append_attention_nvfp4")
+
+
+def prefill_attention_nvfp4(layer: Layer, q, B: int, Tq: int, Hq: int, page_table, max_pages_per_seq: int,
+                            seq_lens, max_seq_len: int, sm_scale: float, out, stream=None) -> None:
+    _check(load().nvkv_prefill_attention_nvfp4(ctypes.byref(layer), _ptr(q), B, Tq, Hq, _ptr(page_table),
+                                               max_pages_per_seq, _ptr(seq_lens), max_seq_len, sm_scale, _ptr(out),
+                                               _stream(stream)),
+           "nvkv_prefill_attention_nvfp4")
 
 
 def cache_array_bytes(fmt: int, part: int, num_pages: int, Hkv: int, page_size: int) -> int:

@@ -5,7 +5,8 @@
 The quantise/calibrate translation unit is compiled with -ffp-contract=off (its fp32 key
 transform is part of the bit-exact encoding); the decode unit with -fno-honor-nans (its
 scores are finite or -inf and every code and scale decodes finite, so max operations need
-no NaN quieting); all HIP code is compiled without packed fp32 instructions.
+no NaN quieting), and so is the prefill-attention unit; all HIP code is compiled without
+packed fp32 instructions.
 """
 from __future__ import annotations
 
@@ -26,6 +27,7 @@ SOURCES = {
     "nvkv_capi.hip": [],
     "nvkv_quantize.hip": ["-ffp-contract=off"],
     "nvkv_decode.hip": ["-fno-honor-nans"],
+    "nvkv_prefill.hip": ["-fno-honor-nans"],
 }
 
 

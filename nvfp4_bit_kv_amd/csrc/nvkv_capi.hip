@@ -179,4 +179,26 @@ nvkv_status nvkv_decode_append_attention_nvfp4(const nvkv_layer* layer, const ui
                        sm_scale, out, workspace, workspace_bytes, split_tokens, stream);
 }
 
+nvkv_status nvkv_prefill_attention_nvfp4(const nvkv_layer* layer, const uint16_t* q, int32_t B, int32_t Tq,
+                                         int32_t Hq, const int32_t* page_table, int32_t max_pages_per_seq,
+                                         const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, float* out,
+                                         void* stream) {
+  const nvkv_status st = check_layer(layer);
+  if (st != NVKV_OK) return st;
+  if (B < 1 || B > kMaxGridYZ) return fail(NVKV_ERR_SHAPE, "B must be in [1, 65535]");
+  if (Tq < 0) return fail(NVKV_ERR_SHAPE, "Tq must be >= 0");
+  if (Tq == 0) return NVKV_OK;
+  if (!q || !page_table || !seq_lens || !out) return fail(NVKV_ERR_NULL, "input/output pointer is NULL");
+  if (Hq < 1 || Hq % layer->num_kv_heads != 0) return fail(NVKV_ERR_SHAPE, "Hq must be a multiple of Hkv");
+  if (Hq != 4 * layer->num_kv_heads) return fail(NVKV_ERR_UNSUPPORTED, "only 4 query heads per KV head");
+  if (max_pages_per_seq < 1 || max_seq_len < 0) return fail(NVKV_ERR_SHAPE, "max_pages_per_seq >= 1, max_seq_len >= 0");
+  if (!std::isfinite(sm_scale)) return fail(NVKV_ERR_SHAPE, "sm_scale must be finite");
+  if (static_cast<int64_t>(B) * Tq * Hq * NVKV_HEAD_DIM > INT64_C(1) << 40)
+    return fail(NVKV_ERR_SHAPE, "B * Tq * Hq too large");
+  (void)hipGetLastError();
+  return hip_status(nvkv::launch_prefill_attention(*layer, q, B, Tq, Hq, page_table, max_pages_per_seq, seq_lens,
+                                                   max_seq_len, sm_scale, out, static_cast<hipStream_t>(stream)),
+                    "prefill attention launch");
+}
+
 }  // extern "C"

@@ -508,61 +508,13 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
 
   // ---------------- query prologue: wavefront w < 4 prepares query head 4h + w ----------------
   if (!empty && q_wave) {
-    float x0 = bf16_to_f32(qw & 0xFFFFu), x1 = bf16_to_f32(qw >> 16);
-    float scale = a.sm_scale * kLog2e;
-    if (!KBF16) {
-      x0 *= sv.x;
-      x1 *= sv.y;
-      if (a.k_flags & NVKV_K_HADAMARD) {
-        const float u0 = x0 + x1, u1 = x0 - x1;
-        x0 = u0;
-        x1 = u1;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const float p0 = __shfl_xor(x0, d, 64), p1 = __shfl_xor(x1, d, 64);
-          const bool up = (lane & d) != 0;
-          x0 = up ? p0 - x0 : x0 + p0;
-          x1 = up ? p1 - x1 : x1 + p1;
-        }
-        scale *= (1.0f / 128.0f);
-      }
-      scale *= gk;
-    }
-    x0 *= scale;
-    x1 *= scale;
-    float m = fmaxf(fabsf(x0), fabsf(x1));
-    m = fmaxf(m, dpp_xor1(m));
-    m = fmaxf(m, dpp_xor2(m));
-    m = fmaxf(m, dpp_row_ror4(m));
-    m = fmaxf(m, dpp_row_ror8(m));
-    m = rows_max(m);
-    int e = 0;
-    if (m > 0.0f) frexpf(m, &e);
-    const int p2 = KBF16 ? 0 : 14 - e;           // max |x| * 2^p2 in [2^13, 2^14)
-    x0 = ldexpf(x0, p2);
-    x1 = ldexpf(x1, p2);
     uint32_t w0, w1, w2;
-    if constexpr (!KBF16) {
-      const _Float16 h0 = static_cast<_Float16>(x0), h1 = static_cast<_Float16>(x1);
-      const _Float16 l0 = static_cast<_Float16>(x0 - static_cast<float>(h0));
-      const _Float16 l1 = static_cast<_Float16>(x1 - static_cast<float>(h1));
-      w0 = __builtin_bit_cast(uint16_t, h0) | (uint32_t(__builtin_bit_cast(uint16_t, h1)) << 16);
-      w1 = __builtin_bit_cast(uint16_t, l0) | (uint32_t(__builtin_bit_cast(uint16_t, l1)) << 16);
-      w2 = 0u;
-    } else {
-      const uint32_t a0 = f32_to_bf16_rne(x0), a1 = f32_to_bf16_rne(x1);
-      const float r0 = x0 - bf16_to_f32(a0), r1 = x1 - bf16_to_f32(a1);
-      const uint32_t b0 = f32_to_bf16_rne(r0), b1 = f32_to_bf16_rne(r1);
-      const uint32_t c0 = f32_to_bf16_rne(r0 - bf16_to_f32(b0)), c1 = f32_to_bf16_rne(r1 - bf16_to_f32(b1));
-      w0 = a0 | (a1 << 16);
-      w1 = b0 | (b1 << 16);
-      w2 = c0 | (c1 << 16);
-    }
+    const float descale = query_terms<KBF16>(qw, sv, a.k_flags, a.sm_scale, gk, lane, w0, w1, w2);
     reinterpret_cast<uint32_t*>(q_lds[wave][0])[lane] = w0;
     reinterpret_cast<uint32_t*>(q_lds[wave][1])[lane] = w1;
     reinterpret_cast<uint32_t*>(q_lds[wave][2])[lane] = w2;
     reinterpret_cast<uint32_t*>(q_lds[wave][3])[lane] = 0u;
-    if (lane == 0) q_descale[wave] = ldexpf(1.0f, -p2);
+    if (lane == 0) q_descale[wave] = descale;
   }
   __syncthreads();
 

@@ -37,4 +37,9 @@ hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, const uint16_t*
                          const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, float* out, void* workspace,
                          const DecodePlan& plan, hipStream_t stream);
 
+// Causal attention of the last Tq positions of each sequence over the cache (no workspace).
+hipError_t launch_prefill_attention(const nvkv_layer& L, const uint16_t* q, int32_t B, int32_t Tq, int32_t Hq,
+                                    const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                    int32_t max_seq_len, float sm_scale, float* out, hipStream_t stream);
+
 }  // namespace nvkv

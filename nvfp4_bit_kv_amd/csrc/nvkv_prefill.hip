@@ -1,0 +1,443 @@
+// Causal multi-query attention over the packed NVFP4 cache (gfx950, MFMA): the attention of
+// a block of Tq query positions per sequence, each position seeing the cached keys up to and
+// including its own.  This is the teacher-forced evaluation of [cache post] (opening
+// paragraph: the model is scored over full windows while attention reads the quantised
+// post-RoPE cache), and the attention of a prefill chunk whose keys were just appended.
+//
+// [cache post] = rstation.ai post "NVFP4 attention cache on W4A4 Qwen3-8B: static key
+// smoothing is near-lossless, key rotations hurt"; [QServe rec] = inference-research record
+// "QServe SmoothAttention (4-bit KV cache ...)" (the smoothing factor rides on the query).
+//
+// Work decomposition: one workgroup of 4 wavefronts per (8 query positions, KV head,
+// sequence).  Its 32 rows are (position, query head) of the KV head's group of 4; a row
+// block of 16 rows holds 4 positions x 4 heads.  The keys 0..p_last of the tile are cut into
+// 32-token iterations dealt round-robin to the wavefronts (split-K inside the workgroup), and
+// the four partial softmax states are merged in LDS at the end, so no workspace is needed.
+// Per iteration a wavefront does, for both row blocks:
+//   QK  S[16 rows x 32 tok] = Q'[16 x 128] Khat^T: the query is held as exact operand terms
+//       (two fp16 terms with a power-of-two row prescale, or three bf16 terms for BF16 keys)
+//       and each term is one MFMA 16x16x32 per 32 dims, accumulating into the same S.
+//       Khat = code * sigma is exact in fp16 (the decode kernel's dequantisation).
+//   online softmax per row in the base-2 domain with the lazily moved running max of the
+//       decode kernel (threshold 8, so p <= 256); the causal mask drops keys beyond a row's
+//       position.
+//   PV  O[16 x 128] += P[16 x 32] Vhat[32 x 128]: P split into hi + lo fp16 terms by
+//       round-toward-zero packed converts, one MFMA per term and 16-dim tile; P goes from
+//       the score layout to the A-operand layout through the wavefront's LDS rows.
+// The cache loads, page lookups and V operand construction are those of the decode kernel
+// (nvkv_tiles.hpp); tiles are processed longest first (the last query positions).
+#include "nvkv_device.hpp"
+#include "nvkv_internal.hpp"
+#include "nvkv_tiles.hpp"
+
+namespace nvkv {
+
+struct PrefillArgs {
+  const uint8_t* k_codes;     // NVFP4 key codes, or BF16 key rows
+  const uint8_t* k_scales;
+  const uint8_t* v_codes;
+  const uint8_t* v_scales;
+  const float* smooth;        // s [Hkv][128]
+  const float* gscale;        // {g_K, g_V}
+  const uint16_t* q;          // bf16 [B][Tq][Hq][128]
+  const int32_t* page_table;  // [B][max_pages_per_seq]
+  const int32_t* seq_lens;    // [B]: cached tokens, the Tq query positions included
+  float* out;                 // fp32 [B][Tq][Hq][128]
+  int32_t hkv, hq, page_size, num_pages, max_pages_per_seq, seq_cap;
+  int32_t page_shift;         // log2(page_size) when it is a power of two, else -1
+  int32_t tq;                 // query positions per sequence
+  uint32_t k_flags;
+  float sm_scale;
+};
+
+constexpr int kPfPos = 8;                   // query positions per workgroup
+constexpr int kPfRows = 4 * kPfPos;         // rows (position, head)
+constexpr int kPfWaves = 4;
+constexpr int kPfStride = 20;               // P row stride in dwords (32 fp16 + padding)
+constexpr int kPfPWords = 16 * kPfStride;   // one P term of one row block
+
+// LDS: the query terms and per-wavefront P buffers live while the iterations run; the
+// partial states of the four wavefronts reuse the same bytes for the final merge.
+template <int NT>
+struct PfLoopSmem {
+  uint16_t q[kPfRows][NT][kHeadDim];          // query terms of row R, dims in natural order
+  float desc[kPfRows];                        // score descale of row R
+  uint32_t p[kPfWaves][2][2][kPfPWords];      // [wave][row block][term hi/lo]
+};
+struct PfMergeSmem {
+  float m[kPfWaves][kPfRows];
+  float l[kPfWaves][kPfRows];
+  float o[kPfWaves][kPfRows][kHeadDim];
+};
+template <int NT>
+union PfSmem {
+  PfLoopSmem<NT> loop;
+  PfMergeSmem merge;
+};
+
+// Per-wavefront softmax state for the two row blocks: lane (c, g) holds rows 4g..4g+3 of
+// each block (one query position, its four heads) in the score layout.
+struct PfState {
+  float m_ref[2][4];
+  float l_acc[2][4];
+  floatx4 acc[2][8];          // O rows 4g+j, column c <-> dim 8c + v
+};
+
+// V operands of PV instructions 2K (dims 8c + 2K, from ev) and 2K + 1 (from od).
+template <int K>
+__device__ __forceinline__ void pf_v_operands(const uint32_t (&ev)[4], const uint32_t (&od)[4], const half2v (&sig)[4],
+                                              u32x4& be, u32x4& bo) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    be[p] = as_u32(fp4_pair_x256<K>(ev[p]) * sig[p]);
+    bo[p] = as_u32(fp4_pair_x256<K>(od[p]) * sig[p]);
+  }
+}
+
+template <int K>
+__device__ __forceinline__ void pf_pv(const uint32_t (&ev)[4], const uint32_t (&od)[4], const half2v (&sig)[4],
+                                      const half8 (&ap)[2][2], PfState& st) {
+  u32x4 be, bo;
+  pf_v_operands<K>(ev, od, sig, be, bo);
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      st.acc[rb][2 * K] =
+          __builtin_amdgcn_mfma_f32_16x16x32_f16(ap[rb][t], __builtin_bit_cast(half8, be), st.acc[rb][2 * K], 0, 0, 0);
+      st.acc[rb][2 * K + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap[rb][t], __builtin_bit_cast(half8, bo),
+                                                                     st.acc[rb][2 * K + 1], 0, 0, 0);
+    }
+}
+
+// One 32-token iteration (tokens t0..t0+31) of a wavefront for its 32 rows.
+template <bool KBF16, int NT>
+__device__ __forceinline__ void pf_iter(const IterLoads<KBF16>& L, const HalfBase (&hbc)[2], int t0, int t_end,
+                                        const u32x4 (&qa)[2][NT][4], const float (&desc)[2][4], const int (&pos)[2],
+                                        const Lane& ln, uint32_t* p_w, PfState& st) {
+  const int c = ln.c, g = ln.g;
+  // ---- QK ----
+  floatx4 sacc[2][2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int eta = 0; eta < 2; ++eta) sacc[rb][eta] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int eta = 0; eta < 2; ++eta) {
+    half2v s0, s1;
+    if constexpr (!KBF16) {
+      s0 = scale_pair_same(L.k.ks[eta][0] >> ln.ks_shift);
+      s1 = scale_pair_same(L.k.ks[eta][1] >> ln.ks_shift);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if constexpr (!KBF16) {
+        const half8 bk = dequant_dword(L.k.kc[eta][u], u < 2 ? s0 : s1);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            sacc[rb][eta] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, qa[rb][t][u]), bk,
+                                                                   sacc[rb][eta], 0, 0, 0);
+      } else {
+        const bf16x8 bk = __builtin_bit_cast(bf16x8, L.k.kr[eta][u]);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            sacc[rb][eta] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[rb][t][u]), bk,
+                                                                    sacc[rb][eta], 0, 0, 0);
+      }
+    }
+  }
+  // ---- masked scores, lazy running max, p = 2^(s - m) ----
+  bool ok[2];
+#pragma unroll
+  for (int eta = 0; eta < 2; ++eta) ok[eta] = hbc[eta].ok && (t0 + 16 * eta + c < t_end);
+  float x[2][2][4];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int eta = 0; eta < 2; ++eta) {
+      const bool vis = ok[eta] && (t0 + 16 * eta + c <= pos[rb]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[rb][eta][j] = vis ? sacc[rb][eta][j] * desc[rb][j] : -INFINITY;
+    }
+  bool need_any = false;
+  float bmax[2][4];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bmax[rb][j] = row16_max(fmaxf(x[rb][0][j], x[rb][1][j]));
+      need_any |= bmax[rb][j] > st.m_ref[rb][j] + kLazyMax;
+    }
+  if (__builtin_expect(__any(need_any), 0)) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // rows differ in their causal masks: a row that does not move (possibly still at
+        // -inf) keeps alpha = 1 rather than evaluating 2^(-inf + inf)
+        const bool need = bmax[rb][j] > st.m_ref[rb][j] + kLazyMax;
+        const float m_new = need ? bmax[rb][j] : st.m_ref[rb][j];
+        const float alpha = need ? exp2f(st.m_ref[rb][j] - m_new) : 1.0f;   // 0 on a row's first keys
+        st.m_ref[rb][j] = m_new;
+        st.l_acc[rb][j] *= alpha;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) st.acc[rb][v][j] *= alpha;
+      }
+  }
+  // p split into hi + lo fp16 terms (|p - hi - lo| < 2^-20 p), written as P rows
+  // (row 4g + j, token pair word c = tokens (c, 16 + c)) of the wavefront's buffers
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float neg_m = (st.m_ref[rb][j] == -INFINITY) ? 0.0f : -st.m_ref[rb][j];
+      const float p0 = __builtin_amdgcn_exp2f(x[rb][0][j] + neg_m);
+      const float p1 = __builtin_amdgcn_exp2f(x[rb][1][j] + neg_m);
+      st.l_acc[rb][j] += p0 + p1;
+      const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+      const half2v lo = __builtin_bit_cast(
+          half2v, __builtin_amdgcn_cvt_pkrtz(p0 - static_cast<float>(hi[0]), p1 - static_cast<float>(hi[1])));
+      p_w[(2 * rb + 0) * kPfPWords + (4 * g + j) * kPfStride + c] = as_u32(hi);
+      p_w[(2 * rb + 1) * kPfPWords + (4 * g + j) * kPfStride + c] = as_u32(lo);
+    }
+  // (LDS operations of one wavefront complete in issue order, and the compiler keeps the
+  // reads after the possibly aliasing writes.)
+  half8 ap[2][2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      ap[rb][t] = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(
+                                                p_w + (2 * rb + t) * kPfPWords + c * kPfStride + 4 * g));
+  // ---- PV: B operand column c <-> dim 8c + v, k = 8g + e <-> token 16 (e & 1) + 4g + (e >> 1) ----
+  const uint32_t w0 = L.vs[0] & 0x7F7F7F7Fu, w1 = L.vs[1] & 0x7F7F7F7Fu;
+  half2v sig[4];
+  uint32_t ev[4], od[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t sel = 0x0Cu | (uint32_t(p) << 8) | (0x0Cu << 16) | (uint32_t(4 + p) << 24);
+    sig[p] = as_half2(__builtin_amdgcn_perm(w1, w0, sel) >> 1);
+    ev[p] = nib_even(L.vd[2 * p], L.vd[2 * p + 1]);
+    od[p] = nib_odd(L.vd[2 * p], L.vd[2 * p + 1]);
+  }
+  pf_pv<0>(ev, od, sig, ap, st);
+  pf_pv<1>(ev, od, sig, ap, st);
+  pf_pv<2>(ev, od, sig, ap, st);
+  pf_pv<3>(ev, od, sig, ap, st);
+}
+
+template <bool KBF16>
+__global__ void __launch_bounds__(256) k_prefill_attn(PrefillArgs a) {
+  constexpr int NT = KBF16 ? 3 : 2;           // query operand terms
+  const int n_tiles = static_cast<int>(gridDim.x);
+  const int tile = n_tiles - 1 - static_cast<int>(blockIdx.x);   // latest positions first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  Lane ln;
+  ln.c = c;
+  ln.g = g;
+  ln.k_off = KBF16 ? static_cast<uint32_t>(c * kHeadDim * 2 + 64 * g) : static_cast<uint32_t>(c * 64 + 16 * g);
+  ln.ks_off = static_cast<uint32_t>((c >> 2) * 32 + 8 * g);
+  ln.ks_shift = static_cast<uint32_t>(8 * (c & 3));
+  ln.v_off = static_cast<uint32_t>(16 * (16 * g + c));
+  ln.vs_off = static_cast<uint32_t>(32 * g + 4 * (c >> 1));
+
+  __shared__ __attribute__((aligned(16))) PfSmem<NT> sm;
+
+  int n = a.seq_lens[b];
+  n = n < 0 ? 0 : (n > a.seq_cap ? a.seq_cap : n);
+  const int i0 = tile * kPfPos;                       // first query index of the tile
+  const int pos0 = n - a.tq + i0;                     // its position (may be negative)
+  const int t_end = min(pos0 + kPfPos, n);            // keys [0, t_end) are needed
+  const const_i32_ptr ptab = __builtin_bit_cast(const_i32_ptr, a.page_table) + static_cast<int64_t>(b) * a.max_pages_per_seq;
+
+  // ---- query prologue: wavefront w prepares rows 8w..8w+7 (row R = 4 * position + head) ----
+  {
+    float2 sv = make_float2(1.0f, 1.0f);
+    if (!KBF16 && (a.k_flags & NVKV_K_SMOOTH)) sv = reinterpret_cast<const float2*>(a.smooth + h * kHeadDim)[lane];
+    const float gk = KBF16 ? 1.0f : a.gscale[0];
+    uint32_t qw[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int R = 8 * wave + k;
+      const int i = i0 + (R >> 2);
+      qw[k] = 0u;
+      if (i < a.tq)
+        qw[k] = reinterpret_cast<const uint32_t*>(
+            a.q + ((static_cast<int64_t>(b) * a.tq + i) * a.hq + 4 * h + (R & 3)) * kHeadDim)[lane];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int R = 8 * wave + k;
+      uint32_t w[3];
+      const float descale = query_terms<KBF16>(qw[k], sv, a.k_flags, a.sm_scale, gk, lane, w[0], w[1], w[2]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) reinterpret_cast<uint32_t*>(sm.loop.q[R][t])[lane] = w[t];
+      if (lane == 0) sm.loop.desc[R] = descale;
+    }
+  }
+  __syncthreads();
+
+  PfState st;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      st.m_ref[rb][j] = -INFINITY;
+      st.l_acc[rb][j] = 0.0f;
+    }
+#pragma unroll
+    for (int v = 0; v < 8; ++v) st.acc[rb][v] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  if (t_end > 0) {
+    // A operands of QK: lane (c, g) = row c of the block; instruction u, item e <-> dim
+    // 32g + 8u + e (the dim order of the key codes a lane loads).
+    u32x4 qa[2][NT][4];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          qa[rb][t][u] = *reinterpret_cast<const u32x4*>(&sm.loop.q[16 * rb + c][t][32 * g + 8 * u]);
+    float desc[2][4];
+    int pos[2];                                       // position of the lane's score rows
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) desc[rb][j] = sm.loop.desc[16 * rb + 4 * g + j];
+      pos[rb] = pos0 + 4 * rb + g;
+    }
+    uint32_t* p_w = sm.loop.p[wave][0][0];
+
+    // iterations it = wave, wave + 4, ...; two register buffers, the next one in flight
+    const int n_it = (t_end + kIterTok - 1) / kIterTok;
+    IterLoads<KBF16> buf0, buf1;
+    HalfBase hb0[2], hb1[2];
+    int it = wave;
+    if (it < n_it) {
+      half_bases<KBF16>(a, load_pages(a, ptab, kIterTok * it, t_end), h, hb0);
+      issue_loads<KBF16>(hb0, ln, buf0);
+    }
+    if (it + kPfWaves < n_it) {
+      half_bases<KBF16>(a, load_pages(a, ptab, kIterTok * (it + kPfWaves), t_end), h, hb1);
+      issue_loads<KBF16>(hb1, ln, buf1);
+    }
+    for (;;) {
+      if (it >= n_it) break;
+      pf_iter<KBF16, NT>(buf0, hb0, kIterTok * it, t_end, qa, desc, pos, ln, p_w, st);
+      if (it + 2 * kPfWaves < n_it) {
+        half_bases<KBF16>(a, load_pages(a, ptab, kIterTok * (it + 2 * kPfWaves), t_end), h, hb0);
+        issue_loads<KBF16>(hb0, ln, buf0);
+      }
+      it += kPfWaves;
+      if (it >= n_it) break;
+      pf_iter<KBF16, NT>(buf1, hb1, kIterTok * it, t_end, qa, desc, pos, ln, p_w, st);
+      if (it + 2 * kPfWaves < n_it) {
+        half_bases<KBF16>(a, load_pages(a, ptab, kIterTok * (it + 2 * kPfWaves), t_end), h, hb1);
+        issue_loads<KBF16>(hb1, ln, buf1);
+      }
+      it += kPfWaves;
+    }
+  }
+  __syncthreads();     // every wavefront is done with the query terms and P buffers
+
+  // ---- wavefront partials -> LDS -> workgroup merge ----
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int R = 16 * rb + 4 * g + j;
+      const float l_tot = row16_sum(st.l_acc[rb][j]);
+      if (c == 0) {
+        sm.merge.m[wave][R] = st.m_ref[rb][j];
+        sm.merge.l[wave][R] = l_tot;
+      }
+      float4* dst = reinterpret_cast<float4*>(&sm.merge.o[wave][R][8 * c]);
+      dst[0] = make_float4(st.acc[rb][0][j], st.acc[rb][1][j], st.acc[rb][2][j], st.acc[rb][3][j]);
+      dst[1] = make_float4(st.acc[rb][4][j], st.acc[rb][5][j], st.acc[rb][6][j], st.acc[rb][7][j]);
+    }
+  __syncthreads();
+  {
+    // thread -> row R = tid / 8, dims 16 (tid % 8) .. + 15
+    const int R = tid >> 3, d0 = 16 * (tid & 7);
+    const int i = i0 + (R >> 2);
+    float mw[kPfWaves], lw[kPfWaves];
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kPfWaves; ++w) {
+      mw[w] = sm.merge.m[w][R];
+      lw[w] = sm.merge.l[w][R];
+      M = lw[w] > 0.0f ? fmaxf(M, mw[w]) : M;
+    }
+    float L = 0.0f;
+    float o[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kPfWaves; ++w) {
+      const float wt = lw[w] > 0.0f ? exp2f(mw[w] - M) : 0.0f;
+      L += wt * lw[w];
+      const float4* src = reinterpret_cast<const float4*>(&sm.merge.o[w][R][d0]);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 v = src[q4];
+        o[4 * q4 + 0] += wt * v.x;
+        o[4 * q4 + 1] += wt * v.y;
+        o[4 * q4 + 2] += wt * v.z;
+        o[4 * q4 + 3] += wt * v.w;
+      }
+    }
+    if (i < a.tq) {
+      const float f = L > 0.0f ? a.gscale[1] / L : 0.0f;
+      float4* dst = reinterpret_cast<float4*>(
+          a.out + ((static_cast<int64_t>(b) * a.tq + i) * a.hq + 4 * h + (R & 3)) * kHeadDim + d0);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        dst[q4] = make_float4(o[4 * q4] * f, o[4 * q4 + 1] * f, o[4 * q4 + 2] * f, o[4 * q4 + 3] * f);
+    }
+  }
+}
+
+hipError_t launch_prefill_attention(const nvkv_layer& L, const uint16_t* q, int32_t B, int32_t Tq, int32_t Hq,
+                                    const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                    int32_t max_seq_len, float sm_scale, float* out, hipStream_t stream) {
+  PrefillArgs a{};
+  a.k_codes = static_cast<const uint8_t*>(L.k_data);
+  a.k_scales = L.k_scales;
+  a.v_codes = static_cast<const uint8_t*>(L.v_data);
+  a.v_scales = L.v_scales;
+  a.smooth = L.k_smooth;
+  a.gscale = L.global_scale;
+  a.q = q;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.hkv = L.num_kv_heads;
+  a.hq = Hq;
+  a.page_size = L.page_size;
+  a.page_shift = (L.page_size & (L.page_size - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(L.page_size)) : -1;
+  a.num_pages = L.num_pages;
+  a.max_pages_per_seq = max_pages_per_seq;
+  const int64_t cap_pages = static_cast<int64_t>(max_pages_per_seq) * L.page_size;
+  a.seq_cap = static_cast<int32_t>(cap_pages < max_seq_len ? cap_pages : max_seq_len);
+  a.tq = Tq;
+  a.k_flags = L.k_flags;
+  a.sm_scale = sm_scale;
+  const dim3 grid((Tq + kPfPos - 1) / kPfPos, L.num_kv_heads, B);
+  const dim3 block(64 * kPfWaves);
+  if (L.k_fmt == NVKV_FMT_BF16)
+    hipLaunchKernelGGL((k_prefill_attn<true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_prefill_attn<false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace nvkv

@@ -11,6 +11,7 @@
 // num_pages, hkv, page_size and page_shift.
 #pragma once
 
+#include "../../include/nvfp4kv.h"
 #include "nvkv_device.hpp"
 
 namespace nvkv {
@@ -215,5 +216,68 @@ __device__ __forceinline__ void valid_tokens(const HalfBase (&hb)[2], int t0, in
   v[1] = hb[1].ok && (t0 + 16 + c < t_end);
 }
 
+
+// Query transform of one row (lane l holds dims 2l, 2l+1 as the bf16 pair qw): q' = q * s,
+// then H(q * s) / 128 when the keys are in the Hadamard basis ([QServe rec]: the smoothing
+// factor is folded into the query; [cache post] Hadamard-128 rows), times sm_scale * log2(e)
+// and the key tensor scale g_K.  BF16 keys take neither transform.  The row is then split
+// into exact operand terms: NVFP4 keys -- a power-of-two prescale 2^p2 puts max |q'| in
+// [2^13, 2^14) and two fp16 terms (hi, lo) keep ~22 bits; BF16 keys -- three bf16 terms.
+// w0..w2 receive the terms of the lane's two dims (w2 = 0 for fp16); returns the descale
+// 2^-p2 to apply to the scores.
+template <bool KBF16>
+__device__ __forceinline__ float query_terms(uint32_t qw, float2 sv, uint32_t k_flags, float sm_scale, float gk,
+                                           int lane, uint32_t& w0, uint32_t& w1, uint32_t& w2) {
+  float x0 = bf16_to_f32(qw & 0xFFFFu), x1 = bf16_to_f32(qw >> 16);
+  float scale = sm_scale * kLog2e;
+  if (!KBF16) {
+    x0 *= sv.x;
+    x1 *= sv.y;
+    if (k_flags & NVKV_K_HADAMARD) {
+      const float u0 = x0 + x1, u1 = x0 - x1;
+      x0 = u0;
+      x1 = u1;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float p0 = __shfl_xor(x0, d, 64), p1 = __shfl_xor(x1, d, 64);
+        const bool up = (lane & d) != 0;
+        x0 = up ? p0 - x0 : x0 + p0;
+        x1 = up ? p1 - x1 : x1 + p1;
+      }
+      scale *= (1.0f / 128.0f);
+    }
+    scale *= gk;
+  }
+  x0 *= scale;
+  x1 *= scale;
+  float m = fmaxf(fabsf(x0), fabsf(x1));
+  m = fmaxf(m, dpp_xor1(m));
+  m = fmaxf(m, dpp_xor2(m));
+  m = fmaxf(m, dpp_row_ror4(m));
+  m = fmaxf(m, dpp_row_ror8(m));
+  m = rows_max(m);
+  int e = 0;
+  if (m > 0.0f) frexpf(m, &e);
+  const int p2 = KBF16 ? 0 : 14 - e;           // max |x| * 2^p2 in [2^13, 2^14)
+  x0 = ldexpf(x0, p2);
+  x1 = ldexpf(x1, p2);
+  if constexpr (!KBF16) {
+    const _Float16 h0 = static_cast<_Float16>(x0), h1 = static_cast<_Float16>(x1);
+    const _Float16 l0 = static_cast<_Float16>(x0 - static_cast<float>(h0));
+    const _Float16 l1 = static_cast<_Float16>(x1 - static_cast<float>(h1));
+    w0 = __builtin_bit_cast(uint16_t, h0) | (uint32_t(__builtin_bit_cast(uint16_t, h1)) << 16);
+    w1 = __builtin_bit_cast(uint16_t, l0) | (uint32_t(__builtin_bit_cast(uint16_t, l1)) << 16);
+    w2 = 0u;
+  } else {
+    const uint32_t a0 = f32_to_bf16_rne(x0), a1 = f32_to_bf16_rne(x1);
+    const float r0 = x0 - bf16_to_f32(a0), r1 = x1 - bf16_to_f32(a1);
+    const uint32_t b0 = f32_to_bf16_rne(r0), b1 = f32_to_bf16_rne(r1);
+    const uint32_t c0 = f32_to_bf16_rne(r0 - bf16_to_f32(b0)), c1 = f32_to_bf16_rne(r1 - bf16_to_f32(b1));
+    w0 = a0 | (a1 << 16);
+    w1 = b0 | (b1 << 16);
+    w2 = c0 | (c1 << 16);
+  }
+  return ldexpf(1.0f, -p2);
+}
 
 }  // namespace nvkv

@@ -16,7 +16,8 @@ weights and datasets are not available):
     u/krylov_schur thread on rstation.ai reports 30-50x RMS norms for Qwen3-8B sink tokens).
   * V ~ N(0,1); queries ~ N(0,1).
 Seeds: seed = ((cfg*16 + role)*64 + layer)*64 + index, roles 0 K, 1 V, 2 query,
-3 channel structure, 10..13 calibration windows 0..3.
+3 channel structure, 4 query blocks (causal prefill attention), 10..13 calibration windows
+0..3.
 """
 from __future__ import annotations
 
@@ -24,6 +25,7 @@ import numpy as np
 
 HEAD_DIM = 128
 ROLE_K, ROLE_V, ROLE_Q, ROLE_CHAN = 0, 1, 2, 3
+ROLE_QBLK = 4
 ROLE_WIN0 = 10
 
 
@@ -96,6 +98,12 @@ def make_queries(cfg: int, layer: int, B: int, hq: int, d: int = HEAD_DIM) -> np
     return bf16_round(rng.standard_normal((B, hq, d)).astype(np.float32))
 
 
+def make_query_block(cfg: int, layer: int, B: int, Tq: int, hq: int, d: int = HEAD_DIM) -> np.ndarray:
+    """Queries of Tq consecutive positions per sequence, bf16 bits [B][Tq][Hq][D], N(0,1)."""
+    rng = np.random.Generator(np.random.PCG64(seed_of(cfg, ROLE_QBLK, layer)))
+    return bf16_round(rng.standard_normal((B, Tq, hq, d)).astype(np.float32))
+
+
 def make_calib_windows(kind: str, cfg: int, layer: int, W: int, Tw: int, hkv: int,
                        sink: bool = True):
     """W calibration windows of keys and values, bf16 bits [W][Tw][Hkv][D] each."""
@@ -163,3 +171,10 @@ def make_queries_device(cfg: int, layer: int, B: int, hq: int, d: int = HEAD_DIM
     gen = torch.Generator(device="cuda")
     gen.manual_seed(seed_of(cfg, ROLE_Q, layer))
     return torch.randn((B, hq, d), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+
+def make_query_block_device(cfg: int, layer: int, B: int, Tq: int, hq: int, d: int = HEAD_DIM):
+    torch = _torch()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed_of(cfg, ROLE_QBLK, layer))
+    return torch.randn((B, Tq, hq, d), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)

@@ -28,7 +28,7 @@ def clib():
 
 def test_every_declared_symbol_is_exported(clib):
     decl = _declared_symbols()
-    assert len(decl) == 9, decl
+    assert len(decl) == 10, decl
     assert sorted(decl) == sorted(nk.EXPORTED)
     for name in decl:
         assert hasattr(clib, name), name
@@ -131,6 +131,24 @@ def test_decode_append_argument_errors(clib):
     need = nk.decode_workspace_bytes(4, 32, 8, 4096, 32)
     assert call(msl=4096, sp=32, wsb=need - 1) == 4
     assert call(lay=_layer(k_fmt=7)) == 3
+
+
+def test_prefill_attention_argument_errors(clib):
+    """The causal prefill-attention entry point validates its arguments before any launch;
+    Tq = 0 is a no-op."""
+    L = _layer()
+    f = clib.nvkv_prefill_attention_nvfp4
+    ok = dict(q=0x10, B=4, Tq=64, Hq=32, pt=0x10, mp=4, sl=0x10, msl=64, sm=0.1, out=0x10)
+    def call(lay=L, **kw):
+        a = dict(ok, **kw)
+        return f(ctypes.byref(lay) if lay is not None else None, a["q"], a["B"], a["Tq"], a["Hq"], a["pt"], a["mp"],
+                 a["sl"], a["msl"], a["sm"], a["out"], None)
+    assert call(lay=None) == 1
+    assert call(q=None) == 1 and call(out=None) == 1 and call(pt=None) == 1 and call(sl=None) == 1
+    assert call(B=0) == 2 and call(B=70000) == 2 and call(Tq=-1) == 2 and call(Hq=12) == 2
+    assert call(Hq=16) == 3 and call(mp=0) == 2 and call(msl=-1) == 2 and call(sm=float("inf")) == 2
+    assert call(lay=_layer(k_fmt=7)) == 3 and call(lay=_layer(page_size=24)) == 2
+    assert call(Tq=0, q=None, out=None) == 0          # nothing to do, nothing launched
 
 
 def test_calibrate_argument_errors(clib):
