@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="step36",
                     help="step36 | step36-vonly | step36-hadamard | step36-had-smooth | long | prefill | "
-                         "prefill-hadamard")
+                         "prefill-hadamard | prefill-attn")
     ap.add_argument("--copies", type=int, default=0, help="rotating cache copies (0: workload default)")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -78,7 +78,10 @@ VARIANTS = {
     "long": dict(cfg="long", k_fmt=1, flags=1, copies=1, label="K+V NVFP4, K smoothed"),
     "prefill": dict(cfg="prefill", k_fmt=1, flags=1, copies=1, label="K smoothed"),
     "prefill-hadamard": dict(cfg="prefill", k_fmt=1, flags=3, copies=1, label="K smoothed + Hadamard-128"),
+    "prefill-attn": dict(cfg="prefill", k_fmt=1, flags=1, copies=1, label="K+V NVFP4, K smoothed",
+                         attention=True),
 }
+MFMA_F16_PEAK_TFLOPS = 2500.0
 
 
 def row_bytes(fmt):
@@ -404,6 +407,192 @@ class PrefillAppend:
                 f"{self.variant['label']}, K and V NVFP4")
 
 
+class PrefillAttention:
+    """Causal prefill attention: per layer, prefill_attention_nvfp4 of all B x T positions
+    over the layer's cache of the same T tokens (a full teacher-forced window)."""
+
+    metric = "NVFP4-KV causal prefill attention: achieved TFLOP/s (% of MFMA fp16 peak) and tokens/s"
+    kernel_label = ("k_prefill_attn (prefill_attention_nvfp4: causal attention of batch 16 x 8192 positions over "
+                    "the cache), per layer")
+    roofline_bound = "mfma"
+    protocol_runs = 3
+
+    def __init__(self, name):
+        import torch
+        import nvfp4_bit_kv_amd as nk
+        from synth import kv_inputs as S
+        self.torch, self.nk, self.S = torch, nk, S
+        v = VARIANTS[name]
+        c = S.CONFIGS[v["cfg"]]
+        self.name, self.variant, self.c = name, v, c
+        self.B, self.T, self.hkv, self.hq, self.L = c["B"], c["T"], c["hkv"], c["hq"], c["layers"]
+        self.flags = v["flags"]
+        self.copies = 1
+        B, T, hkv = self.B, self.T, self.hkv
+        self.pps = T // PAGE
+        self.num_pages = B * self.pps
+        rng = np.random.default_rng(2468)
+        self.table_np = rng.permutation(self.num_pages).reshape(B, self.pps).astype(np.int32)
+        self.table = torch.from_numpy(self.table_np).cuda()
+        t = np.arange(T)
+        slots = (self.table_np[:, t // PAGE] * PAGE + t % PAGE).astype(np.int32)
+        slots_dev = torch.from_numpy(np.ascontiguousarray(slots.reshape(-1))).cuda()
+        self.seq_lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+        self.caches, self.q = [], []
+        self.sample_b = (0, B - 1)
+        for l in range(self.L):
+            kw, vw = calib_windows_device(torch, S, c, l)
+            cache = nk.CacheLayer(self.num_pages, PAGE, hkv, k_flags=self.flags)
+            nk.calibrate_key_smoothing(kw, vw, 4, c["Tw"], hkv, True, self.flags, cache.smooth,
+                                       cache.inv_smooth, cache.gscale)
+            k = S.make_keys_device(c["kind"], c["cfg"], l, B, T, hkv)
+            vv = S.make_values_device(c["cfg"], l, B, T, hkv)
+            nk.quantize_append_kv(cache.struct(), k.reshape(B * T, hkv, 128), vv.reshape(B * T, hkv, 128),
+                                  slots_dev, B * T)
+            self.caches.append((cache, cache.struct()))
+            self.q.append(S.make_query_block_device(c["cfg"], l, B, T, self.hq))
+            if l == 0:
+                self.layer0 = ({b: (k[b].cpu(), vv[b].cpu()) for b in self.sample_b}, kw.cpu(), vw.cpu())
+            del k, vv
+            if (l + 1) % 6 == 0:
+                print(f"[bench] built layer {l + 1}/{self.L}", file=sys.stderr, flush=True)
+        self.out = torch.empty((B, T, self.hq, 128), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        self._oracle = None
+
+    def step(self, cp):
+        for l in range(self.L):
+            self.nk.prefill_attention_nvfp4(self.caches[l][1], self.q[l], self.B, self.T, self.hq, self.table,
+                                            self.pps, self.seq_lens, self.T, SM_SCALE, self.out)
+
+    def snapshot(self):
+        return self.out.clone()
+
+    def launch_flops(self):
+        """Algorithmic flops of one call: QK and PV, 2 flops per multiply-add, over the causal
+        (position, key) pairs: 4 * 128 * Hq * B * T (T + 1) / 2.  The exact-operand term splits
+        (two fp16 query terms, two P terms) double the MFMA work actually issued; they are not
+        counted."""
+        return 4 * 128 * self.hq * self.B * self.T * (self.T + 1) // 2
+
+    def step_flops(self):
+        return self.L * self.launch_flops()
+
+    def launch_bytes(self):
+        """Cache bytes one call must read at least once (144 B per (token, KV head)) plus the
+        queries in and the outputs out."""
+        return self.B * self.T * (self.hkv * 144 + self.hq * 128 * (2 + 4))
+
+    def step_bytes(self):
+        return self.L * self.launch_bytes()
+
+    def tokens_per_step(self):
+        return self.B * self.T
+
+    def launch_times(self, reps):
+        """Average duration of one call: a HIP graph of the calls of all layers replayed
+        between HIP events on the launch stream, divided by the layer count."""
+        torch = self.torch
+        g = capture(torch, lambda: self.step(0))
+        g.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for r in range(reps):
+            ev[r][0].record(stream)
+            g.replay()
+            ev[r][1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3 / self.L
+
+    def _oracle_inputs(self):
+        """Oracle calibration and dequantised cache of layer 0 for the sampled sequences, from
+        the same bf16 inputs as the GPU path."""
+        from oracle import nvfp4_oracle as O
+        if self._oracle is None:
+            torch = self.torch
+            keep, kw, vw = self.layer0
+            s, r, g = O.calibrate(f32_of(torch, kw), f32_of(torch, vw), True, self.flags)
+            seqs = {}
+            for b in self.sample_b:
+                kf, vf = f32_of(torch, keep[b][0]), f32_of(torch, keep[b][1])
+                kc, ks = O.quantize_rows(O.key_transform(kf, r[None], self.flags), g[0])
+                vc, vs = O.quantize_rows(vf, g[1])
+                seqs[b] = (O.dequantize(kc, ks, g[0]), O.dequantize(vc, vs, g[1]))
+            self._oracle = (O, s, g, seqs)
+        return self._oracle
+
+    def _oracle_rows(self, b, positions):
+        """Oracle causal attention of the given positions of sequence b (layer 0), each as the
+        last position of a block of one."""
+        O, s, g, seqs = self._oracle_inputs()
+        khat, vhat = seqs[b]
+        qf = f32_of(self.torch, self.q[0][b, positions].cpu()).astype(np.float64)     # [P][Hq][128]
+        qp = O.query_transform(qf, np.repeat(s, self.hq // self.hkv, 0)[None], self.flags)
+        return np.stack([O.causal_attention(qp[j][None, None], [khat], [vhat], [int(p) + 1], SM_SCALE)[0, 0]
+                         for j, p in enumerate(positions)])
+
+    def check(self):
+        """Sampled rows of layer 0 (first and last sequence; first, tile-boundary, last and
+        random positions, all 32 heads) against the oracle: max |err| <= 1e-3 max|V_hat| and
+        per-row relative L2 <= 1e-4."""
+        torch = self.torch
+        self.nk.prefill_attention_nvfp4(self.caches[0][1], self.q[0], self.B, self.T, self.hq, self.table,
+                                        self.pps, self.seq_lens, self.T, SM_SCALE, self.out)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(77)
+        positions = sorted(set([0, 1, 7, 8, 511, self.T // 2, self.T - 1] + list(rng.integers(0, self.T, 5))))
+        O, s, g, seqs = self._oracle_inputs()
+        ok, max_abs, max_rel = True, 0.0, 0.0
+        for b in self.sample_b:
+            got = self.out[b, positions].cpu().numpy().astype(np.float64)
+            ref = self._oracle_rows(b, positions)
+            vmax = float(np.abs(seqs[b][1]).max())
+            err = float(np.abs(got - ref).max())
+            rel = float((np.linalg.norm(got - ref, axis=-1) / np.maximum(np.linalg.norm(ref, axis=-1), 1e-30)).max())
+            max_abs, max_rel = max(max_abs, err / vmax), max(max_rel, rel)
+            ok &= bool(np.all(np.isfinite(got)) and err <= 1e-3 * vmax and rel <= 1e-4)
+        return dict(ok=ok, sequences=list(self.sample_b), positions=[int(p) for p in positions],
+                    max_abs_err_over_vmax=max_abs, max_rel_l2=max_rel,
+                    tol="max|err| <= 1e-3 max|Vhat|, rel L2 <= 1e-4")
+
+    def cpu_baseline(self, budget_s=12.0):
+        """The oracle (query transform and fp64 causal attention over the dequantised cache of
+        layer 0, calibration and dequantisation done once beforehand, untimed) on random query
+        positions of sequence 0, all 32 heads, one BLAS thread, for a bounded time; positions
+        per second scaled by the mean causal length, divided by the layer count."""
+        from threadpoolctl import threadpool_limits
+        rng = np.random.default_rng(5)
+        with threadpool_limits(limits=1):
+            self._oracle_inputs()
+            done, pairs = 0, 0
+            t0 = time.perf_counter()
+            while True:
+                pos = int(rng.integers(0, self.T))
+                self._oracle_rows(0, [pos])
+                done += 1
+                pairs += pos + 1
+                el = time.perf_counter() - t0
+                if el >= budget_s:
+                    break
+        # full-window tokens per second: the oracle's (position, key) pair rate over the
+        # window's T (T + 1) / 2 pairs per sequence
+        pair_rate = pairs / el
+        tok_s = pair_rate / (self.T * (self.T + 1) / 2) * self.T
+        return dict(value=round(tok_s / self.L, 4), unit="tokens/s", cores=1, kind="oracle",
+                    sample=f"{done} random query positions of sequence 0, layer 0, all {self.hq} heads "
+                           f"({pairs} causal (position, key) pairs) in {el:.1f} s on 1 core of "
+                           f"{len(os.sched_getaffinity(0))}; scaled to full {self.T}-position windows and "
+                           f"divided by {self.L} layers",
+                    oracle_tflops=round(pair_rate * 4 * 128 * self.hq / 1e12, 6))
+
+    def describe(self):
+        c = self.c
+        return (f"{self.name}: causal prefill attention of batch {c['B']} x {c['T']} positions (full window) "
+                f"over each of {c['layers']} layers' 16-token paged NVFP4 cache (shuffled pages), "
+                f"{c['hkv']} KV heads x 128, {c['hq']} query heads, {self.variant['label']}")
+
+
 def capture(torch, fn):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -609,7 +798,9 @@ def main():
     if args.profile_pass:
         args.steps, args.warmup, args.no_cpu_baseline = min(args.steps, 20), min(args.warmup, 5), True
     print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
-    if VARIANTS[args.workload]["cfg"] == "prefill":
+    if VARIANTS[args.workload].get("attention"):
+        wl = PrefillAttention(args.workload)
+    elif VARIANTS[args.workload]["cfg"] == "prefill":
         wl = PrefillAppend(args.workload)
     else:
         wl = DecodeStep(args.workload, args.copies, args.split_tokens, fused=not args.separate)
@@ -629,9 +820,10 @@ def main():
     protocol = None
     if not args.profile_pass:
         reps = []
+        runs = getattr(wl, "protocol_runs", 30)
         for _ in range(3):
-            reps.append(time_graphs(torch, graphs, 30, 3) / 30)
-        protocol = {"repetitions": 3, "runs": 30, "median_ms": round(float(np.median(reps)), 5),
+            reps.append(time_graphs(torch, graphs, runs, min(3, runs)) / runs)
+        protocol = {"repetitions": 3, "runs": runs, "median_ms": round(float(np.median(reps)), 5),
                     "min_ms": round(float(np.min(reps)), 5), "max_ms": round(float(np.max(reps)), 5)}
     # the same decode step as two calls per layer, for comparison
     separate_ms = None
@@ -643,7 +835,8 @@ def main():
     print("[bench] per-launch timing of the dominant kernel", file=sys.stderr, flush=True)
     durs = wl.launch_times(max(3, min(30, args.steps // 5)))
     avg_launch = float(np.mean(durs))
-    achieved = wl.launch_bytes() / avg_launch / 1e9
+    mfma = getattr(wl, "roofline_bound", "hbm") == "mfma"
+    achieved = wl.launch_flops() / avg_launch / 1e12 if mfma else wl.launch_bytes() / avg_launch / 1e9
 
     if args.sweep_splits and isinstance(wl, DecodeStep):
         sweep_splits(torch, wl, [int(x) for x in args.sweep_splits.split(",")])
@@ -655,11 +848,12 @@ def main():
 
     step_s = ms * 1e-3
     gbs = wl.step_bytes() / step_s / 1e9
+    tflops = wl.step_flops() / step_s / 1e12 if mfma else None
     c = wl.c
     line = {
         "metric": wl.metric,
-        "value": round(gbs, 2),
-        "unit": "GB/s",
+        "value": round(tflops, 2) if mfma else round(gbs, 2),
+        "unit": "TFLOP/s" if mfma else "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
@@ -675,11 +869,14 @@ def main():
         "tokens_per_s": round(wl.tokens_per_step() / step_s, 2),
         "hbm_frac_of_step": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": {
-            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_per_launch(wl),
+            "bound": "mfma" if mfma else "hbm", "achieved": round(achieved, 2),
+            "peak": MFMA_F16_PEAK_TFLOPS if mfma else HBM_PEAK_GBS, "unit": "TFLOP/s" if mfma else "GB/s",
+            "frac": round(achieved / (MFMA_F16_PEAK_TFLOPS if mfma else HBM_PEAK_GBS), 4),
+            "traffic": traffic_per_launch(wl),
             "kernel": wl.kernel_label,
             "bytes_per_launch": wl.launch_bytes(), "avg_launch_us": round(avg_launch * 1e6, 3),
             "min_launch_us": round(float(np.min(durs)) * 1e6, 3),
+            **({"flops_per_launch": wl.launch_flops()} if mfma else {}),
         },
         "cpu_baseline": base,
         "graph_replay_matches_eager": replay_ok,
