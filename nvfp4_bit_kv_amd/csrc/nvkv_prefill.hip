@@ -12,7 +12,8 @@
 // sequence).  Its 32 rows are (position, query head) of the KV head's group of 4; a row
 // block of 16 rows holds 4 positions x 4 heads.  The keys 0..p_last of the tile are cut into
 // 32-token iterations dealt round-robin to the wavefronts (split-K inside the workgroup), and
-// the four partial softmax states are merged in LDS at the end, so no workspace is needed.
+// the four partial softmax states are merged pairwise in LDS at the end, so no workspace is
+// needed.
 // Per iteration a wavefront does, for both row blocks:
 //   QK  S[16 rows x 32 tok] = Q'[16 x 128] Khat^T: the query is held as exact operand terms
 //       (two fp16 terms with a power-of-two row prescale, or three bf16 terms for BF16 keys)
@@ -60,28 +61,66 @@ constexpr int kPfPWords = 16 * kPfStride;   // one P term of one row block
 // partial states of the four wavefronts reuse the same bytes for the final merge.
 template <int NT>
 struct PfLoopSmem {
-  uint16_t q[kPfRows][NT][kHeadDim];          // query terms of row R, dims in natural order
+  // query terms in QK A-operand order: block (row block, term, instruction u) holds, for
+  // lane L = c + 16 g, dims 32g + 8u .. 32g + 8u + 7 of row c (16 B), so a wavefront reads
+  // each operand as one contiguous 1 KB
+  u32x4 qa[2][NT][4][64];
   float desc[kPfRows];                        // score descale of row R
   uint32_t p[kPfWaves][2][2][kPfPWords];      // [wave][row block][term hi/lo]
 };
-struct PfMergeSmem {
-  float m[kPfWaves][kPfRows];
-  float l[kPfWaves][kPfRows];
-  float o[kPfWaves][kPfRows][kHeadDim];
+// Per-wavefront softmax state for the two row blocks: lane (c, g) holds rows 4g..4g+3 of
+// each block (one query position, its four heads) in the score layout.
+struct PfState {
+  float m_ref[2][4];
+  float thr[2][4];            // raw-score threshold of the lazy max: (m_ref + 8) / descale
+  float l_acc[2][4];
+  floatx4 acc[2][8];          // O rows 4g+j, column c <-> dim 8c + v
 };
+
+// Pairwise merge of the wavefront states in two rounds through two slots, each holding one
+// wavefront's state in its own register layout (per lane: m, l of rows 4g+j of both row
+// blocks, and the 16 accumulator quads).
+struct PfMergeSmem {
+  float m[2][2][4][64];
+  float l[2][2][4][64];
+  floatx4 o[2][2][8][64];
+};
+// Fold the state held in merge slot k into this wavefront's state (same lane layout).
+__device__ __forceinline__ void pf_merge_from(const PfMergeSmem& ms, int k, int lane, PfState& st) {
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float m1 = st.m_ref[rb][j], m2 = ms.m[k][rb][j][lane];
+      const float M = fmaxf(m1, m2);
+      const float a1 = m1 == -INFINITY ? 0.0f : exp2f(m1 - M);
+      const float a2 = m2 == -INFINITY ? 0.0f : exp2f(m2 - M);
+      st.m_ref[rb][j] = M;
+      st.l_acc[rb][j] = st.l_acc[rb][j] * a1 + ms.l[k][rb][j][lane] * a2;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) st.acc[rb][v][j] = st.acc[rb][v][j] * a1 + ms.o[k][rb][v][lane][j] * a2;
+    }
+}
+
+__device__ __forceinline__ void pf_merge_to(PfMergeSmem& ms, int k, int lane, const PfState& st) {
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ms.m[k][rb][j][lane] = st.m_ref[rb][j];
+      ms.l[k][rb][j][lane] = st.l_acc[rb][j];
+    }
+#pragma unroll
+    for (int v = 0; v < 8; ++v) ms.o[k][rb][v][lane] = st.acc[rb][v];
+  }
+}
+
 template <int NT>
 union PfSmem {
   PfLoopSmem<NT> loop;
   PfMergeSmem merge;
 };
 
-// Per-wavefront softmax state for the two row blocks: lane (c, g) holds rows 4g..4g+3 of
-// each block (one query position, its four heads) in the score layout.
-struct PfState {
-  float m_ref[2][4];
-  float l_acc[2][4];
-  floatx4 acc[2][8];          // O rows 4g+j, column c <-> dim 8c + v
-};
 
 // V operands of PV instructions 2K (dims 8c + 2K, from ev) and 2K + 1 (from od).
 template <int K>
@@ -113,7 +152,7 @@ __device__ __forceinline__ void pf_pv(const uint32_t (&ev)[4], const uint32_t (&
 // One 32-token iteration (tokens t0..t0+31) of a wavefront for its 32 rows.
 template <bool KBF16, int NT>
 __device__ __forceinline__ void pf_iter(const IterLoads<KBF16>& L, const HalfBase (&hbc)[2], int t0, int t_end,
-                                        const u32x4 (&qa)[2][NT][4], const float (&desc)[2][4], const int (&pos)[2],
+                                        const u32x4 (&qa)[2][NT][4][64], const float (&desc)[2][4], const int (&pos)[2],
                                         const Lane& ln, uint32_t* p_w, PfState& st) {
   const int c = ln.c, g = ln.g;
   // ---- QK ----
@@ -137,7 +176,7 @@ __device__ __forceinline__ void pf_iter(const IterLoads<KBF16>& L, const HalfBas
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
           for (int t = 0; t < NT; ++t)
-            sacc[rb][eta] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, qa[rb][t][u]), bk,
+            sacc[rb][eta] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, qa[rb][t][u][ln.c + 16 * ln.g]), bk,
                                                                    sacc[rb][eta], 0, 0, 0);
       } else {
         const bf16x8 bk = __builtin_bit_cast(bf16x8, L.k.kr[eta][u]);
@@ -145,33 +184,29 @@ __device__ __forceinline__ void pf_iter(const IterLoads<KBF16>& L, const HalfBas
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
           for (int t = 0; t < NT; ++t)
-            sacc[rb][eta] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[rb][t][u]), bk,
+            sacc[rb][eta] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[rb][t][u][ln.c + 16 * ln.g]), bk,
                                                                     sacc[rb][eta], 0, 0, 0);
       }
     }
   }
-  // ---- masked scores, lazy running max, p = 2^(s - m) ----
-  bool ok[2];
-#pragma unroll
-  for (int eta = 0; eta < 2; ++eta) ok[eta] = hbc[eta].ok && (t0 + 16 * eta + c < t_end);
+  // ---- scores (masked to -inf where needed) and the lazy running max.  The row descale
+  // (a power of two) is folded into the exponent's FMA and into each row's raw threshold, so
+  // the common case needs no cross-lane reduction: only when some raw score passes its row's
+  // threshold is the row max taken and the reference moved. ----
   float x[2][2][4];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int eta = 0; eta < 2; ++eta) {
-      const bool vis = ok[eta] && (t0 + 16 * eta + c <= pos[rb]);
+      const bool vis = hbc[eta].ok && (t0 + 16 * eta + c < t_end) && (t0 + 16 * eta + c <= pos[rb]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[rb][eta][j] = vis ? sacc[rb][eta][j] * desc[rb][j] : -INFINITY;
+      for (int j = 0; j < 4; ++j) x[rb][eta][j] = vis ? sacc[rb][eta][j] : -INFINITY;
     }
   bool need_any = false;
-  float bmax[2][4];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bmax[rb][j] = row16_max(fmaxf(x[rb][0][j], x[rb][1][j]));
-      need_any |= bmax[rb][j] > st.m_ref[rb][j] + kLazyMax;
-    }
+    for (int j = 0; j < 4; ++j) need_any |= (x[rb][0][j] > st.thr[rb][j]) | (x[rb][1][j] > st.thr[rb][j]);
   if (__builtin_expect(__any(need_any), 0)) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
@@ -179,10 +214,12 @@ __device__ __forceinline__ void pf_iter(const IterLoads<KBF16>& L, const HalfBas
       for (int j = 0; j < 4; ++j) {
         // rows differ in their causal masks: a row that does not move (possibly still at
         // -inf) keeps alpha = 1 rather than evaluating 2^(-inf + inf)
-        const bool need = bmax[rb][j] > st.m_ref[rb][j] + kLazyMax;
-        const float m_new = need ? bmax[rb][j] : st.m_ref[rb][j];
+        const float bmax = row16_max(fmaxf(x[rb][0][j], x[rb][1][j])) * desc[rb][j];
+        const bool need = bmax > st.m_ref[rb][j] + kLazyMax;
+        const float m_new = need ? bmax : st.m_ref[rb][j];
         const float alpha = need ? exp2f(st.m_ref[rb][j] - m_new) : 1.0f;   // 0 on a row's first keys
         st.m_ref[rb][j] = m_new;
+        st.thr[rb][j] = (m_new + kLazyMax) / desc[rb][j];
         st.l_acc[rb][j] *= alpha;
 #pragma unroll
         for (int v = 0; v < 8; ++v) st.acc[rb][v][j] *= alpha;
@@ -195,8 +232,8 @@ __device__ __forceinline__ void pf_iter(const IterLoads<KBF16>& L, const HalfBas
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float neg_m = (st.m_ref[rb][j] == -INFINITY) ? 0.0f : -st.m_ref[rb][j];
-      const float p0 = __builtin_amdgcn_exp2f(x[rb][0][j] + neg_m);
-      const float p1 = __builtin_amdgcn_exp2f(x[rb][1][j] + neg_m);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[rb][0][j], desc[rb][j], neg_m));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[rb][1][j], desc[rb][j], neg_m));
       st.l_acc[rb][j] += p0 + p1;
       const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0, p1));
       const half2v lo = __builtin_bit_cast(
@@ -230,8 +267,10 @@ __device__ __forceinline__ void pf_iter(const IterLoads<KBF16>& L, const HalfBas
   pf_pv<3>(ev, od, sig, ap, st);
 }
 
+// Two workgroups per CU, so two wavefronts per SIMD: registers are capped at 256 (launch
+// bounds), which the single load buffer fits without spills.
 template <bool KBF16>
-__global__ void __launch_bounds__(256) k_prefill_attn(PrefillArgs a) {
+__global__ void __launch_bounds__(256, 2) k_prefill_attn(PrefillArgs a) {
   constexpr int NT = KBF16 ? 3 : 2;           // query operand terms
   const int n_tiles = static_cast<int>(gridDim.x);
   const int tile = n_tiles - 1 - static_cast<int>(blockIdx.x);   // latest positions first
@@ -278,7 +317,11 @@ __global__ void __launch_bounds__(256) k_prefill_attn(PrefillArgs a) {
       uint32_t w[3];
       const float descale = query_terms<KBF16>(qw[k], sv, a.k_flags, a.sm_scale, gk, lane, w[0], w[1], w[2]);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) reinterpret_cast<uint32_t*>(sm.loop.q[R][t])[lane] = w[t];
+      for (int t = 0; t < NT; ++t) {
+        const int d = 2 * lane;                                  // dims d, d + 1
+        const int gg = d >> 5, uu = (d & 31) >> 3, ww = (d & 7) >> 1;
+        reinterpret_cast<uint32_t*>(&sm.loop.qa[R >> 4][t][uu][(R & 15) + 16 * gg])[ww] = w[t];
+      }
       if (lane == 0) sm.loop.desc[R] = descale;
     }
   }
@@ -290,6 +333,7 @@ __global__ void __launch_bounds__(256) k_prefill_attn(PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       st.m_ref[rb][j] = -INFINITY;
+      st.thr[rb][j] = -INFINITY;
       st.l_acc[rb][j] = 0.0f;
     }
 #pragma unroll
@@ -297,16 +341,8 @@ __global__ void __launch_bounds__(256) k_prefill_attn(PrefillArgs a) {
   }
 
   if (t_end > 0) {
-    // A operands of QK: lane (c, g) = row c of the block; instruction u, item e <-> dim
-    // 32g + 8u + e (the dim order of the key codes a lane loads).
-    u32x4 qa[2][NT][4];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          qa[rb][t][u] = *reinterpret_cast<const u32x4*>(&sm.loop.q[16 * rb + c][t][32 * g + 8 * u]);
+    // A operands of QK come from LDS at each use (sm.loop.qa): in registers they would take
+    // 64-96 of the 256
     float desc[2][4];
     int pos[2];                                       // position of the lane's score rows
 #pragma unroll
@@ -319,91 +355,53 @@ __global__ void __launch_bounds__(256) k_prefill_attn(PrefillArgs a) {
 
     // iterations it = wave, wave + 4, ...; two register buffers, the next one in flight
     const int n_it = (t_end + kIterTok - 1) / kIterTok;
-    IterLoads<KBF16> buf0, buf1;
-    HalfBase hb0[2], hb1[2];
+    // One register buffer: the next iteration's loads are issued as soon as this one's
+    // operands are consumed.  Two buffers would push the kernel past 256 registers (one
+    // wavefront per SIMD instead of two) and cost 1.6x (measured).
+    IterLoads<KBF16> buf;
+    HalfBase hb[2];
     int it = wave;
     if (it < n_it) {
-      half_bases<KBF16>(a, load_pages(a, ptab, kIterTok * it, t_end), h, hb0);
-      issue_loads<KBF16>(hb0, ln, buf0);
+      half_bases<KBF16>(a, load_pages(a, ptab, kIterTok * it, t_end), h, hb);
+      issue_loads<KBF16>(hb, ln, buf);
     }
-    if (it + kPfWaves < n_it) {
-      half_bases<KBF16>(a, load_pages(a, ptab, kIterTok * (it + kPfWaves), t_end), h, hb1);
-      issue_loads<KBF16>(hb1, ln, buf1);
-    }
-    for (;;) {
-      if (it >= n_it) break;
-      pf_iter<KBF16, NT>(buf0, hb0, kIterTok * it, t_end, qa, desc, pos, ln, p_w, st);
-      if (it + 2 * kPfWaves < n_it) {
-        half_bases<KBF16>(a, load_pages(a, ptab, kIterTok * (it + 2 * kPfWaves), t_end), h, hb0);
-        issue_loads<KBF16>(hb0, ln, buf0);
+    for (; it < n_it; it += kPfWaves) {
+      // (a separate unmasked instance for the iterations below the diagonal spills registers
+      // and runs 4x slower: measured)
+      pf_iter<KBF16, NT>(buf, hb, kIterTok * it, t_end, sm.loop.qa, desc, pos, ln, p_w, st);
+      if (it + kPfWaves < n_it) {
+        half_bases<KBF16>(a, load_pages(a, ptab, kIterTok * (it + kPfWaves), t_end), h, hb);
+        issue_loads<KBF16>(hb, ln, buf);
       }
-      it += kPfWaves;
-      if (it >= n_it) break;
-      pf_iter<KBF16, NT>(buf1, hb1, kIterTok * it, t_end, qa, desc, pos, ln, p_w, st);
-      if (it + 2 * kPfWaves < n_it) {
-        half_bases<KBF16>(a, load_pages(a, ptab, kIterTok * (it + 2 * kPfWaves), t_end), h, hb1);
-        issue_loads<KBF16>(hb1, ln, buf1);
-      }
-      it += kPfWaves;
     }
   }
   __syncthreads();     // every wavefront is done with the query terms and P buffers
 
-  // ---- wavefront partials -> LDS -> workgroup merge ----
+  // ---- workgroup merge: waves 2, 3 -> 0, 1; then 1 -> 0, which writes the output ----
+  if (wave >= 2) pf_merge_to(sm.merge, wave - 2, lane, st);
+  __syncthreads();
+  if (wave < 2) pf_merge_from(sm.merge, wave, lane, st);
+  __syncthreads();
+  if (wave == 1) pf_merge_to(sm.merge, 0, lane, st);
+  __syncthreads();
+  if (wave != 0) return;
+  pf_merge_from(sm.merge, 0, lane, st);
+  const float gv = a.gscale[1];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int R = 16 * rb + 4 * g + j;
-      const float l_tot = row16_sum(st.l_acc[rb][j]);
-      if (c == 0) {
-        sm.merge.m[wave][R] = st.m_ref[rb][j];
-        sm.merge.l[wave][R] = l_tot;
-      }
-      float4* dst = reinterpret_cast<float4*>(&sm.merge.o[wave][R][8 * c]);
-      dst[0] = make_float4(st.acc[rb][0][j], st.acc[rb][1][j], st.acc[rb][2][j], st.acc[rb][3][j]);
-      dst[1] = make_float4(st.acc[rb][4][j], st.acc[rb][5][j], st.acc[rb][6][j], st.acc[rb][7][j]);
-    }
-  __syncthreads();
-  {
-    // thread -> row R = tid / 8, dims 16 (tid % 8) .. + 15
-    const int R = tid >> 3, d0 = 16 * (tid & 7);
-    const int i = i0 + (R >> 2);
-    float mw[kPfWaves], lw[kPfWaves];
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kPfWaves; ++w) {
-      mw[w] = sm.merge.m[w][R];
-      lw[w] = sm.merge.l[w][R];
-      M = lw[w] > 0.0f ? fmaxf(M, mw[w]) : M;
-    }
-    float L = 0.0f;
-    float o[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[e] = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kPfWaves; ++w) {
-      const float wt = lw[w] > 0.0f ? exp2f(mw[w] - M) : 0.0f;
-      L += wt * lw[w];
-      const float4* src = reinterpret_cast<const float4*>(&sm.merge.o[w][R][d0]);
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 v = src[q4];
-        o[4 * q4 + 0] += wt * v.x;
-        o[4 * q4 + 1] += wt * v.y;
-        o[4 * q4 + 2] += wt * v.z;
-        o[4 * q4 + 3] += wt * v.w;
+      const float L = row16_sum(st.l_acc[rb][j]);
+      const int R = 16 * rb + 4 * g + j;                  // row (position 4rb + g, head j)
+      const int i = i0 + (R >> 2);
+      if (i < a.tq) {
+        const float f = L > 0.0f ? gv / L : 0.0f;
+        float4* dst = reinterpret_cast<float4*>(
+            a.out + ((static_cast<int64_t>(b) * a.tq + i) * a.hq + 4 * h + j) * kHeadDim + 8 * c);
+        dst[0] = make_float4(st.acc[rb][0][j] * f, st.acc[rb][1][j] * f, st.acc[rb][2][j] * f, st.acc[rb][3][j] * f);
+        dst[1] = make_float4(st.acc[rb][4][j] * f, st.acc[rb][5][j] * f, st.acc[rb][6][j] * f, st.acc[rb][7][j] * f);
       }
     }
-    if (i < a.tq) {
-      const float f = L > 0.0f ? a.gscale[1] / L : 0.0f;
-      float4* dst = reinterpret_cast<float4*>(
-          a.out + ((static_cast<int64_t>(b) * a.tq + i) * a.hq + 4 * h + (R & 3)) * kHeadDim + d0);
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        dst[q4] = make_float4(o[4 * q4] * f, o[4 * q4 + 1] * f, o[4 * q4 + 2] * f, o[4 * q4 + 3] * f);
-    }
-  }
 }
 
 hipError_t launch_prefill_attention(const nvkv_layer& L, const uint16_t* q, int32_t B, int32_t Tq, int32_t Hq,
