@@ -22,6 +22,8 @@ What the oracle computes (plain, slow, obviously correct; NumPy, fp64 unless not
   * quantize_rows       -- NVFP4 encoding: per 16-element block an E4M3 scale chosen so the
                            block absmax maps to 6, then E2M1 codes; both roundings are
                            round-to-nearest-even on the EXACT real quotient.
+  * quantize_rows_mse   -- the same encoding with each key block's E4M3 scale searched for
+                           the smallest exact squared error (optional key flag).
   * dequantize          -- code value * block scale * tensor scale, in fp64 (exact).
   * query_transform     -- q*s, optionally H(q*s)/128, in fp64.
   * attention           -- textbook softmax attention over the dequantised cache, fp64.
@@ -42,6 +44,9 @@ Readings taken where the pages leave a step open (each is repeated in the design
   - smoothing is applied before the Hadamard basis when both are selected.
   - a block of Tq queries of a sequence holding n cached tokens sits at positions
     n-Tq .. n-1 (the block's own keys are in the cache); position p sees keys 0..p.
+  - MSE-searched key scales: candidates are the absmax-to-6 code and every E4M3 code that
+    puts the block maximum between 7/4 and 7 times the scale; the exact squared error
+    decides, ties to the absmax-to-6 code, then to the smallest code.
 
 Every function here is pinned by a CPU test against something other than itself
 (brute-force nearest search with exact rationals, closed forms printed on the pages,
@@ -57,6 +62,7 @@ N_BLOCKS = HEAD_DIM // BLOCK
 
 FLAG_SMOOTH = 1
 FLAG_HADAMARD = 2
+FLAG_MSE_SCALE = 4
 
 # Largest E2M1 magnitude ([OSFP4] section 1: the FP4 constellation tops out at 6) and
 # largest finite E4M3FN value (bias 7, mantissa 0b110 at exponent 15).
@@ -200,19 +206,22 @@ def _tensor_scale(amax: float) -> np.float32:
 # flushes entries 24x below the block max; section 3: absmax-to-6 per 16-entry group at
 # inference; [cache post] opening paragraph: 16-blocks along head_dim, post-RoPE K/V).
 # ----------------------------------------------------------------------------------------
-def quantize_rows(y32: np.ndarray, g: float):
-    """Rows of 128 fp32 values -> (codes u8 [..., 64], scales u8 [..., 8]).
+def absmax_scale_codes(A: np.ndarray, g64) -> np.ndarray:
+    """E4M3 block-scale codes by the absmax-to-6 rule: RNE of the exact A/(6g), saturating
+    at 448 (code 126)."""
+    return rne_grid_index(A, 6.0 * g64, E4M3_GRID)
 
-    Block b = elements 16b..16b+15.  A_b = max |y|; scale code S_b = E4M3 RNE of the exact
-    A_b/(6g), saturating at 448; sigma_b = value(S_b).  Element magnitude code =
-    E2M1 RNE of the exact |y|/(sigma_b g) (0 when sigma_b = 0); nibble = 0 for magnitude 0,
-    else sign<<3 | magnitude.  Byte k = nibble(2k) | nibble(2k+1) << 4."""
+
+def encode_blocks(y32: np.ndarray, g: float, S: np.ndarray):
+    """Rows of 128 fp32 values and a chosen E4M3 scale code per block ([..., 8]) -> (codes u8
+    [..., 64], scales u8 [..., 8]).  Element magnitude code = E2M1 RNE of the exact
+    |y|/(sigma_b g) (0 when sigma_b = 0); nibble = 0 for magnitude 0, else sign<<3 |
+    magnitude.  Byte k = nibble(2k) | nibble(2k+1) << 4."""
     y32 = np.asarray(y32, dtype=np.float32)
     lead = y32.shape[:-1]
     y = y32.astype(np.float64).reshape(lead + (N_BLOCKS, BLOCK))
     g64 = np.float64(np.float32(g))
-    A = np.abs(y).max(axis=-1)
-    S = rne_grid_index(A, 6.0 * g64, E4M3_GRID)
+    S = np.asarray(S, dtype=np.int64)
     sigma = E4M3_GRID[S]
     unit = (sigma * g64)[..., None] * np.ones_like(y)
     mag = rne_grid_index(np.abs(y), unit, E2M1_MAG_GRID)
@@ -221,6 +230,105 @@ def quantize_rows(y32: np.ndarray, g: float):
     nib = np.where(mag == 0, 0, (sign << 3) | mag).reshape(lead + (HEAD_DIM,))
     codes = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
     return codes, S.astype(np.uint8)
+
+
+def quantize_rows(y32: np.ndarray, g: float):
+    """Rows of 128 fp32 values -> (codes u8 [..., 64], scales u8 [..., 8]).
+
+    Block b = elements 16b..16b+15.  A_b = max |y|; scale code S_b = E4M3 RNE of the exact
+    A_b/(6g), saturating at 448; sigma_b = value(S_b); the elements are then encoded by
+    encode_blocks."""
+    y32 = np.asarray(y32, dtype=np.float32)
+    lead = y32.shape[:-1]
+    y = y32.astype(np.float64).reshape(lead + (N_BLOCKS, BLOCK))
+    g64 = np.float64(np.float32(g))
+    return encode_blocks(y32, g, absmax_scale_codes(np.abs(y).max(axis=-1), g64))
+
+
+# ----------------------------------------------------------------------------------------
+# MSE-searched key block scales ([OSFP4] section 1: absmax-to-6 zeroes entries 24x below the
+# block maximum and other scale choices can lower the distortion; appendix H: unweighted
+# MSE-optimal E4M3 scales as a baseline; section 3 and appendix C: the deployed weight scales
+# come from a search over valid E4M3 scales under the deterministic FP4 error, one block at a
+# time for round-to-nearest; section 2.1 and appendix A (Lemma 1): the smoothed FP4 error is
+# flat, at its minimum, for values between 7/4 and 7 times the scale).
+#
+# Readings (the pages give no candidate set): the candidates of a block are its absmax-to-6
+# code and every E4M3 code c >= 1 whose scale puts the block maximum inside Lemma 1's
+# interval, 7/4 <= A/(g sigma_c) <= 7; the chosen code minimises the block's squared error
+# sum_j (y_j - y_hat_j)^2 over the candidates, with y_hat the round-to-nearest FP4
+# dequantisation; ties go to the absmax-to-6 code, then to the smallest code.  The tensor
+# scale g is the absmax-to-6 calibration's.
+# ----------------------------------------------------------------------------------------
+MSE_RATIO_LO = 1.75
+MSE_RATIO_HI = 7.0
+
+
+def mse_candidate_mask(A: np.ndarray, g64, c: int) -> np.ndarray:
+    """Blocks (by absmax A) for which E4M3 code c >= 1 lies in the search interval.  Both
+    products are exact in fp64 (24 + 4 + 3 significant bits)."""
+    u = E4M3_GRID[c] * g64
+    return (MSE_RATIO_LO * u <= A) & (A <= MSE_RATIO_HI * u)
+
+
+def mse_criterion(absy: np.ndarray, c: np.ndarray, g64) -> np.ndarray:
+    """J_c with  sum_j (y_j - y_hat_j)^2 = sum_j y_j^2 + g * J_c  for blocks |y| [n][16]
+    encoded with scale codes c [n]; the first sum does not depend on c, so the smallest J
+    is the smallest squared error.
+
+    With u = g sigma_c and FP4 magnitudes m_j (y_hat_j = m_j u, same sign as y_j):
+      sum (y - m u)^2 - sum y^2 = u^2 M2 - 2 u P = g * sigma_c (g sigma_c M2 - 2 P),
+      P = sum m_j |y_j|,  M2 = sum m_j^2.
+    Every step is exact in fp64, so J is the exact real number: m_j |y_j| != 0 needs
+    |y_j| >= u/4 while |y_j| <= A <= 9u for every block that has more than one candidate,
+    so the terms of P lie within 37 bits of each other; 4 M2 is an integer below 2^12;
+    g sigma_c M2 has at most 24 + 4 + 12 bits; their difference at most 42; times the 4-bit
+    sigma_c at most 46."""
+    c = np.asarray(c, dtype=np.int64)
+    sigma = E4M3_GRID[c]
+    unit = (sigma * g64)[:, None] * np.ones_like(absy)
+    mag = rne_grid_index(absy, unit, E2M1_MAG_GRID)
+    mag = np.where((sigma == 0.0)[:, None], 0, mag)
+    m = E2M1_MAG_GRID[mag]
+    P = (m * absy).sum(axis=-1)
+    M2 = (m * m).sum(axis=-1)
+    return sigma * (g64 * sigma * M2 - 2.0 * P)
+
+
+def mse_scale_codes(y32: np.ndarray, g: float) -> np.ndarray:
+    """E4M3 scale code per block ([..., 8]) minimising the block's squared FP4 error over
+    the candidates described above; the absmax-to-6 code is evaluated first and then the
+    other candidates in increasing code order, and a candidate replaces the best so far only
+    when its error is strictly smaller."""
+    y32 = np.asarray(y32, dtype=np.float32)
+    lead = y32.shape[:-1]
+    absy = np.abs(y32.astype(np.float64)).reshape(-1, BLOCK)
+    g64 = np.float64(np.float32(g))
+    A = absy.max(axis=-1)
+    s0 = absmax_scale_codes(A, g64)
+    best = s0.copy()
+    best_j = mse_criterion(absy, s0, g64)
+    for c in range(1, len(E4M3_GRID)):
+        idx = np.nonzero(mse_candidate_mask(A, g64, c) & (s0 != c))[0]
+        if idx.size == 0:
+            continue
+        j = mse_criterion(absy[idx], np.full(idx.size, c), g64)
+        win = j < best_j[idx]
+        best[idx[win]] = c
+        best_j[idx[win]] = j[win]
+    return best.reshape(lead + (N_BLOCKS,))
+
+
+def quantize_rows_mse(y32: np.ndarray, g: float):
+    """quantize_rows with each block's scale chosen by mse_scale_codes."""
+    return encode_blocks(y32, g, mse_scale_codes(y32, g))
+
+
+def quantize_keys(y32: np.ndarray, g: float, flags: int):
+    """Transformed key rows -> NVFP4 with the block-scale rule selected by flags."""
+    if flags & FLAG_MSE_SCALE:
+        return quantize_rows_mse(y32, g)
+    return quantize_rows(y32, g)
 
 
 def unpack_nibbles(codes: np.ndarray) -> np.ndarray:

@@ -10,6 +10,7 @@ import pytest
 
 from oracle import nvfp4_oracle as O
 from tests import test_oracle_codec as C
+from tests import test_oracle_mse_scale as M
 from tests import test_oracle_transforms as T
 
 
@@ -103,6 +104,40 @@ def _causal_wrong_offset(qp, k_hat, v_hat, seq_lens, sm_scale):
     return ORIG_CA(qp, k_hat, v_hat, [min(int(n), Tq) for n in seq_lens], sm_scale)
 
 
+def _mse_criterion_no_cross_factor(absy, c, g64):
+    """Drops the factor 2 of the cross term."""
+    c = np.asarray(c, dtype=np.int64)
+    sigma = O.E4M3_GRID[c]
+    mag = O.rne_grid_index(absy, (sigma * g64)[:, None] * np.ones_like(absy), O.E2M1_MAG_GRID)
+    m = O.E2M1_MAG_GRID[np.where((sigma == 0.0)[:, None], 0, mag)]
+    return sigma * (g64 * sigma * (m * m).sum(-1) - (m * absy).sum(-1))
+
+
+def _mse_search(y32, g, ties_to_last=False, with_absmax=True):
+    absy = np.abs(np.asarray(y32, np.float32).astype(np.float64)).reshape(-1, O.BLOCK)
+    g64 = np.float64(np.float32(g))
+    A = absy.max(-1)
+    s0 = O.absmax_scale_codes(A, g64)
+    best = s0.copy()
+    best_j = O.mse_criterion(absy, s0, g64) if with_absmax else np.full(A.shape, np.inf)
+    for c in range(1, len(O.E4M3_GRID)):
+        idx = np.nonzero(O.mse_candidate_mask(A, g64, c) & ((s0 != c) | (not with_absmax)))[0]
+        if idx.size:
+            j = O.mse_criterion(absy[idx], np.full(idx.size, c), g64)
+            win = (j <= best_j[idx]) if ties_to_last else (j < best_j[idx])
+            best[idx[win]] = c
+            best_j[idx[win]] = j[win]
+    return best.reshape(np.asarray(y32).shape[:-1] + (O.N_BLOCKS,))
+
+
+def _mse_ties_to_last(y32, g):
+    return _mse_search(y32, g, ties_to_last=True)
+
+
+def _mse_without_absmax_code(y32, g):
+    return _mse_search(y32, g, with_absmax=False)
+
+
 def _dequant_drop_g(codes, scales, g):
     return ORIG_DQ(codes, scales, 1.0)
 
@@ -127,6 +162,14 @@ CASES = [
     ("causal_attention", _causal_sees_one_less, [T.test_causal_attention_matches_torch_sdpa_fp64,
                                                  T.test_causal_attention_special_cases]),
     ("causal_attention", _causal_wrong_offset, [T.test_causal_attention_matches_torch_sdpa_fp64]),
+    ("mse_criterion", _mse_criterion_no_cross_factor, [M.test_mse_scale_vs_fraction_brute_force_random_blocks]),
+    ("MSE_RATIO_HI", 6.0, [M.test_mse_scale_vs_fraction_brute_force_random_blocks,
+                           M.test_mse_candidates_are_one_run_near_the_absmax_code]),
+    ("MSE_RATIO_LO", 1.5, [M.test_mse_scale_vs_fraction_brute_force_random_blocks,
+                           M.test_mse_candidates_are_one_run_near_the_absmax_code]),
+    ("mse_scale_codes", _mse_ties_to_last, [M.test_mse_worked_example_with_tie]),
+    ("mse_scale_codes", _mse_without_absmax_code, [M.test_mse_scale_vs_fraction_brute_force_random_blocks,
+                                                   M.test_mse_special_cases]),
 ]
 
 
