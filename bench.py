@@ -12,10 +12,13 @@ Default workload ("step36"): one decode step of a Qwen3-8B-shaped attention cach
   - steps replay HIP graphs over 4 rotating copies of the 36-layer cache (1.5 GB, beyond the
     256 MB last-level cache).
 Other workloads (run by hand with --workload):
-  - step36-vonly, step36-hadamard, step36-had-smooth: the same step with other cache formats;
+  - step36-vonly, step36-hadamard, step36-had-smooth, step36-mse: the same step with other
+    cache formats (step36-mse: MSE-searched key block scales);
   - long: decode step at batch 64 x 32768 context (87 GB packed cache);
-  - prefill, prefill-hadamard: quantize_append_kv of 16 x 8192 new tokens into each of 36
-    paged layers.
+  - prefill, prefill-hadamard, prefill-mse: quantize_append_kv of 16 x 8192 new tokens into
+    each of 36 paged layers;
+  - prefill-attn: causal prefill attention of the 16 x 8192 positions over each of the 36
+    layers' caches.
 
 Printed: one JSON line with
   - the step throughput (algorithmic bytes / step time) and tokens/s;
@@ -50,8 +53,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="step36",
-                    help="step36 | step36-vonly | step36-hadamard | step36-had-smooth | long | prefill | "
-                         "prefill-hadamard | prefill-attn")
+                    help="step36 | step36-vonly | step36-hadamard | step36-had-smooth | step36-mse | long | "
+                         "prefill | prefill-hadamard | prefill-mse | prefill-attn")
     ap.add_argument("--copies", type=int, default=0, help="rotating cache copies (0: workload default)")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -75,9 +78,12 @@ VARIANTS = {
     "step36-hadamard": dict(cfg="step36", k_fmt=1, flags=2, copies=4, label="K+V NVFP4, K Hadamard-128"),
     "step36-had-smooth": dict(cfg="step36", k_fmt=1, flags=3, copies=4,
                               label="K+V NVFP4, K smoothed + Hadamard-128"),
+    "step36-mse": dict(cfg="step36", k_fmt=1, flags=5, copies=4,
+                       label="K+V NVFP4, K smoothed, MSE-searched key scales"),
     "long": dict(cfg="long", k_fmt=1, flags=1, copies=1, label="K+V NVFP4, K smoothed"),
     "prefill": dict(cfg="prefill", k_fmt=1, flags=1, copies=1, label="K smoothed"),
     "prefill-hadamard": dict(cfg="prefill", k_fmt=1, flags=3, copies=1, label="K smoothed + Hadamard-128"),
+    "prefill-mse": dict(cfg="prefill", k_fmt=1, flags=5, copies=1, label="K smoothed, MSE-searched key scales"),
     "prefill-attn": dict(cfg="prefill", k_fmt=1, flags=1, copies=1, label="K+V NVFP4, K smoothed",
                          attention=True),
 }
@@ -344,7 +350,7 @@ class PrefillAppend:
         s, r, g = self._oracle_calib()
         k = f32_of(torch, self.k[0][rows].cpu())
         v = f32_of(torch, self.v[0][rows].cpu())
-        kc, ks = O.quantize_rows(O.key_transform(k, r[None], self.flags), g[0])
+        kc, ks = O.quantize_keys(O.key_transform(k, r[None], self.flags), g[0], self.flags)
         vc, vs = O.quantize_rows(v, g[1])
         return kc, ks, vc, vs
 
@@ -516,7 +522,7 @@ class PrefillAttention:
             seqs = {}
             for b in self.sample_b:
                 kf, vf = f32_of(torch, keep[b][0]), f32_of(torch, keep[b][1])
-                kc, ks = O.quantize_rows(O.key_transform(kf, r[None], self.flags), g[0])
+                kc, ks = O.quantize_keys(O.key_transform(kf, r[None], self.flags), g[0], self.flags)
                 vc, vs = O.quantize_rows(vf, g[1])
                 seqs[b] = (O.dequantize(kc, ks, g[0]), O.dequantize(vc, vs, g[1]))
             self._oracle = (O, s, g, seqs)
@@ -664,7 +670,7 @@ def _oracle_decode_inputs(wl):
             kf, vf = f32_of(torch, keep[b][0]), f32_of(torch, keep[b][1])
             kc = ks = None
             if wl.k_fmt == 1:
-                kc, ks = O.quantize_rows(O.key_transform(kf, r[None], wl.flags), g[0])
+                kc, ks = O.quantize_keys(O.key_transform(kf, r[None], wl.flags), g[0], wl.flags)
             vc, vs = O.quantize_rows(vf, g[1])
             seqs[b] = (kf, vf, (kc, ks, vc, vs))
         wl._oracle = (s, r, g, qf, seqs)
@@ -679,7 +685,7 @@ def _oracle_sequence(O, wl, s, r, g, qf, kf, vf, b, codes, append_last):
     kc, ks, vc, vs = codes
     if append_last:
         if wl.k_fmt == 1:
-            nkc, nks = O.quantize_rows(O.key_transform(kf[T - 1:], r[None], wl.flags), g[0])
+            nkc, nks = O.quantize_keys(O.key_transform(kf[T - 1:], r[None], wl.flags), g[0], wl.flags)
             kc, ks = np.concatenate([kc[:T - 1], nkc]), np.concatenate([ks[:T - 1], nks])
         nvc, nvs = O.quantize_rows(vf[T - 1:], g[1])
         vc, vs = np.concatenate([vc[:T - 1], nvc]), np.concatenate([vs[:T - 1], nvs])

@@ -79,7 +79,15 @@ typedef enum nvkv_status {
 } nvkv_status;
 
 enum { NVKV_FMT_BF16 = 0, NVKV_FMT_NVFP4 = 1 };
-enum { NVKV_K_SMOOTH = 1u, NVKV_K_HADAMARD = 2u };
+/* Key options.  NVKV_K_SMOOTH: static per-channel smoothing ([cache post] cache-config table;
+ * [QServe rec] SmoothAttention).  NVKV_K_HADAMARD: Hadamard-128 basis on head_dim ([cache post]
+ * table).  NVKV_K_MSE_SCALE: each key block's E4M3 scale is searched for the smallest squared
+ * FP4 error instead of mapping the block maximum to 6 ([OSFP4] sections 1 and 3, appendices C
+ * and H; candidates are the absmax-to-6 code and every code that puts the block maximum
+ * between 7/4 and 7 scale units, the flat interval of section 2.1 and appendix A; ties keep
+ * the absmax-to-6 code, then the smaller code).  It changes only how keys are encoded: the
+ * cache format, the calibration (g_K) and the attention calls are unchanged. */
+enum { NVKV_K_SMOOTH = 1u, NVKV_K_HADAMARD = 2u, NVKV_K_MSE_SCALE = 4u };
 enum { NVKV_PART_CODES = 0, NVKV_PART_SCALES = 1 };
 
 #define NVKV_HEAD_DIM 128
@@ -93,7 +101,7 @@ typedef struct nvkv_layer {
   int32_t num_pages;          /* pages in k_data / v_data                                  */
   int32_t k_fmt;              /* NVKV_FMT_NVFP4 or NVKV_FMT_BF16                           */
   int32_t v_fmt;              /* NVKV_FMT_NVFP4                                            */
-  uint32_t k_flags;           /* NVKV_K_SMOOTH | NVKV_K_HADAMARD; 0 for BF16 keys          */
+  uint32_t k_flags;           /* NVKV_K_SMOOTH | NVKV_K_HADAMARD | NVKV_K_MSE_SCALE; 0 for BF16 keys */
   int32_t reserved;           /* must be 0                                                 */
   void *k_data;               /* NVFP4 codes or BF16 rows, layout above                    */
   void *v_data;               /* NVFP4 codes                                               */
@@ -112,6 +120,7 @@ typedef struct nvkv_layer {
  *                g_out[0] = fl32(A_K / 2688), A_K = max |y| over every window, position
  *                (including 0) and head of the keys transformed as selected by k_flags
  *                (smoothing by r, then the Hadamard butterfly); 1 when A_K = 0.
+ *                NVKV_K_MSE_SCALE in k_flags is accepted and does not change the result.
  *   From v_win:  g_out[1] = fl32(A_V / 2688), A_V = max |v|; 1 when A_V = 0.
  *   s_out, r_out: fp32 [Hkv][128] (needed when k_win != NULL); g_out: fp32 [2].  Entries whose
  *   input is NULL are left untouched.  s_out and g_out double as the reduction buffers, so

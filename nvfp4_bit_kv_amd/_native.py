@@ -16,7 +16,7 @@ NVKV_OK = 0
 STATUS_NAMES = {0: "NVKV_OK", 1: "NVKV_ERR_NULL", 2: "NVKV_ERR_SHAPE", 3: "NVKV_ERR_UNSUPPORTED",
                 4: "NVKV_ERR_WORKSPACE", 5: "NVKV_ERR_HIP"}
 FMT_BF16, FMT_NVFP4 = 0, 1
-K_SMOOTH, K_HADAMARD = 1, 2
+K_SMOOTH, K_HADAMARD, K_MSE_SCALE = 1, 2, 4
 PART_CODES, PART_SCALES = 0, 1
 HEAD_DIM = 128
 

@@ -35,7 +35,8 @@ nvkv_status check_layer(const nvkv_layer* L) {
   if (static_cast<int64_t>(L->num_pages) * L->page_size > INT32_MAX) return fail(NVKV_ERR_SHAPE, "num_pages * page_size exceeds int32");
   if (L->k_fmt != NVKV_FMT_NVFP4 && L->k_fmt != NVKV_FMT_BF16) return fail(NVKV_ERR_UNSUPPORTED, "unknown k_fmt");
   if (L->v_fmt != NVKV_FMT_NVFP4) return fail(NVKV_ERR_UNSUPPORTED, "v_fmt must be NVKV_FMT_NVFP4");
-  if (L->k_flags & ~(NVKV_K_SMOOTH | NVKV_K_HADAMARD)) return fail(NVKV_ERR_UNSUPPORTED, "unknown k_flags bits");
+  if (L->k_flags & ~(NVKV_K_SMOOTH | NVKV_K_HADAMARD | NVKV_K_MSE_SCALE))
+    return fail(NVKV_ERR_UNSUPPORTED, "unknown k_flags bits");
   if (L->k_fmt == NVKV_FMT_BF16 && L->k_flags != 0) return fail(NVKV_ERR_UNSUPPORTED, "key transforms need NVFP4 keys");
   if (!L->k_data || !L->v_data || !L->v_scales || !L->global_scale) return fail(NVKV_ERR_NULL, "cache pointer is NULL");
   if (L->k_fmt == NVKV_FMT_NVFP4 && !L->k_scales) return fail(NVKV_ERR_NULL, "k_scales is NULL");
@@ -87,7 +88,8 @@ nvkv_status nvkv_calibrate_key_smoothing(const uint16_t* k_win, const uint16_t* 
   if (W < 1 || W > kMaxGridYZ || T < 1 || Hkv < 1) return fail(NVKV_ERR_SHAPE, "W, T, Hkv must be >= 1 (W <= 65535)");
   if (static_cast<int64_t>(W) * T * Hkv * NVKV_HEAD_DIM > INT32_MAX)
     return fail(NVKV_ERR_SHAPE, "calibration windows exceed 2^31 elements");
-  if (k_flags & ~(NVKV_K_SMOOTH | NVKV_K_HADAMARD)) return fail(NVKV_ERR_UNSUPPORTED, "unknown k_flags bits");
+  if (k_flags & ~(NVKV_K_SMOOTH | NVKV_K_HADAMARD | NVKV_K_MSE_SCALE))
+    return fail(NVKV_ERR_UNSUPPORTED, "unknown k_flags bits");
   (void)hipGetLastError();
   return hip_status(nvkv::launch_calibrate(k_win, v_win, W, T, Hkv, exclude_pos0, k_flags, s_out, r_out, g_out,
                                            static_cast<hipStream_t>(stream)),

@@ -254,6 +254,7 @@ struct NewTokenStage {
   uint8_t ks[32];                  // key scales: block b at byte 4b (token 0 of its quad)
   uint8_t vc[256];                 // value words: word w at byte 16w (quad-interleaved)
   uint8_t vs[32];                  // value scales: block b at byte 4b
+  float ky[kHeadDim];              // transformed key row (MSE-searched key scales only)
 };
 
 // Registers of the encoding wavefront: the whole wavefront encodes the new token, lane L
@@ -328,7 +329,15 @@ __device__ __forceinline__ void new_token_encode(const DecodeArgs& a, int h, int
   float A = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
   A = fmaxf(A, __shfl_xor(A, 1, 64));
   A = fmaxf(A, __shfl_xor(A, 2, 64));
-  const uint32_t S = e4m3_scale_code(A, R.g);
+  uint32_t S = e4m3_scale_code(A, R.g);
+  if (!KBF16 && (a.k_flags & NVKV_K_MSE_SCALE)) {
+    // MSE-searched key scales: the key row goes through LDS and the whole wavefront
+    // searches its 8 blocks (8 lanes per block); key lane L then takes block (L >> 2) & 7's code
+    if (!is_v) *reinterpret_cast<float4*>(&st.ky[4 * (lane & 31)]) = make_float4(y[0], y[1], y[2], y[3]);
+    const uint32_t s_row = mse_scale_code_row(st.ky, a.gscale[0], lane);
+    const uint32_t s_blk = static_cast<uint32_t>(__shfl(static_cast<int>(s_row), 8 * blk, 64));
+    if (!is_v) S = s_blk;
+  }
   const float sigma = e4m3_value(S);
   uint32_t bits = 0u;
   if (sigma > 0.0f) {

@@ -127,15 +127,11 @@ __device__ __forceinline__ uint32_t e2m1_nibble(float y, const E2m1Thresholds& t
   return m | (m ? sign : 0u);
 }
 
-// Encode one block: returns the scale code, writes the 16 nibbles packed in two dwords
-// (byte k = nibble 2k | nibble 2k+1 << 4).
-__device__ __forceinline__ uint32_t encode_block(const float (&y)[kBlock], float g, uint32_t& lo,
-                                                 uint32_t& hi) {
+// Encode one block with a given scale code S: writes the 16 nibbles packed in two dwords
+// (byte k = nibble 2k | nibble 2k+1 << 4); a zero scale gives an all-zero block.
+__device__ __forceinline__ void encode_block_with(const float (&y)[kBlock], float g, uint32_t S, uint32_t& lo,
+                                                  uint32_t& hi) {
 #pragma clang fp contract(off)
-  float A = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kBlock; ++i) A = fmaxf(A, fabsf(y[i]));
-  const uint32_t S = e4m3_scale_code(A, g);
   const float sigma = e4m3_value(S);
   // straight-line: a zero scale (underflowing block) masks the codes to 0 afterwards
   const E2m1Thresholds t(sigma);
@@ -146,6 +142,177 @@ __device__ __forceinline__ uint32_t encode_block(const float (&y)[kBlock], float
   for (int i = 0; i < 8; ++i) h |= e2m1_nibble(y[8 + i], t, g) << (4 * i);
   lo = sigma > 0.0f ? l : 0u;
   hi = sigma > 0.0f ? h : 0u;
+}
+
+__device__ __forceinline__ float block_absmax(const float (&y)[kBlock]) {
+  float A = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kBlock; ++i) A = fmaxf(A, fabsf(y[i]));
+  return A;
+}
+
+// Encode one block with the absmax-to-6 scale: returns the scale code.
+__device__ __forceinline__ uint32_t encode_block(const float (&y)[kBlock], float g, uint32_t& lo,
+                                                 uint32_t& hi) {
+  const uint32_t S = e4m3_scale_code(block_absmax(y), g);
+  encode_block_with(y, g, S, lo, hi);
+  return S;
+}
+
+// ---------------------------------------------------------------------------------------
+// MSE-searched key block scale ([OSFP4] section 1: other scales than absmax-to-6 can lower
+// the FP4 distortion; section 3 and appendix C: a deterministic search over valid E4M3
+// scales, block by block for round-to-nearest; appendix H: MSE-optimal E4M3 scales; section
+// 2.1 and appendix A, Lemma 1: the smoothed FP4 error is flat for values between 7/4 and 7
+// times the scale).  Candidates: the absmax-to-6 code S0 and every code c >= 1 with
+// 7/4 <= A/(g sigma_c) <= 7; they form one run of at most kMseMaxCand codes that starts no
+// lower than S0 - 2.  The smallest squared error wins; ties keep S0, then the smaller code.
+//
+// Ranking criterion: with u = g sigma, FP4 magnitudes m_j and y_hat_j = m_j u (sign of y_j),
+//   sum (y - y_hat)^2 = sum y^2 + g J,   J = sigma (u M2 - 2P),  P = sum m_j |y_j|,  M2 = sum m_j^2.
+// Each step is exact in fp64: a nonzero m_j needs |y_j| >= u/4 and every compared block has
+// |y_j| <= A <= 9u, so the products m_j |y_j| lie within 37 bits of each other and their sum
+// is exact in any order; u M2 has at most 28 + 12 bits, u M2 - 2P at most 42, times the 4-bit
+// sigma at most 46.  So J is the exact real number and the decision needs no rounding rule.
+// ---------------------------------------------------------------------------------------
+constexpr int kMseMaxCand = 17;
+
+// Twice the E2M1 magnitude of a 3-bit magnitude code: 0, 1, 2, 3, 4, 6, 8, 12.
+__device__ __forceinline__ uint32_t e2m1_twice_mag(uint32_t m) { return (0xC8643210u >> (4u * m)) & 15u; }
+
+// 2P and 4 M2 over N elements of a block (|y| given in fp64) for scale sigma > 0.
+template <int N>
+__device__ __forceinline__ void mse_partials(const float (&y)[N], const double (&ay)[N], float sigma, float g,
+                                             double& p2, uint32_t& m4) {
+  const E2m1Thresholds t(sigma);
+  p2 = 0.0;
+  m4 = 0u;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint32_t v2 = e2m1_twice_mag(e2m1_nibble(y[i], t, g) & 7u);
+    p2 = __builtin_fma(static_cast<double>(v2), ay[i], p2);   // exact (see above)
+    m4 += v2 * v2;
+  }
+}
+
+__device__ __forceinline__ double mse_criterion(float sigma, float g, double p2, uint32_t m4) {
+  const double u = static_cast<double>(g) * static_cast<double>(sigma);
+  return static_cast<double>(sigma) * (u * static_cast<double>(m4) * 0.25 - p2);
+}
+
+// Is code c's scale too small for the block maximum (A > 7 g sigma_c)?  Too large (A <
+// 7/4 g sigma_c)?  Both products are exact in fp32 (7 and 1.75 have 3 significant bits).
+__device__ __forceinline__ bool mse_below(float s, float A, float g) { return __builtin_fmaf(-7.0f * s, g, A) > 0.0f; }
+__device__ __forceinline__ bool mse_above(float s, float A, float g) { return __builtin_fmaf(-1.75f * s, g, A) < 0.0f; }
+
+// First code of the candidate run (or a code past it when the run is empty).
+__device__ __forceinline__ uint32_t mse_first_code(uint32_t S0, float A, float g) {
+  uint32_t c = S0 >= 3u ? S0 - 2u : 1u;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) c += (c < 126u && mse_below(e4m3_value(c), A, g)) ? 1u : 0u;
+  return c;
+}
+
+// Criterion J of code c for a block held by one lane (c >= 1).
+__device__ __forceinline__ double mse_code_criterion(const float (&y)[kBlock], const double (&ay)[kBlock], uint32_t c,
+                                                     float g) {
+  const float s = e4m3_value(c);
+  double p2;
+  uint32_t m4;
+  mse_partials<kBlock>(y, ay, s, g, p2, m4);
+  return mse_criterion(s, g, p2, m4);
+}
+
+// Search for a block held by one lane: S0 first, then the run in increasing code order, a
+// candidate replacing the best only when strictly better.
+__device__ __forceinline__ uint32_t mse_scale_code(const float (&y)[kBlock], float A, float g, uint32_t S0) {
+#pragma clang fp contract(off)
+  double ay[kBlock];
+#pragma unroll
+  for (int i = 0; i < kBlock; ++i) ay[i] = static_cast<double>(fabsf(y[i]));
+  uint32_t best = S0;
+  double best_j = S0 ? mse_code_criterion(y, ay, S0, g) : 0.0;
+  uint32_t c = mse_first_code(S0, A, g);
+  for (int k = 0; k < kMseMaxCand; ++k, ++c) {
+    if (c > 126u) break;
+    const float s = e4m3_value(c);
+    if (mse_above(s, A, g)) break;                 // this code and every larger one
+    if (mse_below(s, A, g) || c == S0) continue;
+    const double j = mse_code_criterion(y, ay, c, g);
+    if (j < best_j) {
+      best_j = j;
+      best = c;
+    }
+  }
+  return best;
+}
+
+// Search for the 8 blocks of a 128-element row staged in LDS (row[128]), by a whole
+// wavefront: lane L takes block L >> 3 and evaluates entries v = (L & 7) + 8t, t = 0, 1, 2,
+// of the block's candidate list (entry 0: S0; entry v >= 1: code first + v - 1 of the run,
+// at most kMseMaxCand entries); the block's eight lanes then keep the smallest (J, rank),
+// rank = -1 for S0 and the code otherwise, which is the order of the one-lane search.  The
+// call must be reached by all 64 lanes; every lane returns its block's code.
+__device__ __forceinline__ uint32_t mse_scale_code_row(const float* row, float g, int lane) {
+#pragma clang fp contract(off)
+  const int sub = lane & 7;
+  float y[kBlock];
+  const float4* src = reinterpret_cast<const float4*>(row + kBlock * (lane >> 3));
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = src[q];
+    y[4 * q] = v.x;
+    y[4 * q + 1] = v.y;
+    y[4 * q + 2] = v.z;
+    y[4 * q + 3] = v.w;
+  }
+  double ay[kBlock];
+#pragma unroll
+  for (int i = 0; i < kBlock; ++i) ay[i] = static_cast<double>(fabsf(y[i]));
+  const float A = block_absmax(y);
+  const uint32_t S0 = e4m3_scale_code(A, g);
+  const uint32_t first = mse_first_code(S0, A, g);
+  double best_j = __builtin_inf();
+  int best_rank = 0x7FFFFFFF;
+  uint32_t best = S0;
+  static_assert(3 * 8 >= kMseMaxCand + 1, "three entries per lane cover the list");
+  for (int t = 0; t < 3; ++t) {
+    const int v = sub + 8 * t;
+    const uint32_t c = v == 0 ? S0 : first + static_cast<uint32_t>(v - 1);
+    bool valid = v == 0;
+    if (v > 0 && v <= kMseMaxCand && c <= 126u) {
+      const float s = e4m3_value(c);
+      valid = !mse_below(s, A, g) && !mse_above(s, A, g);
+    }
+    if (!valid) continue;
+    const double j = c == 0u ? 0.0 : mse_code_criterion(y, ay, c, g);
+    const int rank = c == S0 ? -1 : static_cast<int>(c);
+    if (j < best_j || (j == best_j && rank < best_rank)) {
+      best_j = j;
+      best_rank = rank;
+      best = c;
+    }
+  }
+#pragma unroll
+  for (int d = 1; d < 8; d <<= 1) {
+    const double oj = __shfl_xor(best_j, d, 64);
+    const int orank = __shfl_xor(best_rank, d, 64);
+    const uint32_t oc = static_cast<uint32_t>(__shfl_xor(static_cast<int>(best), d, 64));
+    if (oj < best_j || (oj == best_j && orank < best_rank)) {
+      best_j = oj;
+      best_rank = orank;
+      best = oc;
+    }
+  }
+  return best;
+}
+
+// Encode one block with the MSE-searched scale: returns the scale code.
+__device__ __forceinline__ uint32_t encode_block_mse(const float (&y)[kBlock], float g, uint32_t& lo,
+                                                     uint32_t& hi) {
+  const float A = block_absmax(y);
+  const uint32_t S = mse_scale_code(y, A, g, e4m3_scale_code(A, g));
+  encode_block_with(y, g, S, lo, hi);
   return S;
 }
 

@@ -63,7 +63,10 @@ __device__ __forceinline__ int32_t append_slot(const AppendPair& p, int n) {
   return (pg < 0 || s64 >= p.max_slot) ? -1 : static_cast<int32_t>(s64);
 }
 
-// grid: x = token chunks of kTokPerWg, y = KV head (y < Hkv: keys, else values)
+// grid: x = token chunks of kTokPerWg, y = KV head (y < Hkv: keys, else values).  MSE:
+// compiled with the key block-scale search (which needs more registers than the plain
+// encoder, so the plain launch does not carry it).
+template <bool MSE>
 __global__ void __launch_bounds__(256) k_quantize_append(AppendPair p) {
   const int which = static_cast<int>(blockIdx.y) >= p.hkv ? 1 : 0;
   const AppendArgs a = which ? p.a[1] : p.a[0];   // uniform select, no dynamic indexing
@@ -116,7 +119,8 @@ __global__ void __launch_bounds__(256) k_quantize_append(AppendPair p) {
     }
     if (a.flags & 2u) hadamard_row<8>(y, blk);
     uint32_t lo, hi;
-    const uint32_t S = encode_block(y, gsc, lo, hi);
+    const uint32_t S = (MSE && (a.flags & NVKV_K_MSE_SCALE)) ? encode_block_mse(y, gsc, lo, hi)
+                                                             : encode_block(y, gsc, lo, hi);
     if (!ok) continue;
     if (!a.quad_words) {
       *reinterpret_cast<uint2*>(a.codes + row_index * 64 + blk * 8) = make_uint2(lo, hi);
@@ -241,7 +245,10 @@ hipError_t launch_quantize_append_rows(const nvkv_layer& L, const uint16_t* k_ne
   p.page_size = L.page_size;
   p.max_slot = static_cast<int64_t>(L.num_pages) * L.page_size;
   const dim3 grid((N + kTokPerWg - 1) / kTokPerWg, 2 * L.num_kv_heads);
-  hipLaunchKernelGGL(k_quantize_append, grid, dim3(64 * kAppendWaves), 0, stream, p);
+  if (p.a[0].flags & NVKV_K_MSE_SCALE)
+    hipLaunchKernelGGL(k_quantize_append<true>, grid, dim3(64 * kAppendWaves), 0, stream, p);
+  else
+    hipLaunchKernelGGL(k_quantize_append<false>, grid, dim3(64 * kAppendWaves), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -68,7 +68,8 @@ def _layer(**kw):
 BAD_LAYERS = [
     (dict(head_dim=64), 2), (dict(num_kv_heads=0), 2), (dict(page_size=24), 2), (dict(page_size=0), 2),
     (dict(num_pages=0), 2), (dict(reserved=1), 2), (dict(k_fmt=7), 3), (dict(v_fmt=0), 3),
-    (dict(k_flags=4), 3), (dict(k_fmt=0, k_flags=1), 3), (dict(k_data=None), 1), (dict(v_scales=None), 1),
+    (dict(k_flags=8), 3), (dict(k_fmt=0, k_flags=1), 3), (dict(k_fmt=0, k_flags=4), 3), (dict(k_data=None), 1),
+    (dict(v_scales=None), 1),
     (dict(k_scales=None), 1), (dict(k_smooth=None), 1), (dict(k_inv_smooth=None), 1),
     (dict(global_scale=None), 1),
 ]

@@ -8,7 +8,8 @@ sequence is quantised into the cache and attended in the same launch.
 * the stale content of the new token's slot is never read (the slot is pre-filled with a
   different token before the call);
 * every split size, ragged lengths (n = 0, 1, page and split boundaries), bf16 keys, an
-  out-of-range page for the new token.
+  out-of-range page for the new token, MSE-searched key scales (the new token's search runs
+  on four lanes per block inside the decode launch).
 """
 import numpy as np
 import pytest
@@ -17,7 +18,7 @@ import torch
 from oracle import nvfp4_oracle as O
 from synth import kv_inputs as S
 from tests import _pipeline as P
-from tests.test_gpu_parity import (FLAG_SETS, assert_close, gpu_calibrate, gpu_fill_cache, oracle_decode,
+from tests.test_gpu_parity import (FLAG_SETS, MSE, MSE_FLAG_SETS, assert_close, gpu_calibrate, gpu_fill_cache, oracle_decode,
                                    oracle_layer)
 
 pytestmark = pytest.mark.gpu
@@ -75,8 +76,8 @@ def check_cache_rows(cache, pages, hkv, kc, ks, vc, vs, seq_lens, k_bf16=None):
         assert np.array_equal(gc, vc[b, :n]) and np.array_equal(gs, vs[b, :n]), f"V rows differ, seq {b}"
 
 
-@pytest.mark.parametrize("name", ["tiny", "layer"])
-@pytest.mark.parametrize("flags", FLAG_SETS)
+@pytest.mark.parametrize("name,flags", [(n, f) for n in ("tiny", "layer") for f in FLAG_SETS]
+                         + [("tiny", f) for f in MSE_FLAG_SETS] + [("layer", MSE | 1)])
 @pytest.mark.parametrize("paged", [False, True])
 def test_decode_append_parity(lib, name, flags, paged):
     c, k, v, kw, vw, q = P.workload(name)

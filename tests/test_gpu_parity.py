@@ -5,8 +5,11 @@
   relative L2 <= 1e-4 against the fp64 oracle.
 Workloads: the tiny reference (1 KV head, 4 query heads, context 256) and one Qwen3-8B-shaped
 layer (8 KV heads, 32 query heads, batch 4, context 2304); contiguous and 16-token paged
-caches with a shuffled page table; every key-transform combination; BF16 keys.
+caches with a shuffled page table; every key-transform combination; BF16 keys; the
+MSE-searched key block scale (NVKV_K_MSE_SCALE) with each key transform.
 """
+import hashlib
+
 import numpy as np
 import pytest
 import torch
@@ -19,6 +22,12 @@ from tests.conftest import gpu_available
 pytestmark = pytest.mark.gpu
 
 FLAG_SETS = [0, 1, 2, 3]
+MSE = O.FLAG_MSE_SCALE
+MSE_FLAG_SETS = [MSE, MSE | 1, MSE | 3]
+# (workload, key flags): every flag set on the tiny reference, the MSE search on the
+# Qwen3-8B layer with smoothing (the oracle's search takes ~15 s per layer)
+QUANT_CASES = ([(n, f) for n in ("tiny", "layer") for f in FLAG_SETS] + [("tiny", f) for f in MSE_FLAG_SETS]
+               + [("layer", MSE | 1)])
 ATOL_FRAC = 1e-3
 REL_L2 = 1e-4
 
@@ -52,13 +61,28 @@ def gpu_fill_cache(nk, k, v, hkv, flags, pages, s, r, g, k_fmt=1, chunk=None):
     return cache
 
 
+_ORACLE_LAYERS = {}
+
+
+def _digest(*arrays) -> str:
+    h = hashlib.sha1()
+    for a in arrays:
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()
+
+
 def oracle_layer(k, v, kw, vw, flags, exclude_pos0=True):
-    kwf, vwf = S.bf16_to_f32(kw), S.bf16_to_f32(vw)
-    s, r, g = O.calibrate(kwf, vwf, exclude_pos0=exclude_pos0, k_flags=flags)
-    y = O.key_transform(S.bf16_to_f32(k), r[None, None], flags)
-    kc, ks = O.quantize_rows(y, g[0])
-    vc, vs = O.quantize_rows(S.bf16_to_f32(v), g[1])
-    return s, r, g, kc, ks, vc, vs
+    """Oracle calibration and encoding of one layer (memoised per input and flags; callers
+    treat the returned arrays as read-only)."""
+    key = (_digest(k, v, kw, vw), flags, exclude_pos0)
+    if key not in _ORACLE_LAYERS:
+        kwf, vwf = S.bf16_to_f32(kw), S.bf16_to_f32(vw)
+        s, r, g = O.calibrate(kwf, vwf, exclude_pos0=exclude_pos0, k_flags=flags)
+        y = O.key_transform(S.bf16_to_f32(k), r[None, None], flags)
+        kc, ks = O.quantize_keys(y, g[0], flags)
+        vc, vs = O.quantize_rows(S.bf16_to_f32(v), g[1])
+        _ORACLE_LAYERS[key] = (s, r, g, kc, ks, vc, vs)
+    return _ORACLE_LAYERS[key]
 
 
 @pytest.mark.parametrize("name", ["tiny", "layer"])
@@ -73,8 +97,7 @@ def test_calibrate_bit_exact(lib, name, flags):
         assert np.array_equal(g.cpu().numpy().view(np.uint32), go.view(np.uint32)), (g, go)
 
 
-@pytest.mark.parametrize("name", ["tiny", "layer"])
-@pytest.mark.parametrize("flags", FLAG_SETS)
+@pytest.mark.parametrize("name,flags", QUANT_CASES)
 @pytest.mark.parametrize("paged", [False, True])
 def test_quantize_bit_exact(lib, name, flags, paged):
     c, k, v, kw, vw, q = P.workload(name)
@@ -137,8 +160,8 @@ def assert_close(got, ref, vmax, seq_lens):
         assert rel.max() <= REL_L2, f"seq {b}: rel L2 {rel.max():.3e} > {REL_L2}"
 
 
-@pytest.mark.parametrize("name", ["tiny", "layer"])
-@pytest.mark.parametrize("flags", FLAG_SETS)
+@pytest.mark.parametrize("name,flags", [(n, f) for n in ("tiny", "layer") for f in FLAG_SETS]
+                         + [("tiny", MSE | 3), ("layer", MSE | 1)])
 @pytest.mark.parametrize("paged", [False, True])
 def test_decode_parity(lib, name, flags, paged):
     c, k, v, kw, vw, q = P.workload(name)

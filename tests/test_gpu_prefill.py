@@ -6,8 +6,8 @@ query position, query head) relative L2 <= 1e-4 against the fp64 oracle; rows wh
 falls before the sequence start are exactly zero.
 
 Cases: the tiny reference as a full teacher-forced window (Tq = T = 256) and a Qwen3-8B layer
-(B = 4, T = 2304) with a 40-position block; every key-transform combination, contiguous and
-paged caches; ragged lengths (0, shorter than the block, page and tile boundaries, a block
+(B = 4, T = 2304) with a 40-position block; every key-transform combination and MSE-searched
+key scales, contiguous and paged caches; ragged lengths (0, shorter than the block, page and tile boundaries, a block
 size that is not a multiple of the 8-position tile); BF16 keys; a full 2304-position window
 checked on sampled rows; agreement of the last row with the decode kernel.
 """
@@ -18,7 +18,7 @@ import torch
 from oracle import nvfp4_oracle as O
 from synth import kv_inputs as S
 from tests import _pipeline as P
-from tests.test_gpu_parity import FLAG_SETS, gpu_calibrate, gpu_decode, gpu_fill_cache, oracle_layer
+from tests.test_gpu_parity import FLAG_SETS, MSE, gpu_calibrate, gpu_decode, gpu_fill_cache, oracle_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -83,8 +83,8 @@ def build_layer(lib, name, flags, paged, T=None, B=None, k_fmt=1):
     return c, k, so, go, kc, ks, vc, vs, pages, cache
 
 
-@pytest.mark.parametrize("name,Tq", [("tiny", 256), ("layer", 40)])
-@pytest.mark.parametrize("flags", FLAG_SETS)
+@pytest.mark.parametrize("name,Tq,flags", [(n, t, f) for n, t in (("tiny", 256), ("layer", 40)) for f in FLAG_SETS]
+                         + [("tiny", 256, MSE | 3), ("layer", 40, MSE | 1)])
 @pytest.mark.parametrize("paged", [False, True])
 def test_prefill_parity(lib, name, Tq, flags, paged):
     c, k, so, go, kc, ks, vc, vs, pages, cache = build_layer(lib, name, flags, paged)
