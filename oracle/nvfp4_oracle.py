@@ -25,7 +25,10 @@ What the oracle computes (plain, slow, obviously correct; NumPy, fp64 unless not
   * quantize_rows_mse   -- the same encoding with each key block's E4M3 scale searched for
                            the smallest exact squared error (optional key flag).
   * dequantize          -- code value * block scale * tensor scale, in fp64 (exact).
-  * query_transform     -- q*s, optionally H(q*s)/128, in fp64.
+  * klt_basis           -- the static per-head KLT key basis (fp64 eigendecomposition of the
+                           calibration keys' covariance, fp32 result); rotate_fp32 applies
+                           it to key rows in a fixed fp32 order.
+  * query_transform     -- q*s, optionally H(q*s)/128 or B^T(q*s), in fp64.
   * attention           -- textbook softmax attention over the dequantised cache, fp64.
   * causal_attention    -- the same for a block of query positions with the causal mask
                            (teacher-forced evaluation over the cache), fp64.
@@ -44,6 +47,11 @@ Readings taken where the pages leave a step open (each is repeated in the design
   - smoothing is applied before the Hadamard basis when both are selected.
   - a block of Tq queries of a sequence holding n cached tokens sits at positions
     n-Tq .. n-1 (the block's own keys are in the cache); position p sees keys 0..p.
+  - KLT basis: eigenvectors of the centred covariance of the (smoothed) calibration keys over
+    the smoothing's positions, decreasing eigenvalues, largest entry of each positive (ties
+    within a relative 1e-6: the first), fp32;
+    keys rotated by a sequential fp32 sum without fused multiply-add; not combined with the
+    Hadamard basis.
   - MSE-searched key scales: candidates are the absmax-to-6 code and every E4M3 code that
     puts the block maximum between 7/4 and 7 times the scale; the exact squared error
     decides, ties to the absmax-to-6 code, then to the smallest code.
@@ -63,6 +71,7 @@ N_BLOCKS = HEAD_DIM // BLOCK
 FLAG_SMOOTH = 1
 FLAG_HADAMARD = 2
 FLAG_MSE_SCALE = 4
+FLAG_KLT = 8
 
 # Largest E2M1 magnitude ([OSFP4] section 1: the FP4 constellation tops out at 6) and
 # largest finite E4M3FN value (bias 7, mantissa 0b110 at exponent 15).
@@ -156,15 +165,76 @@ def sylvester_hadamard(n: int = HEAD_DIM) -> np.ndarray:
     return H
 
 
-def key_transform(x: np.ndarray, r: np.ndarray | None, flags: int) -> np.ndarray:
-    """Post-RoPE key rows x (any float dtype holding bf16 values, last axis 128) -> fp32 rows
-    that get quantised.  Smoothing: y_j = fl32(x_j * r_j); then the Hadamard butterfly."""
+def key_transform(x: np.ndarray, r: np.ndarray | None, flags: int, basis: np.ndarray | None = None) -> np.ndarray:
+    """Post-RoPE key rows x (any float dtype holding bf16 values, last axes [Hkv][128]) -> fp32
+    rows that get quantised.  Smoothing: y_j = fl32(x_j * r_j); then the Hadamard butterfly or
+    the KLT basis rotation (basis [Hkv][128][128], see rotate_fp32)."""
+    if (flags & FLAG_HADAMARD) and (flags & FLAG_KLT):
+        raise ValueError("the Hadamard and KLT key bases exclude each other")
     y = np.asarray(x, dtype=np.float32)
     if flags & FLAG_SMOOTH:
         y = (y * np.asarray(r, dtype=np.float32)).astype(np.float32)
     if flags & FLAG_HADAMARD:
         y = hadamard_butterfly_fp32(y)
+    if flags & FLAG_KLT:
+        y = rotate_fp32(y, basis)
     return y
+
+
+# ----------------------------------------------------------------------------------------
+# Static per-head KLT key basis ([cache post] cache-config table rows "K: static per-head
+# KLT" and "K: static KLT + smoothing": the keys of each KV head are expressed in a fixed
+# basis computed once from calibration data, optionally after the static smoothing).
+#
+# Readings (the pages name the transform only): the KLT of a head is the eigenbasis of the
+# covariance (mean removed) of that head's calibration keys, taken after the smoothing when
+# both are selected, over the positions the smoothing calibration uses (position 0 excluded);
+# columns in decreasing eigenvalue order, each signed so that its largest-magnitude entry is
+# positive (entries within a relative 1e-6 of the largest count as ties, and the first of
+# them decides, so that rounding noise cannot flip a sign); stored as fp32.  Keys are rotated z = B^T y with each
+# output a sequential fp32 sum over the input index, every product and every sum rounded to
+# fp32 (no fused multiply-add), so that codes are reproducible bit for bit; the query side
+# applies the same fp32 basis in fp64.  The Hadamard and KLT bases are not combined.
+# ----------------------------------------------------------------------------------------
+KLT_SIGN_TIE = 1e-6     # entries within this relative distance of the largest count as ties
+
+
+def klt_basis(k_win: np.ndarray, r: np.ndarray | None, k_flags: int, exclude_pos0: bool = True):
+    """k_win [W][T][Hkv][128] (bf16 values) -> (basis f32 [Hkv][128][128], eigenvalues f64
+    [Hkv][128]); column i of basis[h] is the eigenvector of eigenvalue i (decreasing)."""
+    y = key_transform(np.asarray(k_win, dtype=np.float32), None if r is None else r[None, None],
+                      k_flags & FLAG_SMOOTH)
+    y = y[:, 1:] if exclude_pos0 else y
+    hkv = y.shape[2]
+    X = y.astype(np.float64).reshape(-1, hkv, HEAD_DIM)
+    basis = np.zeros((hkv, HEAD_DIM, HEAD_DIM), dtype=np.float32)
+    lam_out = np.zeros((hkv, HEAD_DIM))
+    for h in range(hkv):
+        D = X[:, h] - X[:, h].mean(axis=0)
+        C = D.T @ D / D.shape[0]
+        lam, V = np.linalg.eigh(C)                  # increasing
+        order = np.argsort(-lam, kind="stable")
+        lam, V = lam[order], V[:, order]
+        for i in range(HEAD_DIM):
+            a = np.abs(V[:, i])
+            j = int(np.argmax(a >= (1.0 - KLT_SIGN_TIE) * a.max()))   # first (near-)largest entry
+            if V[j, i] < 0:
+                V[:, i] = -V[:, i]
+        basis[h] = V.astype(np.float32)
+        lam_out[h] = lam
+    return basis, lam_out
+
+
+def rotate_fp32(y: np.ndarray, basis: np.ndarray) -> np.ndarray:
+    """z[..., h, i] = sum_j basis[h, j, i] * y[..., h, j], the sum taken sequentially over
+    j = 0..127 with every product and every partial sum rounded to fp32."""
+    y = np.asarray(y, dtype=np.float32)
+    B = np.asarray(basis, dtype=np.float32)
+    acc = np.zeros(y.shape, dtype=np.float32)
+    for j in range(HEAD_DIM):
+        prod = (B[:, j, :] * y[..., :, j:j + 1]).astype(np.float32)
+        acc = (acc + prod).astype(np.float32)
+    return acc
 
 
 # ----------------------------------------------------------------------------------------
@@ -176,7 +246,8 @@ def calibrate(k_win: np.ndarray | None, v_win: np.ndarray | None,
               exclude_pos0: bool = True, k_flags: int = FLAG_SMOOTH):
     """k_win, v_win: [W][T][Hkv][128] arrays of bf16 values (as float).
     Returns (s [Hkv][128] f32, r [Hkv][128] f32, g [2] f32) with g = (g_K, g_V).
-    A part whose windows are None is returned as None (s, r) / NaN (g entry)."""
+    A part whose windows are None is returned as None (s, r) / NaN (g entry).  With the KLT
+    flag, g_K is taken over keys rotated by klt_basis of the same windows."""
     s = r = None
     g = np.array([np.nan, np.nan], dtype=np.float32)
     if k_win is not None:
@@ -187,7 +258,8 @@ def calibrate(k_win: np.ndarray | None, v_win: np.ndarray | None,
         # is exact-rounding for sqrt and division: 53 >= 2*24 + 2).
         s = np.where(a == 0.0, 1.0, np.sqrt(a)).astype(np.float32)
         r = (np.float32(1.0) / s).astype(np.float32)
-        y = key_transform(np.asarray(k_win, dtype=np.float32), r[None, None], k_flags)
+        basis = klt_basis(k_win, r, k_flags, exclude_pos0)[0] if k_flags & FLAG_KLT else None
+        y = key_transform(np.asarray(k_win, dtype=np.float32), r[None, None], k_flags, basis)
         g[0] = _tensor_scale(np.abs(y.astype(np.float64)).max())
     if v_win is not None:
         g[1] = _tensor_scale(np.abs(np.asarray(v_win, dtype=np.float64)).max())
@@ -358,15 +430,19 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, g: float) -> np.ndarray:
 # post-RoPE cache; smoothing row: SmoothAttention, keys divided and queries multiplied by s;
 # Hadamard rows: an orthogonal basis change on head_dim).
 # ----------------------------------------------------------------------------------------
-def query_transform(q: np.ndarray, s: np.ndarray | None, flags: int) -> np.ndarray:
-    """q [..., 128] (bf16 values) -> q' in fp64: q*s, then H(q*s)/128 when Hadamard is on.
-    ``s`` broadcasts against q (one row per KV head of each query head)."""
+def query_transform(q: np.ndarray, s: np.ndarray | None, flags: int, basis: np.ndarray | None = None) -> np.ndarray:
+    """q [..., 128] (bf16 values) -> q' in fp64: q*s, then H(q*s)/128 when Hadamard is on, or
+    B^T (q*s) with the KLT basis.  ``s`` and ``basis`` ([..., 128, 128]) broadcast against q
+    (one entry per KV head of each query head)."""
     qp = np.asarray(q, dtype=np.float64)
     if flags & FLAG_SMOOTH:
         qp = qp * np.asarray(s, dtype=np.float64)
     if flags & FLAG_HADAMARD:
         H = sylvester_hadamard(HEAD_DIM).astype(np.float64)
         qp = qp @ H.T / 128.0
+    if flags & FLAG_KLT:
+        B = np.asarray(basis, dtype=np.float64)
+        qp = np.einsum("...j,...ji->...i", qp, B)
     return qp
 
 

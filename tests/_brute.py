@@ -56,3 +56,23 @@ def e2m1_encode_brute(x: Fraction, unit: Fraction) -> int:
             if (c & 7) % 2 == 0 and (best[1] & 7) % 2 == 1:
                 best = (d, c, v)
     return best[1]
+
+
+def fraction_to_f32(x: Fraction):
+    """Round-to-nearest-even of an exact rational to fp32 (zero and the normal range)."""
+    import numpy as np
+    if x == 0:
+        return np.float32(0.0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    q = a / Fraction(2) ** (e - 23)                  # in [2^23, 2^24)
+    n = q.numerator // q.denominator
+    rem = q - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return np.float32(sign * float(Fraction(n) * Fraction(2) ** (e - 23)))

@@ -10,6 +10,7 @@ import pytest
 
 from oracle import nvfp4_oracle as O
 from tests import test_oracle_codec as C
+from tests import test_oracle_klt as K
 from tests import test_oracle_mse_scale as M
 from tests import test_oracle_transforms as T
 
@@ -138,6 +139,49 @@ def _mse_without_absmax_code(y32, g):
     return _mse_search(y32, g, with_absmax=False)
 
 
+def _klt_variant(k_win, r, k_flags, exclude_pos0=True, centred=True, descending=True, sign=1.0):
+    y = O.key_transform(np.asarray(k_win, np.float32), None if r is None else r[None, None], k_flags & O.FLAG_SMOOTH)
+    y = y[:, 1:] if exclude_pos0 else y
+    hkv = y.shape[2]
+    X = y.astype(np.float64).reshape(-1, hkv, 128)
+    B = np.zeros((hkv, 128, 128), np.float32)
+    L = np.zeros((hkv, 128))
+    for h in range(hkv):
+        D = X[:, h] - X[:, h].mean(0) if centred else X[:, h]
+        lam, V = np.linalg.eigh(D.T @ D / D.shape[0])
+        order = np.argsort(-lam if descending else lam, kind="stable")
+        lam, V = lam[order], V[:, order]
+        for i in range(128):
+            a = np.abs(V[:, i])
+            j = int(np.argmax(a >= (1 - 1e-6) * a.max()))
+            if sign * V[j, i] < 0:
+                V[:, i] = -V[:, i]
+        B[h], L[h] = V.astype(np.float32), lam
+    return B, L
+
+
+def _klt_uncentred(k_win, r, k_flags, exclude_pos0=True):
+    return _klt_variant(k_win, r, k_flags, exclude_pos0, centred=False)
+
+
+def _klt_ascending(k_win, r, k_flags, exclude_pos0=True):
+    return _klt_variant(k_win, r, k_flags, exclude_pos0, descending=False)
+
+
+def _klt_largest_negative(k_win, r, k_flags, exclude_pos0=True):
+    return _klt_variant(k_win, r, k_flags, exclude_pos0, sign=-1.0)
+
+
+def _rotate_transposed(y, basis):
+    return ORIG_ROT(y, np.swapaxes(np.asarray(basis), 1, 2))
+
+
+def _query_basis_not_transposed(q, s, flags, basis=None):
+    if flags & O.FLAG_KLT:
+        basis = np.swapaxes(np.asarray(basis), -1, -2)
+    return ORIG_QT(q, s, flags, basis)
+
+
 def _dequant_drop_g(codes, scales, g):
     return ORIG_DQ(codes, scales, 1.0)
 
@@ -147,6 +191,8 @@ ORIG_KT = O.key_transform
 ORIG_CAL = O.calibrate
 ORIG_DQ = O.dequantize
 ORIG_CA = O.causal_attention
+ORIG_ROT = O.rotate_fp32
+ORIG_QT = O.query_transform
 
 CASES = [
     ("rne_grid_index", _ties_to_odd, [C.test_e4m3_block_scale_vs_fraction_brute_force,
@@ -170,6 +216,13 @@ CASES = [
     ("mse_scale_codes", _mse_ties_to_last, [M.test_mse_worked_example_with_tie]),
     ("mse_scale_codes", _mse_without_absmax_code, [M.test_mse_scale_vs_fraction_brute_force_random_blocks,
                                                    M.test_mse_special_cases]),
+    ("klt_basis", _klt_uncentred, [K.test_klt_basis_closed_form_hadamard_columns]),
+    ("klt_basis", _klt_ascending, [K.test_klt_basis_closed_form_hadamard_columns]),
+    ("klt_basis", _klt_largest_negative, [K.test_klt_basis_closed_form_hadamard_columns,
+                                          K.test_diagonal_covariance_gives_an_exact_permutation]),
+    ("rotate_fp32", _rotate_transposed, [K.test_rotation_order_vs_exact_rationals]),
+    ("query_transform", _query_basis_not_transposed,
+     [lambda: K.test_klt_keeps_scores_and_g_is_over_rotated_keys(O.FLAG_KLT)]),
 ]
 
 
