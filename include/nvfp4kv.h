@@ -87,7 +87,13 @@ enum { NVKV_FMT_BF16 = 0, NVKV_FMT_NVFP4 = 1 };
  * between 7/4 and 7 scale units, the flat interval of section 2.1 and appendix A; ties keep
  * the absmax-to-6 code, then the smaller code).  It changes only how keys are encoded: the
  * cache format, the calibration (g_K) and the attention calls are unchanged. */
-enum { NVKV_K_SMOOTH = 1u, NVKV_K_HADAMARD = 2u, NVKV_K_MSE_SCALE = 4u };
+enum { NVKV_K_SMOOTH = 1u, NVKV_K_HADAMARD = 2u, NVKV_K_MSE_SCALE = 4u, NVKV_K_KLT = 8u };
+/* NVKV_K_KLT: static per-head KLT key basis ([cache post] cache-config table rows "K: static
+ * per-head KLT" and "K: static KLT + smoothing"): keys are rotated z = B^T y after the optional
+ * smoothing, queries q' = B^T (q * s), with B = layer->k_basis from nvkv_calibrate_key_basis.
+ * Each z_i is the sequential fp32 sum over j = 0..127 of fl32(B[j][i] * y_j), every product and
+ * partial sum rounded to fp32 (no fused multiply-add), so codes are reproducible bit for bit.
+ * Not combined with NVKV_K_HADAMARD. */
 enum { NVKV_PART_CODES = 0, NVKV_PART_SCALES = 1 };
 
 #define NVKV_HEAD_DIM 128
@@ -110,6 +116,9 @@ typedef struct nvkv_layer {
   const float *k_smooth;      /* s [Hkv][128]: query side; required when NVKV_K_SMOOTH     */
   const float *k_inv_smooth;  /* r [Hkv][128] = fl32(1/s): key side; required with SMOOTH  */
   const float *global_scale;  /* [2] = {g_K, g_V}; g_K unused for BF16 keys                */
+  const float *k_basis;       /* B [Hkv][128][128] fp32, element (j, i) of head h at
+                                 (h*128 + j)*128 + i, column i = basis vector i; required
+                                 with NVKV_K_KLT, ignored otherwise                        */
 } nvkv_layer;
 
 /*
@@ -121,6 +130,8 @@ typedef struct nvkv_layer {
  *                (including 0) and head of the keys transformed as selected by k_flags
  *                (smoothing by r, then the Hadamard butterfly); 1 when A_K = 0.
  *                NVKV_K_MSE_SCALE in k_flags is accepted and does not change the result.
+ *                With NVKV_K_KLT in k_flags, g_out[0] is not written: the basis comes first
+ *                (nvkv_calibrate_key_basis, which then writes g_K).
  *   From v_win:  g_out[1] = fl32(A_V / 2688), A_V = max |v|; 1 when A_V = 0.
  *   s_out, r_out: fp32 [Hkv][128] (needed when k_win != NULL); g_out: fp32 [2].  Entries whose
  *   input is NULL are left untouched.  s_out and g_out double as the reduction buffers, so
@@ -131,6 +142,34 @@ NVKV_API nvkv_status nvkv_calibrate_key_smoothing(const uint16_t *k_win, const u
                                          int32_t exclude_pos0, uint32_t k_flags,
                                          float *s_out, float *r_out, float *g_out,
                                          void *stream);
+
+/*
+ * Static per-head KLT key basis and its tensor scale ([cache post] cache-config table rows
+ * "K: static per-head KLT" and "K: static KLT + smoothing").  Run after
+ * nvkv_calibrate_key_smoothing on the same windows.
+ *   k_win:     bf16 [W][T][Hkv][128] calibration windows.
+ *   r:         fp32 [Hkv][128] key smoothing factors (1/s); used when k_flags has
+ *              NVKV_K_SMOOTH (the basis is then computed from the smoothed keys), else ignored.
+ *   k_flags:   must contain NVKV_K_KLT and not NVKV_K_HADAMARD.
+ *   basis_out: fp32 [Hkv][128][128], layout of nvkv_layer.k_basis.  Column i of head h is the
+ *              eigenvector of the i-th largest eigenvalue of the covariance (mean removed) of
+ *              head h's keys over all windows and positions t >= 1 (t >= 0 when exclude_pos0
+ *              == 0), computed in fp64 (cyclic Jacobi), signed so that its largest-magnitude
+ *              entry is positive (entries within a relative 1e-6 of the largest count as ties;
+ *              the first decides), rounded to fp32.
+ *   g_out:     fp32 [2]; g_out[0] = fl32(A_K / 2688), A_K = max |z| over every window,
+ *              position and head of the keys smoothed and rotated by basis_out (1 when A_K = 0).
+ *              g_out[1] is not touched.
+ *   workspace: device scratch of nvkv_calibrate_key_basis_workspace_bytes(Hkv) bytes,
+ *              256-byte aligned; no initial contents needed.
+ * W >= 1, T >= 2, Hkv >= 1.  Errors: NVKV_ERR_NULL, NVKV_ERR_SHAPE, NVKV_ERR_UNSUPPORTED
+ * (flags), NVKV_ERR_WORKSPACE, NVKV_ERR_HIP.
+ */
+NVKV_API size_t nvkv_calibrate_key_basis_workspace_bytes(int32_t Hkv);
+NVKV_API nvkv_status nvkv_calibrate_key_basis(const uint16_t *k_win, int32_t W, int32_t T, int32_t Hkv,
+                                     int32_t exclude_pos0, uint32_t k_flags, const float *r,
+                                     float *basis_out, float *g_out,
+                                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Quantise-and-append ([cache post] opening paragraph and table; [OSFP4] sections 1, 3 and

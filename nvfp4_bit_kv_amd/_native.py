@@ -16,13 +16,14 @@ NVKV_OK = 0
 STATUS_NAMES = {0: "NVKV_OK", 1: "NVKV_ERR_NULL", 2: "NVKV_ERR_SHAPE", 3: "NVKV_ERR_UNSUPPORTED",
                 4: "NVKV_ERR_WORKSPACE", 5: "NVKV_ERR_HIP"}
 FMT_BF16, FMT_NVFP4 = 0, 1
-K_SMOOTH, K_HADAMARD, K_MSE_SCALE = 1, 2, 4
+K_SMOOTH, K_HADAMARD, K_MSE_SCALE, K_KLT = 1, 2, 4, 8
 PART_CODES, PART_SCALES = 0, 1
 HEAD_DIM = 128
 
 EXPORTED = ["nvkv_calibrate_key_smoothing", "nvkv_quantize_append_kv", "nvkv_decode_workspace_bytes",
             "nvkv_decode_attention_nvfp4", "nvkv_decode_append_attention_nvfp4", "nvkv_cache_array_bytes", "nvkv_cache_bytes_per_token",
-            "nvkv_status_string", "nvkv_last_error", "nvkv_prefill_attention_nvfp4"]
+            "nvkv_status_string", "nvkv_last_error", "nvkv_prefill_attention_nvfp4",
+            "nvkv_calibrate_key_basis_workspace_bytes", "nvkv_calibrate_key_basis"]
 
 
 class NvkvError(RuntimeError):
@@ -41,7 +42,7 @@ class Layer(ctypes.Structure):
         ("k_data", ctypes.c_void_p), ("v_data", ctypes.c_void_p),
         ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
         ("k_smooth", ctypes.c_void_p), ("k_inv_smooth", ctypes.c_void_p),
-        ("global_scale", ctypes.c_void_p),
+        ("global_scale", ctypes.c_void_p), ("k_basis", ctypes.c_void_p),
     ]
 
 
@@ -61,6 +62,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     vp, i32, u32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t
     lib.nvkv_calibrate_key_smoothing.argtypes = [vp, vp, i32, i32, i32, i32, u32, vp, vp, vp, vp]
     lib.nvkv_calibrate_key_smoothing.restype = ctypes.c_int
+    lib.nvkv_calibrate_key_basis_workspace_bytes.argtypes = [i32]
+    lib.nvkv_calibrate_key_basis_workspace_bytes.restype = sz
+    lib.nvkv_calibrate_key_basis.argtypes = [vp, i32, i32, i32, i32, u32, vp, vp, vp, vp, sz, vp]
+    lib.nvkv_calibrate_key_basis.restype = ctypes.c_int
     lib.nvkv_quantize_append_kv.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, i32, vp]
     lib.nvkv_quantize_append_kv.restype = ctypes.c_int
     lib.nvkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -113,6 +118,17 @@ def calibrate_key_smoothing(k_win, v_win, W: int, T: int, Hkv: int, exclude_pos0
     _check(load().nvkv_calibrate_key_smoothing(_ptr(k_win), _ptr(v_win), W, T, Hkv, int(bool(exclude_pos0)),
                                                k_flags, _ptr(s_out), _ptr(r_out), _ptr(g_out), _stream(stream)),
            "nvkv_calibrate_key_smoothing")
+
+
+def calibrate_key_basis_workspace_bytes(Hkv: int) -> int:
+    return int(load().nvkv_calibrate_key_basis_workspace_bytes(Hkv))
+
+
+def calibrate_key_basis(k_win, W: int, T: int, Hkv: int, exclude_pos0: bool, k_flags: int, r, basis_out, g_out,
+                        workspace, workspace_bytes: int, stream=None) -> None:
+    _check(load().nvkv_calibrate_key_basis(_ptr(k_win), W, T, Hkv, int(bool(exclude_pos0)), k_flags, _ptr(r),
+                                           _ptr(basis_out), _ptr(g_out), _ptr(workspace), workspace_bytes,
+                                           _stream(stream)), "nvkv_calibrate_key_basis")
 
 
 def quantize_append_kv(layer: Layer, k_new, v_new, slot_mapping, N: int, stream=None) -> None:

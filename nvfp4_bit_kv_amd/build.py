@@ -2,8 +2,8 @@
 
     python -m nvfp4_bit_kv_amd.build
 
-The quantise/calibrate translation unit is compiled with -ffp-contract=off (its fp32 key
-transform is part of the bit-exact encoding); the decode unit with -fno-honor-nans (its
+The quantise/calibrate and KLT-calibration translation units are compiled with
+-ffp-contract=off (their fp32 key transform is part of the bit-exact encoding); the decode unit with -fno-honor-nans (its
 scores are finite or -inf and every code and scale decodes finite, so max operations need
 no NaN quieting), and so is the prefill-attention unit; all HIP code is compiled without
 packed fp32 instructions.
@@ -26,6 +26,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 SOURCES = {
     "nvkv_capi.hip": [],
     "nvkv_quantize.hip": ["-ffp-contract=off"],
+    "nvkv_klt.hip": ["-ffp-contract=off"],
     "nvkv_decode.hip": ["-fno-honor-nans"],
     "nvkv_prefill.hip": ["-fno-honor-nans"],
 }

@@ -33,6 +33,10 @@ class CacheLayer:
         self.smooth = torch.ones((num_kv_heads, N.HEAD_DIM), **f32)
         self.inv_smooth = torch.ones((num_kv_heads, N.HEAD_DIM), **f32)
         self.gscale = torch.ones((2,), **f32)
+        # KLT key basis [Hkv][128][128] (identity until calibrated); only with N.K_KLT
+        self.basis = None
+        if k_flags & N.K_KLT:
+            self.basis = torch.eye(N.HEAD_DIM, **f32).repeat(num_kv_heads, 1, 1).contiguous()
 
     def struct(self) -> N.Layer:
         L = N.Layer()
@@ -44,4 +48,5 @@ class CacheLayer:
         L.v_scales = self.v_scales.data_ptr()
         L.k_smooth, L.k_inv_smooth = self.smooth.data_ptr(), self.inv_smooth.data_ptr()
         L.global_scale = self.gscale.data_ptr()
+        L.k_basis = self.basis.data_ptr() if self.basis is not None else None
         return L

@@ -35,9 +35,12 @@ nvkv_status check_layer(const nvkv_layer* L) {
   if (static_cast<int64_t>(L->num_pages) * L->page_size > INT32_MAX) return fail(NVKV_ERR_SHAPE, "num_pages * page_size exceeds int32");
   if (L->k_fmt != NVKV_FMT_NVFP4 && L->k_fmt != NVKV_FMT_BF16) return fail(NVKV_ERR_UNSUPPORTED, "unknown k_fmt");
   if (L->v_fmt != NVKV_FMT_NVFP4) return fail(NVKV_ERR_UNSUPPORTED, "v_fmt must be NVKV_FMT_NVFP4");
-  if (L->k_flags & ~(NVKV_K_SMOOTH | NVKV_K_HADAMARD | NVKV_K_MSE_SCALE))
+  if (L->k_flags & ~(NVKV_K_SMOOTH | NVKV_K_HADAMARD | NVKV_K_MSE_SCALE | NVKV_K_KLT))
     return fail(NVKV_ERR_UNSUPPORTED, "unknown k_flags bits");
+  if ((L->k_flags & NVKV_K_HADAMARD) && (L->k_flags & NVKV_K_KLT))
+    return fail(NVKV_ERR_UNSUPPORTED, "the Hadamard and KLT key bases exclude each other");
   if (L->k_fmt == NVKV_FMT_BF16 && L->k_flags != 0) return fail(NVKV_ERR_UNSUPPORTED, "key transforms need NVFP4 keys");
+  if ((L->k_flags & NVKV_K_KLT) && !L->k_basis) return fail(NVKV_ERR_NULL, "k_basis is NULL");
   if (!L->k_data || !L->v_data || !L->v_scales || !L->global_scale) return fail(NVKV_ERR_NULL, "cache pointer is NULL");
   if (L->k_fmt == NVKV_FMT_NVFP4 && !L->k_scales) return fail(NVKV_ERR_NULL, "k_scales is NULL");
   if ((L->k_flags & NVKV_K_SMOOTH) && (!L->k_smooth || !L->k_inv_smooth))
@@ -88,12 +91,40 @@ nvkv_status nvkv_calibrate_key_smoothing(const uint16_t* k_win, const uint16_t* 
   if (W < 1 || W > kMaxGridYZ || T < 1 || Hkv < 1) return fail(NVKV_ERR_SHAPE, "W, T, Hkv must be >= 1 (W <= 65535)");
   if (static_cast<int64_t>(W) * T * Hkv * NVKV_HEAD_DIM > INT32_MAX)
     return fail(NVKV_ERR_SHAPE, "calibration windows exceed 2^31 elements");
-  if (k_flags & ~(NVKV_K_SMOOTH | NVKV_K_HADAMARD | NVKV_K_MSE_SCALE))
+  if (k_flags & ~(NVKV_K_SMOOTH | NVKV_K_HADAMARD | NVKV_K_MSE_SCALE | NVKV_K_KLT))
     return fail(NVKV_ERR_UNSUPPORTED, "unknown k_flags bits");
+  if ((k_flags & NVKV_K_HADAMARD) && (k_flags & NVKV_K_KLT))
+    return fail(NVKV_ERR_UNSUPPORTED, "the Hadamard and KLT key bases exclude each other");
   (void)hipGetLastError();
   return hip_status(nvkv::launch_calibrate(k_win, v_win, W, T, Hkv, exclude_pos0, k_flags, s_out, r_out, g_out,
                                            static_cast<hipStream_t>(stream)),
                     "calibrate launch");
+}
+
+size_t nvkv_calibrate_key_basis_workspace_bytes(int32_t Hkv) {
+  if (Hkv < 1 || Hkv > kMaxGridYZ) return 0;
+  return nvkv::klt_workspace_bytes(Hkv);
+}
+
+nvkv_status nvkv_calibrate_key_basis(const uint16_t* k_win, int32_t W, int32_t T, int32_t Hkv, int32_t exclude_pos0,
+                                     uint32_t k_flags, const float* r, float* basis_out, float* g_out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_win || !basis_out || !g_out) return fail(NVKV_ERR_NULL, "k_win / basis_out / g_out is NULL");
+  if (W < 1 || T < 2 || Hkv < 1 || Hkv > kMaxGridYZ) return fail(NVKV_ERR_SHAPE, "W >= 1, T >= 2, 1 <= Hkv <= 65535");
+  if (static_cast<int64_t>(W) * T * Hkv * NVKV_HEAD_DIM > INT32_MAX)
+    return fail(NVKV_ERR_SHAPE, "calibration windows exceed 2^31 elements");
+  if (k_flags & ~(NVKV_K_SMOOTH | NVKV_K_HADAMARD | NVKV_K_MSE_SCALE | NVKV_K_KLT))
+    return fail(NVKV_ERR_UNSUPPORTED, "unknown k_flags bits");
+  if (!(k_flags & NVKV_K_KLT) || (k_flags & NVKV_K_HADAMARD))
+    return fail(NVKV_ERR_UNSUPPORTED, "k_flags must select the KLT basis and not the Hadamard basis");
+  if ((k_flags & NVKV_K_SMOOTH) && !r) return fail(NVKV_ERR_NULL, "r is NULL with NVKV_K_SMOOTH");
+  if (!workspace || workspace_bytes < nvkv::klt_workspace_bytes(Hkv) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(NVKV_ERR_WORKSPACE, "workspace missing, too small or not 256-byte aligned");
+  (void)hipGetLastError();
+  return hip_status(nvkv::launch_calibrate_basis(k_win, W, T, Hkv, exclude_pos0, k_flags, r, basis_out, g_out,
+                                                 workspace, static_cast<hipStream_t>(stream)),
+                    "calibrate_key_basis launch");
 }
 
 nvkv_status nvkv_quantize_append_kv(const nvkv_layer* layer, const uint16_t* k_new, const uint16_t* v_new,

@@ -38,6 +38,7 @@
 #include "nvkv_device.hpp"
 #include "nvkv_encode.hpp"
 #include "nvkv_internal.hpp"
+#include "nvkv_klt.hpp"
 #include "nvkv_tiles.hpp"
 
 namespace nvkv {
@@ -72,6 +73,7 @@ struct DecodeArgs {
   uint8_t* k_scales_w;
   uint8_t* v_codes_w;
   uint8_t* v_scales_w;
+  const float* basis;         // KLT basis [Hkv][128][128] (NVKV_K_KLT), staged in dynamic LDS
 };
 
 // Online-softmax state of one wavefront.  Lane (c, g) serves query head g: its running max,
@@ -294,7 +296,8 @@ __device__ __forceinline__ void had_cross(float (&y)[4], int lane, int m) {
 // the cache slot too when its page is in range (page pg, offset off).
 template <bool KBF16>
 __device__ __forceinline__ void new_token_encode(const DecodeArgs& a, int h, int lane, const NewTokenRegs& R,
-                                                 int32_t pg, int off, bool ok, NewTokenStage& st) {
+                                                 int32_t pg, int off, bool ok, NewTokenStage& st,
+                                                 const float* basis_lds) {
 #pragma clang fp contract(off)   // part of the bit-exact key transform
   const bool is_v = lane >= 32;
   const int blk = (lane >> 2) & 7, qtr = lane & 3;
@@ -324,6 +327,12 @@ __device__ __forceinline__ void new_token_encode(const DecodeArgs& a, int h, int
     had_cross(y, lane, 4);                                // h = 16
     had_cross(y, lane, 8);                                // h = 32
     had_cross(y, lane, 16);                               // h = 64
+  }
+  if (!KBF16 && (a.k_flags & NVKV_K_KLT)) {
+    // z = B^T y in the fixed rounding order of the append kernel: the key row through LDS,
+    // key lane L computes z[4L .. 4L+3]
+    if (!is_v) *reinterpret_cast<float4*>(&st.ky[4 * (lane & 31)]) = make_float4(y[0], y[1], y[2], y[3]);
+    if (!is_v) rotate_cols<4>(basis_lds, st.ky, 4 * (lane & 31), y);
   }
   // block absmax over the block's four lanes, scale code, E2M1 nibbles
   float A = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
@@ -464,6 +473,12 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   const int64_t unit = static_cast<int64_t>(b) * a.hkv + h;
   const const_i32_ptr ptab = __builtin_bit_cast(const_i32_ptr, a.page_table) + static_cast<int64_t>(b) * a.max_pages_per_seq;
 
+  // KLT key basis of this head into dynamic LDS by every thread; its loads go out before the
+  // cache loads, so waiting for them does not wait for the cache
+  extern __shared__ __attribute__((aligned(16))) float basis_dyn[];
+  const bool klt = !KBF16 && (a.k_flags & NVKV_K_KLT);
+  if (klt) load_basis_lds_x4(a.basis + static_cast<int64_t>(h) * kBasisFloats, basis_dyn, tid, blockDim.x);
+
   // ---- start every independent memory access first: query row, sequence length, pages ----
   const bool q_wave = wave < 4;                 // wavefronts 0..3 prepare query heads 4h..4h+3
   const int hq_w = 4 * h + (q_wave ? wave : 0);
@@ -516,9 +531,10 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   }
 
   // ---------------- query prologue: wavefront w < 4 prepares query head 4h + w ----------------
+  if (klt) __syncthreads();                    // the basis is in LDS
   if (!empty && q_wave) {
     uint32_t w0, w1, w2;
-    const float descale = query_terms<KBF16>(qw, sv, a.k_flags, a.sm_scale, gk, lane, w0, w1, w2);
+    const float descale = query_terms<KBF16>(qw, sv, a.k_flags, a.sm_scale, gk, lane, w0, w1, w2, basis_dyn);
     reinterpret_cast<uint32_t*>(q_lds[wave][0])[lane] = w0;
     reinterpret_cast<uint32_t*>(q_lds[wave][1])[lane] = w1;
     reinterpret_cast<uint32_t*>(q_lds[wave][2])[lane] = w2;
@@ -581,7 +597,7 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
     }
     if (owns_new && app_wave) {
       const bool ok = static_cast<uint32_t>(new_pg) < static_cast<uint32_t>(a.num_pages);
-      new_token_encode<KBF16>(a, h, lane, nreg, new_pg, new_off, ok, nt_stage);
+      new_token_encode<KBF16>(a, h, lane, nreg, new_pg, new_off, ok, nt_stage, basis_dyn);
       if (ok) new_token_update<KBF16>(nt_stage, q_lds, q_descale, lane, ln, st);
     }
   }
@@ -764,26 +780,26 @@ hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, const uint16_t*
   a.n_splits = plan.n_splits;
   a.k_flags = L.k_flags;
   a.sm_scale = sm_scale;
+  a.basis = L.k_basis;
   const dim3 grid(plan.n_splits, L.num_kv_heads, B);
   const dim3 block(64 * plan.waves);
   const bool bf = L.k_fmt == NVKV_FMT_BF16;
-  if (plan.append) {
-    if (bf) {
-      if (plan.pipe2) hipLaunchKernelGGL((k_decode<true, true, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((k_decode<true, false, true>), grid, block, 0, stream, a);
-    } else {
-      if (plan.pipe2) hipLaunchKernelGGL((k_decode<false, true, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((k_decode<false, false, true>), grid, block, 0, stream, a);
-    }
-  } else {
-    if (bf) {
-      if (plan.pipe2) hipLaunchKernelGGL((k_decode<true, true, false>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((k_decode<true, false, false>), grid, block, 0, stream, a);
-    } else {
-      if (plan.pipe2) hipLaunchKernelGGL((k_decode<false, true, false>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((k_decode<false, false, false>), grid, block, 0, stream, a);
-    }
+  using Kernel = void (*)(DecodeArgs);
+  Kernel kern;
+  if (plan.append)
+    kern = bf ? (plan.pipe2 ? k_decode<true, true, true> : k_decode<true, false, true>)
+              : (plan.pipe2 ? k_decode<false, true, true> : k_decode<false, false, true>);
+  else
+    kern = bf ? (plan.pipe2 ? k_decode<true, true, false> : k_decode<true, false, false>)
+              : (plan.pipe2 ? k_decode<false, true, false> : k_decode<false, false, false>);
+  // the KLT key basis of the workgroup's head is staged in dynamic LDS
+  const size_t dyn_lds = (!bf && (L.k_flags & NVKV_K_KLT)) ? kBasisFloats * sizeof(float) : 0;
+  if (dyn_lds) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(dyn_lds));
+    if (e != hipSuccess) return e;
   }
+  hipLaunchKernelGGL(kern, grid, block, dyn_lds, stream, a);
   return hipGetLastError();
 }
 

@@ -20,6 +20,12 @@ hipError_t launch_calibrate(const uint16_t* k_win, const uint16_t* v_win, int32_
                             int32_t exclude_pos0, uint32_t k_flags, float* s_out, float* r_out, float* g_out,
                             hipStream_t stream);
 
+// Static per-head KLT basis and g_K (workspace: fp64 covariance and eigenvectors per head).
+size_t klt_workspace_bytes(int32_t hkv);
+hipError_t launch_calibrate_basis(const uint16_t* k_win, int32_t W, int32_t T, int32_t hkv, int32_t exclude_pos0,
+                                  uint32_t k_flags, const float* r, float* basis_out, float* g_out, void* workspace,
+                                  hipStream_t stream);
+
 // Decode split plan: number of splits and tokens per split for a call.
 struct DecodePlan {
   int32_t split_tokens;   // tokens handled by one workgroup (multiple of 32)

@@ -29,6 +29,7 @@
 // (nvkv_tiles.hpp); tiles are processed longest first (the last query positions).
 #include "nvkv_device.hpp"
 #include "nvkv_internal.hpp"
+#include "nvkv_klt.hpp"
 #include "nvkv_tiles.hpp"
 
 namespace nvkv {
@@ -49,6 +50,7 @@ struct PrefillArgs {
   int32_t tq;                 // query positions per sequence
   uint32_t k_flags;
   float sm_scale;
+  const float* basis;         // KLT basis [Hkv][128][128] (NVKV_K_KLT)
 };
 
 constexpr int kPfPos = 8;                   // query positions per workgroup
@@ -119,6 +121,7 @@ template <int NT>
 union PfSmem {
   PfLoopSmem<NT> loop;
   PfMergeSmem merge;
+  float basis[NT == 2 ? kBasisFloats : 4];    // KLT key basis, query prologue only (NVFP4 keys)
 };
 
 
@@ -297,6 +300,11 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn(PrefillArgs a) {
   const const_i32_ptr ptab = __builtin_bit_cast(const_i32_ptr, a.page_table) + static_cast<int64_t>(b) * a.max_pages_per_seq;
 
   // ---- query prologue: wavefront w prepares rows 8w..8w+7 (row R = 4 * position + head) ----
+  const bool klt = !KBF16 && (a.k_flags & NVKV_K_KLT);
+  if (klt) {                                 // the KLT basis shares the bytes of the loop buffers
+    load_basis_lds(a.basis + static_cast<int64_t>(h) * kBasisFloats, sm.basis, threadIdx.x, 64 * kPfWaves);
+    __syncthreads();
+  }
   {
     float2 sv = make_float2(1.0f, 1.0f);
     if (!KBF16 && (a.k_flags & NVKV_K_SMOOTH)) sv = reinterpret_cast<const float2*>(a.smooth + h * kHeadDim)[lane];
@@ -311,18 +319,23 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn(PrefillArgs a) {
         qw[k] = reinterpret_cast<const uint32_t*>(
             a.q + ((static_cast<int64_t>(b) * a.tq + i) * a.hq + 4 * h + (R & 3)) * kHeadDim)[lane];
     }
+    uint32_t w[8][3];
+    float descale[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      descale[k] = query_terms<KBF16>(qw[k], sv, a.k_flags, a.sm_scale, gk, lane, w[k][0], w[k][1], w[k][2],
+                                      sm.basis);
+    if (klt) __syncthreads();               // every wavefront is done with the basis
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int R = 8 * wave + k;
-      uint32_t w[3];
-      const float descale = query_terms<KBF16>(qw[k], sv, a.k_flags, a.sm_scale, gk, lane, w[0], w[1], w[2]);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int d = 2 * lane;                                  // dims d, d + 1
         const int gg = d >> 5, uu = (d & 31) >> 3, ww = (d & 7) >> 1;
-        reinterpret_cast<uint32_t*>(&sm.loop.qa[R >> 4][t][uu][(R & 15) + 16 * gg])[ww] = w[t];
+        reinterpret_cast<uint32_t*>(&sm.loop.qa[R >> 4][t][uu][(R & 15) + 16 * gg])[ww] = w[k][t];
       }
-      if (lane == 0) sm.loop.desc[R] = descale;
+      if (lane == 0) sm.loop.desc[R] = descale[k];
     }
   }
   __syncthreads();
@@ -429,6 +442,7 @@ hipError_t launch_prefill_attention(const nvkv_layer& L, const uint16_t* q, int3
   a.tq = Tq;
   a.k_flags = L.k_flags;
   a.sm_scale = sm_scale;
+  a.basis = L.k_basis;
   const dim3 grid((Tq + kPfPos - 1) / kPfPos, L.num_kv_heads, B);
   const dim3 block(64 * kPfWaves);
   if (L.k_fmt == NVKV_FMT_BF16)

@@ -13,6 +13,7 @@
 // traffic is the Hadamard butterfly's three block-pair stages.
 #include "nvkv_encode.hpp"
 #include "nvkv_internal.hpp"
+#include "nvkv_klt.hpp"
 
 namespace nvkv {
 
@@ -35,6 +36,7 @@ struct AppendArgs {
   uint32_t flags;             // key transform flags (0 for V)
   int32_t fmt;                // NVKV_FMT_*
   int32_t quad_words;         // 1: codes in the quad-interleaved word layout (NVFP4 values)
+  const float* basis;         // KLT basis [Hkv][128][128] (keys with NVKV_K_KLT), else unused
 };
 
 struct AppendPair {
@@ -65,14 +67,22 @@ __device__ __forceinline__ int32_t append_slot(const AppendPair& p, int n) {
 
 // grid: x = token chunks of kTokPerWg, y = KV head (y < Hkv: keys, else values).  MSE:
 // compiled with the key block-scale search (which needs more registers than the plain
-// encoder, so the plain launch does not carry it).
-template <bool MSE>
+// encoder, so the plain launch does not carry it).  KLT: compiled with the key basis
+// rotation (the head's basis in LDS, each wavefront's 8 rows staged in LDS).
+template <bool MSE, bool KLT>
 __global__ void __launch_bounds__(256) k_quantize_append(AppendPair p) {
   const int which = static_cast<int>(blockIdx.y) >= p.hkv ? 1 : 0;
   const AppendArgs a = which ? p.a[1] : p.a[0];   // uniform select, no dynamic indexing
   const int h = static_cast<int>(blockIdx.y) - (which ? p.hkv : 0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int blk = lane >> 3, tok = lane & 7;
+  __shared__ __attribute__((aligned(16))) float basis_lds[KLT ? kBasisFloats : 4];
+  __shared__ __attribute__((aligned(16))) float row_lds[KLT ? kAppendWaves : 1][KLT ? kTokPerPass : 1][kHeadDim];
+  const bool klt = KLT && a.fmt != NVKV_FMT_BF16 && (a.flags & NVKV_K_KLT);   // uniform per workgroup
+  if constexpr (KLT) {
+    if (klt) load_basis_lds(a.basis + static_cast<int64_t>(h) * kBasisFloats, basis_lds, threadIdx.x, 256);
+    __syncthreads();
+  }
   const bool smooth = a.fmt != NVKV_FMT_BF16 && (a.flags & 1u);
   float r[kBlock];
   if (smooth) {
@@ -118,6 +128,14 @@ __global__ void __launch_bounds__(256) k_quantize_append(AppendPair p) {
       for (int i = 0; i < kBlock; ++i) y[i] = y[i] * r[i];
     }
     if (a.flags & 2u) hadamard_row<8>(y, blk);
+    if constexpr (KLT) {
+      if (klt) {   // z = B^T y: the row through LDS, this lane's 16 outputs in the fixed order
+        float4* dst = reinterpret_cast<float4*>(&row_lds[wave][tok][blk * kBlock]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[q] = make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
+        rotate_cols<kBlock>(basis_lds, row_lds[wave][tok], blk * kBlock, y);
+      }
+    }
     uint32_t lo, hi;
     const uint32_t S = (MSE && (a.flags & NVKV_K_MSE_SCALE)) ? encode_block_mse(y, gsc, lo, hi)
                                                              : encode_block(y, gsc, lo, hi);
@@ -232,9 +250,9 @@ hipError_t launch_quantize_append_rows(const nvkv_layer& L, const uint16_t* k_ne
                                        hipStream_t stream) {
   AppendPair p{};
   p.a[0] = AppendArgs{k_new, static_cast<uint8_t*>(L.k_data), L.k_scales, L.k_inv_smooth, L.global_scale + 0,
-                      L.k_fmt == NVKV_FMT_NVFP4 ? L.k_flags : 0u, L.k_fmt, 0};
+                      L.k_fmt == NVKV_FMT_NVFP4 ? L.k_flags : 0u, L.k_fmt, 0, L.k_basis};
   p.a[1] = AppendArgs{v_new, static_cast<uint8_t*>(L.v_data), L.v_scales, nullptr, L.global_scale + 1, 0u,
-                      L.v_fmt, 1};
+                      L.v_fmt, 1, nullptr};
   p.slots = slots;
   p.page_table = page_table;
   p.seq_lens = seq_lens;
@@ -245,10 +263,11 @@ hipError_t launch_quantize_append_rows(const nvkv_layer& L, const uint16_t* k_ne
   p.page_size = L.page_size;
   p.max_slot = static_cast<int64_t>(L.num_pages) * L.page_size;
   const dim3 grid((N + kTokPerWg - 1) / kTokPerWg, 2 * L.num_kv_heads);
-  if (p.a[0].flags & NVKV_K_MSE_SCALE)
-    hipLaunchKernelGGL(k_quantize_append<true>, grid, dim3(64 * kAppendWaves), 0, stream, p);
-  else
-    hipLaunchKernelGGL(k_quantize_append<false>, grid, dim3(64 * kAppendWaves), 0, stream, p);
+  const bool mse = p.a[0].flags & NVKV_K_MSE_SCALE, klt = p.a[0].flags & NVKV_K_KLT;
+  using Kernel = void (*)(AppendPair);
+  const Kernel kern = klt ? (mse ? k_quantize_append<true, true> : k_quantize_append<false, true>)
+                          : (mse ? k_quantize_append<true, false> : k_quantize_append<false, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * kAppendWaves), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -259,8 +278,9 @@ hipError_t launch_calibrate(const uint16_t* k_win, const uint16_t* v_win, int32_
   uint32_t* s_bits = reinterpret_cast<uint32_t*>(s_out);
   uint32_t* g_bits = reinterpret_cast<uint32_t*>(g_out);
   const int do_k = k_win != nullptr, do_v = v_win != nullptr;
+  const int do_gk = do_k && !(k_flags & NVKV_K_KLT);     // with the KLT basis, g_K comes after the basis
   hipLaunchKernelGGL(k_calib_clear, dim3((C + 255) / 256), dim3(256), 0, stream, s_bits, do_k ? C : 0, g_bits,
-                     do_k, do_v);
+                     do_gk, do_v);
   const int64_t rows = static_cast<int64_t>(W) * T * hkv;
   const int64_t wg_rows = (rows + kRowsPerWg - 1) / kRowsPerWg;
   if (do_k) {
@@ -268,14 +288,15 @@ hipError_t launch_calibrate(const uint16_t* k_win, const uint16_t* v_win, int32_
     hipLaunchKernelGGL(k_calib_channel_absmax, dim3((T + kCalibTokChunk - 1) / kCalibTokChunk, W), dim3(256), 0,
                        stream, k_win, T, hkv, t_begin, s_bits);
     hipLaunchKernelGGL(k_calib_finalize_sr, dim3((C + 255) / 256), dim3(256), 0, stream, s_out, r_out, C);
-    hipLaunchKernelGGL(k_calib_transform_amax, dim3(static_cast<unsigned>(wg_rows)), dim3(256), 0, stream, k_win,
-                       rows, hkv, r_out, k_flags, g_bits + 0);
+    if (do_gk)
+      hipLaunchKernelGGL(k_calib_transform_amax, dim3(static_cast<unsigned>(wg_rows)), dim3(256), 0, stream, k_win,
+                         rows, hkv, r_out, k_flags, g_bits + 0);
   }
   if (do_v) {
     hipLaunchKernelGGL(k_calib_transform_amax, dim3(static_cast<unsigned>(wg_rows)), dim3(256), 0, stream, v_win,
                        rows, hkv, nullptr, 0u, g_bits + 1);
   }
-  hipLaunchKernelGGL(k_calib_finalize_g, dim3(1), dim3(64), 0, stream, g_out, do_k, do_v);
+  hipLaunchKernelGGL(k_calib_finalize_g, dim3(1), dim3(64), 0, stream, g_out, do_gk, do_v);
   return hipGetLastError();
 }
 

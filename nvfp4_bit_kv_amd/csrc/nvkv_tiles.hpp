@@ -224,10 +224,13 @@ __device__ __forceinline__ void valid_tokens(const HalfBase (&hb)[2], int t0, in
 // into exact operand terms: NVFP4 keys -- a power-of-two prescale 2^p2 puts max |q'| in
 // [2^13, 2^14) and two fp16 terms (hi, lo) keep ~22 bits; BF16 keys -- three bf16 terms.
 // w0..w2 receive the terms of the lane's two dims (w2 = 0 for fp16); returns the descale
-// 2^-p2 to apply to the scores.
+// 2^-p2 to apply to the scores.  With the KLT key basis ([cache post] table rows "static
+// per-head KLT"), q' = B^T (q * s) with the head's basis B in LDS (basis_lds, fp32
+// [128][128]); this side of the scores is not an encoding step, so it rounds in any order.
 template <bool KBF16>
 __device__ __forceinline__ float query_terms(uint32_t qw, float2 sv, uint32_t k_flags, float sm_scale, float gk,
-                                           int lane, uint32_t& w0, uint32_t& w1, uint32_t& w2) {
+                                           int lane, uint32_t& w0, uint32_t& w1, uint32_t& w2,
+                                           const float* basis_lds = nullptr) {
   float x0 = bf16_to_f32(qw & 0xFFFFu), x1 = bf16_to_f32(qw >> 16);
   float scale = sm_scale * kLog2e;
   if (!KBF16) {
@@ -245,6 +248,18 @@ __device__ __forceinline__ float query_terms(uint32_t qw, float2 sv, uint32_t k_
         x1 = up ? p1 - x1 : x1 + p1;
       }
       scale *= (1.0f / 128.0f);
+    }
+    if (k_flags & NVKV_K_KLT) {        // lane l: outputs 2l, 2l + 1; input j from lane j / 2
+      float y0 = 0.0f, y1 = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kHeadDim; ++j) {
+        const float qj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int((j & 1) ? x1 : x0), j >> 1));
+        const float2 bj = *reinterpret_cast<const float2*>(basis_lds + j * kHeadDim + 2 * lane);
+        y0 = __builtin_fmaf(bj.x, qj, y0);
+        y1 = __builtin_fmaf(bj.y, qj, y1);
+      }
+      x0 = y0;
+      x1 = y1;
     }
     scale *= gk;
   }

@@ -28,7 +28,7 @@ def clib():
 
 def test_every_declared_symbol_is_exported(clib):
     decl = _declared_symbols()
-    assert len(decl) == 10, decl
+    assert len(decl) == 12, decl
     assert sorted(decl) == sorted(nk.EXPORTED)
     for name in decl:
         assert hasattr(clib, name), name
@@ -68,7 +68,8 @@ def _layer(**kw):
 BAD_LAYERS = [
     (dict(head_dim=64), 2), (dict(num_kv_heads=0), 2), (dict(page_size=24), 2), (dict(page_size=0), 2),
     (dict(num_pages=0), 2), (dict(reserved=1), 2), (dict(k_fmt=7), 3), (dict(v_fmt=0), 3),
-    (dict(k_flags=8), 3), (dict(k_fmt=0, k_flags=1), 3), (dict(k_fmt=0, k_flags=4), 3), (dict(k_data=None), 1),
+    (dict(k_flags=16), 3), (dict(k_fmt=0, k_flags=1), 3), (dict(k_fmt=0, k_flags=4), 3), (dict(k_data=None), 1),
+    (dict(k_flags=10, k_basis=0x3000), 3), (dict(k_flags=9), 1), (dict(k_fmt=0, k_flags=8, k_basis=0x3000), 3),
     (dict(v_scales=None), 1),
     (dict(k_scales=None), 1), (dict(k_smooth=None), 1), (dict(k_inv_smooth=None), 1),
     (dict(global_scale=None), 1),
@@ -160,8 +161,30 @@ def test_calibrate_argument_errors(clib):
     assert f(0x10, None, 0, 8, 2, 1, 1, 0x10, 0x10, 0x10, None) == 2
     assert f(0x10, None, 4, 0, 2, 1, 1, 0x10, 0x10, 0x10, None) == 2
     assert f(0x10, None, 4, 8, 0, 1, 1, 0x10, 0x10, 0x10, None) == 2
-    assert f(0x10, None, 4, 8, 2, 1, 8, 0x10, 0x10, 0x10, None) == 3
+    assert f(0x10, None, 4, 8, 2, 1, 16, 0x10, 0x10, 0x10, None) == 3
+    assert f(0x10, None, 4, 8, 2, 1, 10, 0x10, 0x10, 0x10, None) == 3
     assert f(0x10, None, 4, 1 << 28, 8, 1, 1, 0x10, 0x10, 0x10, None) == 2
+
+
+def test_calibrate_key_basis_argument_errors(clib):
+    f = clib.nvkv_calibrate_key_basis
+    wsb = clib.nvkv_calibrate_key_basis_workspace_bytes(2)
+    assert wsb == 2 * 128 * 128 * 8 * 2
+    assert clib.nvkv_calibrate_key_basis_workspace_bytes(0) == 0
+    ws = 0x100000
+    assert f(None, 4, 8, 2, 1, 9, 0x10, 0x10, 0x10, ws, wsb, None) == 1          # k_win
+    assert f(0x10, 4, 8, 2, 1, 9, 0x10, None, 0x10, ws, wsb, None) == 1          # basis_out
+    assert f(0x10, 4, 8, 2, 1, 9, 0x10, 0x10, None, ws, wsb, None) == 1          # g_out
+    assert f(0x10, 4, 8, 2, 1, 9, None, 0x10, 0x10, ws, wsb, None) == 1          # r with smoothing
+    assert f(0x10, 0, 8, 2, 1, 9, 0x10, 0x10, 0x10, ws, wsb, None) == 2
+    assert f(0x10, 4, 1, 2, 1, 9, 0x10, 0x10, 0x10, ws, wsb, None) == 2          # T >= 2
+    assert f(0x10, 4, 8, 0, 1, 9, 0x10, 0x10, 0x10, ws, wsb, None) == 2
+    assert f(0x10, 4, 8, 2, 1, 1, 0x10, 0x10, 0x10, ws, wsb, None) == 3          # no KLT bit
+    assert f(0x10, 4, 8, 2, 1, 10, 0x10, 0x10, 0x10, ws, wsb, None) == 3         # with Hadamard
+    assert f(0x10, 4, 8, 2, 1, 24, 0x10, 0x10, 0x10, ws, wsb, None) == 3         # unknown bit
+    assert f(0x10, 4, 8, 2, 1, 9, 0x10, 0x10, 0x10, None, wsb, None) == 4        # workspace
+    assert f(0x10, 4, 8, 2, 1, 9, 0x10, 0x10, 0x10, ws, wsb - 1, None) == 4
+    assert f(0x10, 4, 8, 2, 1, 9, 0x10, 0x10, 0x10, ws + 16, wsb, None) == 4     # alignment
 
 
 def test_product_path_has_no_fallback(tmp_path):

@@ -42,13 +42,16 @@ def gpu_calibrate(nk, kw, vw, hkv, flags, exclude_pos0=True):
     return s, r, g
 
 
-def gpu_fill_cache(nk, k, v, hkv, flags, pages, s, r, g, k_fmt=1, chunk=None):
-    """Append every token of every sequence; returns the CacheLayer."""
+def gpu_fill_cache(nk, k, v, hkv, flags, pages, s, r, g, k_fmt=1, chunk=None, basis=None):
+    """Append every token of every sequence; returns the CacheLayer.  basis: the KLT key
+    basis to install (flags with NVKV_K_KLT)."""
     B, T = k.shape[0], k.shape[1]
     cache = nk.CacheLayer(pages.num_pages, pages.page_size, hkv, k_fmt=k_fmt, k_flags=flags if k_fmt == 1 else 0)
     cache.smooth.copy_(s)
     cache.inv_smooth.copy_(r)
-    cache.gscale.copy_(g)
+    cache.gscale.copy_(torch.as_tensor(g))
+    if basis is not None:
+        cache.basis.copy_(torch.as_tensor(basis))
     L = cache.struct()
     slots = np.concatenate([pages.slots(b, 0, T) for b in range(B)])
     kk = k.reshape(B * T, hkv, 128)
