@@ -291,25 +291,20 @@ __device__ __forceinline__ void had_cross(float (&y)[4], int lane, int m) {
   }
 }
 
-// Encode the new token (the transform and encoder of quantize_append_kv, four elements per
-// lane): the LDS stage receives it as token 0 of a 16-token block in the cache layouts, and
-// the cache slot too when its page is in range (page pg, offset off).
+// Transform of the new token's key row (the key transform of quantize_append_kv, four
+// elements per lane): lane L < 32 leaves elements 4L .. 4L + 3 of the transformed key in y;
+// lanes >= 32 leave their value elements untouched.  The whole wavefront takes part (the
+// Hadamard butterfly and the KLT rotation are cross-lane).
 template <bool KBF16>
-__device__ __forceinline__ void new_token_encode(const DecodeArgs& a, int h, int lane, const NewTokenRegs& R,
-                                                 int32_t pg, int off, bool ok, NewTokenStage& st,
-                                                 const float* basis_lds) {
+__device__ __forceinline__ void new_token_transform(const DecodeArgs& a, int lane, const NewTokenRegs& R,
+                                                    NewTokenStage& st, const float* basis_lds, float (&y)[4]) {
 #pragma clang fp contract(off)   // part of the bit-exact key transform
   const bool is_v = lane >= 32;
-  const int blk = (lane >> 2) & 7, qtr = lane & 3;
-  const int64_t ph = static_cast<int64_t>(ok ? pg : 0) * a.hkv + h;
-  const int64_t row_index = ph * a.page_size + off;
-  if (KBF16 && !is_v) {                                   // bf16 keys: plain copy of the row
-    *reinterpret_cast<uint2*>(st.kc + 8 * (lane & 31)) = R.raw;
-    if (ok) *reinterpret_cast<uint2*>(a.k_codes_w + row_index * (kHeadDim * 2) + 8 * (lane & 31)) = R.raw;
-    return;
-  }
-  float y[4] = {bf16_to_f32(R.raw.x & 0xFFFFu), bf16_to_f32(R.raw.x >> 16), bf16_to_f32(R.raw.y & 0xFFFFu),
-                bf16_to_f32(R.raw.y >> 16)};
+  y[0] = bf16_to_f32(R.raw.x & 0xFFFFu);
+  y[1] = bf16_to_f32(R.raw.x >> 16);
+  y[2] = bf16_to_f32(R.raw.y & 0xFFFFu);
+  y[3] = bf16_to_f32(R.raw.y >> 16);
+  if (KBF16) return;
   if (!is_v && (a.k_flags & NVKV_K_SMOOTH)) {             // y_j = fl32(x_j * r_j)
     y[0] = y[0] * R.r.x;
     y[1] = y[1] * R.r.y;
@@ -328,11 +323,50 @@ __device__ __forceinline__ void new_token_encode(const DecodeArgs& a, int h, int
     had_cross(y, lane, 8);                                // h = 32
     had_cross(y, lane, 16);                               // h = 64
   }
-  if (!KBF16 && (a.k_flags & NVKV_K_KLT)) {
-    // z = B^T y in the fixed rounding order of the append kernel: the key row through LDS,
-    // key lane L computes z[4L .. 4L+3]
+  if (a.k_flags & NVKV_K_KLT) {
+    // z = B^T y in the fixed rounding order of the append kernel (each output a sequential
+    // sum over j of rounded products), on the whole wavefront: the key row goes through LDS,
+    // lane l forms z[2l] and z[2l + 1], and key lane L then reads back z[4L .. 4L + 3]
     if (!is_v) *reinterpret_cast<float4*>(&st.ky[4 * (lane & 31)]) = make_float4(y[0], y[1], y[2], y[3]);
-    if (!is_v) rotate_cols<4>(basis_lds, st.ky, 4 * (lane & 31), y);
+    float z0 = 0.0f, z1 = 0.0f;
+#pragma unroll 4
+    for (int j4 = 0; j4 < kHeadDim / 4; ++j4) {
+      const float4 y4 = *reinterpret_cast<const float4*>(&st.ky[4 * j4]);
+      const float yv[4] = {y4.x, y4.y, y4.z, y4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float2 bj = *reinterpret_cast<const float2*>(basis_lds + (4 * j4 + u) * kHeadDim + 2 * lane);
+        z0 = z0 + bj.x * yv[u];
+        z1 = z1 + bj.y * yv[u];
+      }
+    }
+    *reinterpret_cast<float2*>(&st.ky[2 * lane]) = make_float2(z0, z1);
+    const float4 zk = *reinterpret_cast<const float4*>(&st.ky[4 * (lane & 31)]);
+    if (!is_v) {
+      y[0] = zk.x;
+      y[1] = zk.y;
+      y[2] = zk.z;
+      y[3] = zk.w;
+    }
+  }
+}
+
+// Encode the new token from its transformed rows y (new_token_transform): the LDS stage
+// receives it as token 0 of a 16-token block in the cache layouts, and the cache slot too
+// when its page is in range (page pg, offset off).
+template <bool KBF16>
+__device__ __forceinline__ void new_token_encode(const DecodeArgs& a, int h, int lane, const NewTokenRegs& R,
+                                                 const float (&y)[4], int32_t pg, int off, bool ok,
+                                                 NewTokenStage& st) {
+#pragma clang fp contract(off)
+  const bool is_v = lane >= 32;
+  const int blk = (lane >> 2) & 7, qtr = lane & 3;
+  const int64_t ph = static_cast<int64_t>(ok ? pg : 0) * a.hkv + h;
+  const int64_t row_index = ph * a.page_size + off;
+  if (KBF16 && !is_v) {                                   // bf16 keys: plain copy of the row
+    *reinterpret_cast<uint2*>(st.kc + 8 * (lane & 31)) = R.raw;
+    if (ok) *reinterpret_cast<uint2*>(a.k_codes_w + row_index * (kHeadDim * 2) + 8 * (lane & 31)) = R.raw;
+    return;
   }
   // block absmax over the block's four lanes, scale code, E2M1 nibbles
   float A = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
@@ -444,7 +478,9 @@ __device__ __forceinline__ void new_token_update(const NewTokenStage& st, const 
 // holds position seq_len - 1 it quantises the new token into its cache slot and an LDS stage
 // once the query prologue is done and adds the token to its own softmax state; the cache
 // wavefronts read the split without that position.
-template <bool KBF16, bool PIPE2, bool APPEND>
+// KLT: compiled with the KLT key basis (basis staging and both rotations); the other
+// instances carry none of that code.
+template <bool KBF16, bool PIPE2, bool APPEND, bool KLT>
 __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -473,11 +509,13 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   const int64_t unit = static_cast<int64_t>(b) * a.hkv + h;
   const const_i32_ptr ptab = __builtin_bit_cast(const_i32_ptr, a.page_table) + static_cast<int64_t>(b) * a.max_pages_per_seq;
 
-  // KLT key basis of this head into dynamic LDS by every thread; its loads go out before the
-  // cache loads, so waiting for them does not wait for the cache
+  // KLT key basis of this head into dynamic LDS (followed by a 128-float slot per query
+  // wavefront for the rotation) by the four query wavefronts, a quarter each;
+  // their loads go out before their cache loads, so waiting for them does not wait for the
+  // cache, and the other wavefronts issue their cache loads at once
   extern __shared__ __attribute__((aligned(16))) float basis_dyn[];
-  const bool klt = !KBF16 && (a.k_flags & NVKV_K_KLT);
-  if (klt) load_basis_lds_x4(a.basis + static_cast<int64_t>(h) * kBasisFloats, basis_dyn, tid, blockDim.x);
+  const bool klt = KLT && !KBF16 && (a.k_flags & NVKV_K_KLT);
+  if (klt && wave < 4) load_basis_quarter(a.basis + static_cast<int64_t>(h) * kBasisFloats, basis_dyn, wave, lane);
 
   // ---- start every independent memory access first: query row, sequence length, pages ----
   const bool q_wave = wave < 4;                 // wavefronts 0..3 prepare query heads 4h..4h+3
@@ -532,9 +570,15 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
 
   // ---------------- query prologue: wavefront w < 4 prepares query head 4h + w ----------------
   if (klt) __syncthreads();                    // the basis is in LDS
+  // the new token's key transform: with the KLT rotation the idle extra wavefront does it
+  // during the query prologue, otherwise after it
+  float ny[4];
+  const bool nt_early = klt && owns_new && app_wave;
+  if (nt_early) new_token_transform<KBF16>(a, lane, nreg, nt_stage, basis_dyn, ny);
   if (!empty && q_wave) {
     uint32_t w0, w1, w2;
-    const float descale = query_terms<KBF16>(qw, sv, a.k_flags, a.sm_scale, gk, lane, w0, w1, w2, basis_dyn);
+    const float descale = query_terms<KBF16>(qw, sv, a.k_flags, a.sm_scale, gk, lane, w0, w1, w2, basis_dyn,
+                                                  basis_dyn + kBasisFloats + (wave & 3) * kHeadDim);
     reinterpret_cast<uint32_t*>(q_lds[wave][0])[lane] = w0;
     reinterpret_cast<uint32_t*>(q_lds[wave][1])[lane] = w1;
     reinterpret_cast<uint32_t*>(q_lds[wave][2])[lane] = w2;
@@ -597,7 +641,8 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
     }
     if (owns_new && app_wave) {
       const bool ok = static_cast<uint32_t>(new_pg) < static_cast<uint32_t>(a.num_pages);
-      new_token_encode<KBF16>(a, h, lane, nreg, new_pg, new_off, ok, nt_stage, basis_dyn);
+      if (!nt_early) new_token_transform<KBF16>(a, lane, nreg, nt_stage, basis_dyn, ny);
+      new_token_encode<KBF16>(a, h, lane, nreg, ny, new_pg, new_off, ok, nt_stage);
       if (ok) new_token_update<KBF16>(nt_stage, q_lds, q_descale, lane, ln, st);
     }
   }
@@ -785,15 +830,20 @@ hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, const uint16_t*
   const dim3 block(64 * plan.waves);
   const bool bf = L.k_fmt == NVKV_FMT_BF16;
   using Kernel = void (*)(DecodeArgs);
+  const bool klt = !bf && (L.k_flags & NVKV_K_KLT);
   Kernel kern;
-  if (plan.append)
-    kern = bf ? (plan.pipe2 ? k_decode<true, true, true> : k_decode<true, false, true>)
-              : (plan.pipe2 ? k_decode<false, true, true> : k_decode<false, false, true>);
-  else
-    kern = bf ? (plan.pipe2 ? k_decode<true, true, false> : k_decode<true, false, false>)
-              : (plan.pipe2 ? k_decode<false, true, false> : k_decode<false, false, false>);
+  if (klt) {
+    if (plan.append) kern = plan.pipe2 ? k_decode<false, true, true, true> : k_decode<false, false, true, true>;
+    else kern = plan.pipe2 ? k_decode<false, true, false, true> : k_decode<false, false, false, true>;
+  } else if (plan.append) {
+    kern = bf ? (plan.pipe2 ? k_decode<true, true, true, false> : k_decode<true, false, true, false>)
+              : (plan.pipe2 ? k_decode<false, true, true, false> : k_decode<false, false, true, false>);
+  } else {
+    kern = bf ? (plan.pipe2 ? k_decode<true, true, false, false> : k_decode<true, false, false, false>)
+              : (plan.pipe2 ? k_decode<false, true, false, false> : k_decode<false, false, false, false>);
+  }
   // the KLT key basis of the workgroup's head is staged in dynamic LDS
-  const size_t dyn_lds = (!bf && (L.k_flags & NVKV_K_KLT)) ? kBasisFloats * sizeof(float) : 0;
+  const size_t dyn_lds = klt ? (kBasisFloats + 4 * kHeadDim) * sizeof(float) : 0;
   if (dyn_lds) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(dyn_lds));

@@ -23,25 +23,17 @@ __device__ __forceinline__ void load_basis_lds(const float* __restrict__ basis_h
   for (int i = tid; i < kBasisFloats / 4; i += nthreads) dst[i] = src[i];
 }
 
-// The same copy with four loads of a thread in flight before its stores (one memory latency
-// per 4 * nthreads float4 instead of one per nthreads).
-__device__ __forceinline__ void load_basis_lds_x4(const float* __restrict__ basis_h, float* lds, int tid,
-                                                  int nthreads) {
-  const float4* src = reinterpret_cast<const float4*>(basis_h);
-  float4* dst = reinterpret_cast<float4*>(lds);
-  for (int i0 = tid; i0 < kBasisFloats / 4; i0 += 4 * nthreads) {
-    float4 v[4];
+// One wavefront copies a quarter of the basis (rows 32q .. 32q+31), all 16 of each lane's
+// loads issued before its stores.
+__device__ __forceinline__ void load_basis_quarter(const float* __restrict__ basis_h, float* lds, int quarter,
+                                                   int lane) {
+  const float4* src = reinterpret_cast<const float4*>(basis_h) + quarter * (kBasisFloats / 16);
+  float4* dst = reinterpret_cast<float4*>(lds) + quarter * (kBasisFloats / 16);
+  float4 v[16];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = i0 + k * nthreads;
-      v[k] = src[i < kBasisFloats / 4 ? i : 0];
-    }
+  for (int k = 0; k < 16; ++k) v[k] = src[64 * k + lane];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = i0 + k * nthreads;
-      if (i < kBasisFloats / 4) dst[i] = v[k];
-    }
-  }
+  for (int k = 0; k < 16; ++k) dst[64 * k + lane] = v[k];
 }
 
 // z_k = sum over j = 0..127 of fl32(B[j][c0 + k] * row[j]), k < N (a multiple of 4, c0 a

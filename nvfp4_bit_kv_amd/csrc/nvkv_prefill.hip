@@ -291,6 +291,7 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn(PrefillArgs a) {
   ln.vs_off = static_cast<uint32_t>(32 * g + 4 * (c >> 1));
 
   __shared__ __attribute__((aligned(16))) PfSmem<NT> sm;
+  __shared__ __attribute__((aligned(16))) float q_rot[KBF16 ? 1 : kPfWaves][KBF16 ? 4 : kHeadDim];   // KLT rows
 
   int n = a.seq_lens[b];
   n = n < 0 ? 0 : (n > a.seq_cap ? a.seq_cap : n);
@@ -324,7 +325,7 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn(PrefillArgs a) {
 #pragma unroll
     for (int k = 0; k < 8; ++k)
       descale[k] = query_terms<KBF16>(qw[k], sv, a.k_flags, a.sm_scale, gk, lane, w[k][0], w[k][1], w[k][2],
-                                      sm.basis);
+                                      sm.basis, q_rot[KBF16 ? 0 : wave]);
     if (klt) __syncthreads();               // every wavefront is done with the basis
 #pragma unroll
     for (int k = 0; k < 8; ++k) {

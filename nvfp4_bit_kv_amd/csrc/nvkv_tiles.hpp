@@ -230,7 +230,7 @@ __device__ __forceinline__ void valid_tokens(const HalfBase (&hb)[2], int t0, in
 template <bool KBF16>
 __device__ __forceinline__ float query_terms(uint32_t qw, float2 sv, uint32_t k_flags, float sm_scale, float gk,
                                            int lane, uint32_t& w0, uint32_t& w1, uint32_t& w2,
-                                           const float* basis_lds = nullptr) {
+                                           const float* basis_lds = nullptr, float* row_lds = nullptr) {
   float x0 = bf16_to_f32(qw & 0xFFFFu), x1 = bf16_to_f32(qw >> 16);
   float scale = sm_scale * kLog2e;
   if (!KBF16) {
@@ -249,17 +249,24 @@ __device__ __forceinline__ float query_terms(uint32_t qw, float2 sv, uint32_t k_
       }
       scale *= (1.0f / 128.0f);
     }
-    if (k_flags & NVKV_K_KLT) {        // lane l: outputs 2l, 2l + 1; input j from lane j / 2
-      float y0 = 0.0f, y1 = 0.0f;
+    if (k_flags & NVKV_K_KLT) {
+      // the row through this wavefront's LDS slot (row_lds, 128 floats); lane l forms outputs
+      // 2l, 2l + 1 as four interleaved partial sums each
+      *reinterpret_cast<float2*>(row_lds + 2 * lane) = make_float2(x0, x1);
+      float y0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, y1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+      for (int j4 = 0; j4 < kHeadDim / 4; ++j4) {
+        const float4 q4 = *reinterpret_cast<const float4*>(row_lds + 4 * j4);
+        const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
-      for (int j = 0; j < kHeadDim; ++j) {
-        const float qj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int((j & 1) ? x1 : x0), j >> 1));
-        const float2 bj = *reinterpret_cast<const float2*>(basis_lds + j * kHeadDim + 2 * lane);
-        y0 = __builtin_fmaf(bj.x, qj, y0);
-        y1 = __builtin_fmaf(bj.y, qj, y1);
+        for (int u = 0; u < 4; ++u) {
+          const float2 bj = *reinterpret_cast<const float2*>(basis_lds + (4 * j4 + u) * kHeadDim + 2 * lane);
+          y0[u] = __builtin_fmaf(bj.x, qv[u], y0[u]);
+          y1[u] = __builtin_fmaf(bj.y, qv[u], y1[u]);
+        }
       }
-      x0 = y0;
-      x1 = y1;
+      x0 = (y0[0] + y0[1]) + (y0[2] + y0[3]);
+      x1 = (y1[0] + y1[1]) + (y1[2] + y1[3]);
     }
     scale *= gk;
   }
