@@ -384,9 +384,9 @@ __device__ __forceinline__ void new_token_encode(const DecodeArgs& a, int h, int
   const float sigma = e4m3_value(S);
   uint32_t bits = 0u;
   if (sigma > 0.0f) {
-    const E2m1Thresholds t(sigma);
+    const E2m1Thresholds t(sigma, R.g);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bits |= e2m1_nibble(y[i], t, R.g) << (4 * i);
+    for (int i = 0; i < 4; ++i) bits |= e2m1_nibble(y[i], t) << (4 * i);
   }
   // word w = 2 blk + (qtr >> 1) holds elements 8w..8w+7: even quarters take the odd
   // neighbour's 16 bits as their high half

@@ -32,12 +32,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Value of a non-negative E4M3FN code 0..126, exact in fp32: (m/8 + [e > 0]) * 2^(max(e,1) - 7)
-// (one formula for normal and subnormal codes, so it compiles to straight-line code).
+// Value of a non-negative E4M3FN code 0..126, exact in fp32.  Normal codes (exponent field
+// e >= 1, mantissa m) are 2^(e-7) (1 + m/8): the fp32 pattern with exponent e + 120 and the
+// three mantissa bits on top, i.e. (c + 960) << 20.  Subnormal codes are m * 2^-9.
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t e = c >> 3, m = c & 7u;
-  const float frac = static_cast<float>(m) * 0.125f + (e ? 1.0f : 0.0f);
-  return __builtin_ldexpf(frac, static_cast<int>(e ? e : 1u) - 7);
+  const float sub = static_cast<float>(c) * 0x1p-9f;
+  const float nrm = __uint_as_float((c + 960u) << 20);
+  return c < 8u ? sub : nrm;
 }
 
 // Neighbours of a positive finite fp32 value (bit-pattern steps).

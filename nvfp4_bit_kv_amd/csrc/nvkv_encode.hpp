@@ -92,39 +92,73 @@ __device__ __forceinline__ uint32_t e4m3_scale_code(float A, float g) {
   return static_cast<uint32_t>(c + (up ? 1 : 0) - (down ? 1 : 0));
 }
 
-// Per-block E2M1 thresholds P_k = t_k * sigma (exact), t = midpoints of the magnitude grid
-// {0, .5, 1, 1.5, 2, 3, 4, 6}.
+// Per-block E2M1 decision bounds.  The midpoints of the magnitude grid {0, .5, 1, 1.5, 2,
+// 3, 4, 6} are t = .25, .75, 1.25, 1.75, 2.5, 3.5, 5, and the exact threshold of midpoint k is
+// T_k = t_k sigma g.  A tie goes to the even code: up at odd k (0.75, 1.75, 3.5: the value
+// passes when a >= T_k) and down at even k (it passes when a > T_k).  For an fp32 value a,
+// "a >= T" is "a >= RU(T)" and "a > T" is "a > RD(T)", with RU / RD the fp32 values next
+// above / below T (both T when T is an fp32 value; otherwise no fp32 value lies between them,
+// so neither comparison can meet T itself).  Each bound comes once per block from the rounded
+// product and the sign of its exact error (one FMA), so an element costs three plain compares.
+// Valid for products far above the fp32 subnormal range, as everywhere in this encoder.
+__device__ __forceinline__ float bound_rd(float P, float g) {
+#pragma clang fp contract(off)
+  const float p = P * g;
+  const float e = __builtin_fmaf(P, g, -p);                 // exact P*g - p
+  return e < 0.0f ? __uint_as_float(__float_as_uint(p) - 1u) : p;
+}
+__device__ __forceinline__ float bound_ru(float P, float g) {
+#pragma clang fp contract(off)
+  const float p = P * g;
+  const float e = __builtin_fmaf(P, g, -p);
+  return e > 0.0f ? __uint_as_float(__float_as_uint(p) + 1u) : p;
+}
+
 struct E2m1Thresholds {
-  float p0, p1, p2, p3, p4, p5, p6;
-  __device__ __forceinline__ explicit E2m1Thresholds(float sigma)
-      : p0(0.25f * sigma), p1(0.75f * sigma), p2(1.25f * sigma), p3(1.75f * sigma),
-        p4(2.5f * sigma), p5(3.5f * sigma), p6(5.0f * sigma) {
-    // keep the seven products in registers: left to itself the compiler re-forms them at
-    // every use and turns the threshold selects of all 16 elements into branches
-    asm volatile("" : "+v"(p0), "+v"(p1), "+v"(p2), "+v"(p3), "+v"(p4), "+v"(p5), "+v"(p6));
+  float u0, u1, u2, u3, u4, u5, u6;       // RD, RU, RD, RU, RD, RU, RD of T_0 .. T_6
+  __device__ __forceinline__ E2m1Thresholds(float sigma, float g)
+      : u0(bound_rd(0.25f * sigma, g)), u1(bound_ru(0.75f * sigma, g)), u2(bound_rd(1.25f * sigma, g)),
+        u3(bound_ru(1.75f * sigma, g)), u4(bound_rd(2.5f * sigma, g)), u5(bound_ru(3.5f * sigma, g)),
+        u6(bound_rd(5.0f * sigma, g)) {
+    // keep the seven bounds in registers: left to itself the compiler re-forms them at every
+    // use and turns the bound selects of all 16 elements into branches
+    asm volatile("" : "+v"(u0), "+v"(u1), "+v"(u2), "+v"(u3), "+v"(u4), "+v"(u5), "+v"(u6));
   }
 };
 
-// Signed E2M1 nibble of y in a block with scale sigma > 0 and tensor scale g: magnitude =
-// round-to-nearest (ties to the even code) of the exact |y|/(sigma g), saturating at 6;
-// a zero magnitude is stored as code 0.  Three exact comparisons (binary search).
-__device__ __forceinline__ uint32_t e2m1_nibble(float y, const E2m1Thresholds& t, float g) {
-#pragma clang fp contract(off)
-  const float a = fabsf(y);
-  const bool b2 = __builtin_fmaf(-t.p3, g, a) >= 0.0f;            // 1.75: tie -> code 4
-  // threshold choices as bit selects on all-ones / all-zero masks (nested conditional
+// E2M1 magnitude code (0..7) of a = |y| >= 0 in a block with scale sigma > 0: round to nearest
+// (ties to the even code) of the exact a/(sigma g), saturating at 6.  Binary search with the
+// comparison type of each level fixed (levels 1, 2: ties up, >=; level 3: ties down, >).
+__device__ __forceinline__ uint32_t e2m1_mag(float a, const E2m1Thresholds& t) {
+  const bool b2 = a >= t.u3;
+  // bound choices as bit selects on all-ones / all-zero masks (nested conditional
   // expressions are compiled to branches here)
   const uint32_t m2 = b2 ? 0xFFFFFFFFu : 0u;
-  const float t1 = __uint_as_float((__float_as_uint(t.p5) & m2) | (__float_as_uint(t.p1) & ~m2));  // 3.5 / 0.75: tie -> up
-  const bool b1 = __builtin_fmaf(-t1, g, a) >= 0.0f;
+  const float t1 = __uint_as_float((__float_as_uint(t.u5) & m2) | (__float_as_uint(t.u1) & ~m2));
+  const bool b1 = a >= t1;
   const uint32_t m1 = b1 ? 0xFFFFFFFFu : 0u;
-  const uint32_t hi2 = (__float_as_uint(t.p6) & m1) | (__float_as_uint(t.p4) & ~m1);
-  const uint32_t lo2 = (__float_as_uint(t.p2) & m1) | (__float_as_uint(t.p0) & ~m1);
-  const float t0 = __uint_as_float((hi2 & m2) | (lo2 & ~m2));      // 5, 2.5, 1.25, 0.25: tie -> down
-  const bool b0 = __builtin_fmaf(-t0, g, a) > 0.0f;
-  const uint32_t m = (uint32_t(b2) << 2) | (uint32_t(b1) << 1) | uint32_t(b0);
+  const uint32_t hi2 = (__float_as_uint(t.u6) & m1) | (__float_as_uint(t.u4) & ~m1);
+  const uint32_t lo2 = (__float_as_uint(t.u2) & m1) | (__float_as_uint(t.u0) & ~m1);
+  const float t0 = __uint_as_float((hi2 & m2) | (lo2 & ~m2));
+  const bool b0 = a > t0;
+  return (uint32_t(b2) << 2) | (uint32_t(b1) << 1) | uint32_t(b0);
+}
+
+// Signed E2M1 nibble of y: magnitude code, sign bit 3, a zero magnitude stored as code 0.
+__device__ __forceinline__ uint32_t e2m1_nibble(float y, const E2m1Thresholds& t) {
+  const uint32_t m = e2m1_mag(fabsf(y), t);
   const uint32_t sign = (__float_as_uint(y) >> 28) & 8u;
   return m | (m ? sign : 0u);
+}
+
+// Eight signed nibbles packed in a word (nibble i = element i): the sign bits are set for
+// every element and then cleared where the magnitude is zero, once per word.
+__device__ __forceinline__ uint32_t e2m1_pack8(const float* y, const E2m1Thresholds& t) {
+  uint32_t w = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w |= (e2m1_mag(fabsf(y[i]), t) | ((__float_as_uint(y[i]) >> 28) & 8u)) << (4 * i);
+  const uint32_t z = ~(w | (w >> 1) | (w >> 2)) & 0x11111111u;     // bit 0 of nibbles with magnitude 0
+  return w & ~(z << 3);
 }
 
 // Encode one block with a given scale code S: writes the 16 nibbles packed in two dwords
@@ -134,12 +168,8 @@ __device__ __forceinline__ void encode_block_with(const float (&y)[kBlock], floa
 #pragma clang fp contract(off)
   const float sigma = e4m3_value(S);
   // straight-line: a zero scale (underflowing block) masks the codes to 0 afterwards
-  const E2m1Thresholds t(sigma);
-  uint32_t l = 0u, h = 0u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) l |= e2m1_nibble(y[i], t, g) << (4 * i);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) h |= e2m1_nibble(y[8 + i], t, g) << (4 * i);
+  const E2m1Thresholds t(sigma, g);
+  const uint32_t l = e2m1_pack8(&y[0], t), h = e2m1_pack8(&y[8], t);
   lo = sigma > 0.0f ? l : 0u;
   hi = sigma > 0.0f ? h : 0u;
 }
@@ -184,12 +214,12 @@ __device__ __forceinline__ uint32_t e2m1_twice_mag(uint32_t m) { return (0xC8643
 template <int N>
 __device__ __forceinline__ void mse_partials(const float (&y)[N], const double (&ay)[N], float sigma, float g,
                                              double& p2, uint32_t& m4) {
-  const E2m1Thresholds t(sigma);
+  const E2m1Thresholds t(sigma, g);
   p2 = 0.0;
   m4 = 0u;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const uint32_t v2 = e2m1_twice_mag(e2m1_nibble(y[i], t, g) & 7u);
+    const uint32_t v2 = e2m1_twice_mag(e2m1_mag(fabsf(y[i]), t));
     p2 = __builtin_fma(static_cast<double>(v2), ay[i], p2);   // exact (see above)
     m4 += v2 * v2;
   }

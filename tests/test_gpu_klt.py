@@ -180,3 +180,34 @@ def test_klt_end_to_end_with_gpu_calibration(lib):
     got = gpu_decode(lib, cache, q, pages, seq, c["T"])
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     assert rel < 1e-2, rel
+
+
+def test_calibrate_key_basis_zero_windows(lib):
+    """All-zero calibration keys: a zero covariance, whose eigenbasis is the identity in both
+    implementations (no rotation happens; ties keep index order), and g_K = 1 (A_K = 0)."""
+    hkv = 2
+    kw = np.zeros((2, 9, hkv, 128), np.uint16)
+    r = torch.ones((hkv, 128), dtype=torch.float32, device="cuda")
+    Bg, g = gpu_calibrate_basis(lib, kw, hkv, KLT, r)
+    Bo, _ = O.klt_basis(S.bf16_to_f32(kw), None, KLT)
+    assert np.array_equal(Bg, Bo) and np.array_equal(Bg[0], np.eye(128, dtype=np.float32))
+    assert float(g[0]) == 1.0
+
+
+def test_calibrate_key_basis_rank_deficient(lib):
+    """Keys confined (up to bf16 rounding) to a 16-dimensional subspace: the 16 leading
+    columns are determined and match the oracle's; the near-null space is only required to
+    be orthonormal and orthogonal to them."""
+    rng = np.random.default_rng(17)
+    U = np.linalg.qr(rng.standard_normal((128, 16)))[0]
+    kw = S.bf16_round((rng.standard_normal((3, 65, 1, 16)) * np.linspace(3, 1, 16)) @ U.T)
+    r = torch.ones((1, 128), dtype=torch.float32, device="cuda")
+    Bg, g = gpu_calibrate_basis(lib, kw, 1, KLT, r)
+    kwf = S.bf16_to_f32(kw)
+    Bo, lam = O.klt_basis(kwf, None, KLT)
+    Bh, Bref = Bg[0].astype(np.float64), Bo[0].astype(np.float64)
+    assert np.max(np.abs(Bh.T @ Bh - np.eye(128))) <= 1e-5
+    assert np.max(np.abs(Bh[:, :16] - Bref[:, :16])) <= 1e-5
+    assert lam[0][15] > 1e3 * lam[0][16]
+    _, _, go = O.calibrate(kwf, None, True, KLT)
+    assert abs(float(g[0]) - float(go[0])) <= 1e-5 * float(go[0])
