@@ -156,7 +156,7 @@ __device__ __forceinline__ void pf_pv(const uint32_t (&ev)[4], const uint32_t (&
 template <bool KBF16, int NT>
 __device__ __forceinline__ void pf_iter(const IterLoads<KBF16>& L, const HalfBase (&hbc)[2], int t0, int t_end,
                                         const u32x4 (&qa)[2][NT][4][64], const float (&desc)[2][4], const int (&pos)[2],
-                                        const Lane& ln, uint32_t* p_w, PfState& st) {
+                                        const Lane& ln, uint32_t* p_w, PfState& st, bool full) {
   const int c = ln.c, g = ln.g;
   // ---- QK ----
   floatx4 sacc[2][2];
@@ -196,15 +196,26 @@ __device__ __forceinline__ void pf_iter(const IterLoads<KBF16>& L, const HalfBas
   // (a power of two) is folded into the exponent's FMA and into each row's raw threshold, so
   // the common case needs no cross-lane reduction: only when some raw score passes its row's
   // threshold is the row max taken and the reference moved. ----
+  // full (wave-uniform): every key of the iteration is visible to every row of the tile, so
+  // the causal and range masks are skipped (all iterations below the diagonal)
   float x[2][2][4];
+  if (full) {
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int eta = 0; eta < 2; ++eta) {
-      const bool vis = hbc[eta].ok && (t0 + 16 * eta + c < t_end) && (t0 + 16 * eta + c <= pos[rb]);
+      for (int eta = 0; eta < 2; ++eta)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[rb][eta][j] = vis ? sacc[rb][eta][j] : -INFINITY;
-    }
+        for (int j = 0; j < 4; ++j) x[rb][eta][j] = sacc[rb][eta][j];
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int eta = 0; eta < 2; ++eta) {
+        const bool vis = hbc[eta].ok && (t0 + 16 * eta + c < t_end) && (t0 + 16 * eta + c <= pos[rb]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[rb][eta][j] = vis ? sacc[rb][eta][j] : -INFINITY;
+      }
+  }
   bool need_any = false;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
@@ -382,7 +393,9 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn(PrefillArgs a) {
     for (; it < n_it; it += kPfWaves) {
       // (a separate unmasked instance for the iterations below the diagonal spills registers
       // and runs 4x slower: measured)
-      pf_iter<KBF16, NT>(buf, hb, kIterTok * it, t_end, sm.loop.qa, desc, pos, ln, p_w, st);
+      const int t_last = kIterTok * it + kIterTok - 1;
+      const bool full = __all(hb[0].ok && hb[1].ok && t_last < t_end && t_last <= pos0);
+      pf_iter<KBF16, NT>(buf, hb, kIterTok * it, t_end, sm.loop.qa, desc, pos, ln, p_w, st, full);
       if (it + kPfWaves < n_it) {
         half_bases<KBF16>(a, load_pages(a, ptab, kIterTok * (it + kPfWaves), t_end), h, hb);
         issue_loads<KBF16>(hb, ln, buf);
