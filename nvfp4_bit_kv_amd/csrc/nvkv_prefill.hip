@@ -152,11 +152,16 @@ __device__ __forceinline__ void pf_pv(const uint32_t (&ev)[4], const uint32_t (&
     }
 }
 
-// One 32-token iteration (tokens t0..t0+31) of a wavefront for its 32 rows.
-template <bool KBF16, int NT>
-__device__ __forceinline__ void pf_iter(const IterLoads<KBF16>& L, const HalfBase (&hbc)[2], int t0, int t_end,
+// One 32-token iteration (tokens t0..t0+31) of a wavefront for its 32 rows.  L is the
+// wavefront's single load buffer: after_k() runs once QK has consumed L.k and may refill it
+// (the next iteration's key loads), after_v() once the V operands have been taken from L.vd
+// and L.vs and may refill those; so the loads of the next iteration are in flight during the
+// softmax and PV of this one.  ok[eta]: the page of half eta is in range.
+template <bool KBF16, int NT, class AfterK, class AfterV>
+__device__ __forceinline__ void pf_iter(const IterLoads<KBF16>& L, const bool (&ok)[2], int t0, int t_end,
                                         const u32x4 (&qa)[2][NT][4][64], const float (&desc)[2][4], const int (&pos)[2],
-                                        const Lane& ln, uint32_t* p_w, PfState& st, bool full) {
+                                        const Lane& ln, uint32_t* p_w, PfState& st, bool full, AfterK&& after_k,
+                                        AfterV&& after_v) {
   const int c = ln.c, g = ln.g;
   // ---- QK ----
   floatx4 sacc[2][2];
@@ -192,6 +197,7 @@ __device__ __forceinline__ void pf_iter(const IterLoads<KBF16>& L, const HalfBas
       }
     }
   }
+  after_k();
   // ---- scores (masked to -inf where needed) and the lazy running max.  The row descale
   // (a power of two) is folded into the exponent's FMA and into each row's raw threshold, so
   // the common case needs no cross-lane reduction: only when some raw score passes its row's
@@ -211,7 +217,7 @@ __device__ __forceinline__ void pf_iter(const IterLoads<KBF16>& L, const HalfBas
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int eta = 0; eta < 2; ++eta) {
-        const bool vis = hbc[eta].ok && (t0 + 16 * eta + c < t_end) && (t0 + 16 * eta + c <= pos[rb]);
+        const bool vis = ok[eta] && (t0 + 16 * eta + c < t_end) && (t0 + 16 * eta + c <= pos[rb]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) x[rb][eta][j] = vis ? sacc[rb][eta][j] : -INFINITY;
       }
@@ -275,6 +281,7 @@ __device__ __forceinline__ void pf_iter(const IterLoads<KBF16>& L, const HalfBas
     ev[p] = nib_even(L.vd[2 * p], L.vd[2 * p + 1]);
     od[p] = nib_odd(L.vd[2 * p], L.vd[2 * p + 1]);
   }
+  after_v();
   pf_pv<0>(ev, od, sig, ap, st);
   pf_pv<1>(ev, od, sig, ap, st);
   pf_pv<2>(ev, od, sig, ap, st);
@@ -395,11 +402,22 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn(PrefillArgs a) {
       // and runs 4x slower: measured)
       const int t_last = kIterTok * it + kIterTok - 1;
       const bool full = __all(hb[0].ok && hb[1].ok && t_last < t_end && t_last <= pos0);
-      pf_iter<KBF16, NT>(buf, hb, kIterTok * it, t_end, sm.loop.qa, desc, pos, ln, p_w, st, full);
-      if (it + kPfWaves < n_it) {
-        half_bases<KBF16>(a, load_pages(a, ptab, kIterTok * (it + kPfWaves), t_end), h, hb);
-        issue_loads<KBF16>(hb, ln, buf);
-      }
+      const bool ok[2] = {hb[0].ok, hb[1].ok};
+      const bool has_next = it + kPfWaves < n_it;
+      // page entries of the next iteration (scalar loads), needed once QK is done
+      IterPages pn{};
+      if (has_next) pn = load_pages(a, ptab, kIterTok * (it + kPfWaves), t_end);
+      pf_iter<KBF16, NT>(
+          buf, ok, kIterTok * it, t_end, sm.loop.qa, desc, pos, ln, p_w, st, full,
+          [&] {
+            if (has_next) {
+              half_bases<KBF16>(a, pn, h, hb);
+              issue_k_loads<KBF16>(hb, ln, buf.k);
+            }
+          },
+          [&] {
+            if (has_next) issue_v_loads<KBF16>(hb, ln, buf);
+          });
     }
   }
   __syncthreads();     // every wavefront is done with the query terms and P buffers
