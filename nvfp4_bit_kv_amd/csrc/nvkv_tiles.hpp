@@ -171,35 +171,6 @@ __device__ __forceinline__ void half_bases(const Args& a, const IterPages& P, in
   }
 }
 
-// Key part of an iteration's loads (codes and scales, or BF16 rows).
-template <bool KBF16>
-__device__ __forceinline__ void issue_k_loads(const HalfBase (&hb)[2], const Lane& ln, KLoads<KBF16>& K) {
-#pragma unroll
-  for (int eta = 0; eta < 2; ++eta) {
-    if constexpr (!KBF16) {
-      K.kc[eta] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hb[eta].kc, ln.k_off, 0, kNonTemporal));
-      K.ks[eta] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(hb[eta].ks, ln.ks_off, 0, 0));
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        K.kr[eta][u] =
-            __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hb[eta].kc, ln.k_off + 16 * u, 0, kNonTemporal));
-    }
-  }
-}
-
-// Value part of an iteration's loads (codes and scales).
-template <bool KBF16>
-__device__ __forceinline__ void issue_v_loads(const HalfBase (&hb)[2], const Lane& ln, IterLoads<KBF16>& L) {
-#pragma unroll
-  for (int eta = 0; eta < 2; ++eta) {
-    const u32x4 v4 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hb[eta].vc, ln.v_off, 0, kNonTemporal));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) L.vd[2 * j + eta] = v4[j];
-    L.vs[eta] = __builtin_amdgcn_raw_buffer_load_b32(hb[eta].vs, ln.vs_off, 0, 0);
-  }
-}
-
 template <bool KBF16>
 __device__ __forceinline__ void issue_loads(const HalfBase (&hb)[2], const Lane& ln, IterLoads<KBF16>& L) {
 #pragma unroll
