@@ -161,15 +161,57 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const float* y, const E2m1Thresho
   return w & ~(z << 3);
 }
 
+// Clear the sign bit of every nibble whose magnitude is zero (a zero is stored as code 0).
+__device__ __forceinline__ uint32_t clear_zero_signs(uint32_t w) {
+  const uint32_t z = ~(w | (w >> 1) | (w >> 2)) & 0x11111111u;     // bit 0 of nibbles with magnitude 0
+  return w & ~(z << 3);
+}
+
+// Eight elements through the hardware E2M1 converter: nibble i = RNE(y_i * Rs) with ties to
+// the even code, saturating at 6, sign from y_i (so a zero magnitude may carry a sign bit).
+// The converter divides by the power of two of its scale operand; 1 leaves the input as is.
+__device__ __forceinline__ uint32_t cvt_pack8(const float* y, float Rs) {
+#pragma clang fp contract(off)
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0] * Rs, y[1] * Rs, 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2] * Rs, y[3] * Rs, 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4] * Rs, y[5] * Rs, 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6] * Rs, y[7] * Rs, 1.0f, 3);
+  return w;
+}
+
+// Relative margins of the bracketing quotients: 1 -/+ 2^-20.
+constexpr float kBracketDown = 1.0f - 0x1p-20f;
+constexpr float kBracketUp = 1.0f + 0x1p-20f;
+
 // Encode one block with a given scale code S: writes the 16 nibbles packed in two dwords
 // (byte k = nibble 2k | nibble 2k+1 << 4); a zero scale gives an all-zero block.
+//
+// Fast path: the exact quotient Q = |y| / (sigma g) is bracketed by q1 = |y| R (1 - 2^-20) and
+// q2 = |y| R (1 + 2^-20), R = rcp(fl(sigma g)): the reciprocal (1 ulp), the product sigma g
+// and the two multiplications stay within 3 ulp (3 * 2^-23) of the exact factors, far inside
+// the 2^-20 margin, so q1 < Q < q2 whenever sigma g is a normal number.  Round to nearest is
+// monotonic, so when the converter gives both brackets the same code that code is RNE(Q),
+// exactly the decision of the bound-based encoder.  Where they differ (Q within about 2^-20
+// of a midpoint, a few elements in a million) the block takes the exact bound-based encoder.
 __device__ __forceinline__ void encode_block_with(const float (&y)[kBlock], float g, uint32_t S, uint32_t& lo,
                                                   uint32_t& hi) {
 #pragma clang fp contract(off)
   const float sigma = e4m3_value(S);
-  // straight-line: a zero scale (underflowing block) masks the codes to 0 afterwards
-  const E2m1Thresholds t(sigma, g);
-  const uint32_t l = e2m1_pack8(&y[0], t), h = e2m1_pack8(&y[8], t);
+  const float u = sigma * g;
+  const float R = __builtin_amdgcn_rcpf(u);
+  const float r1 = R * kBracketDown, r2 = R * kBracketUp;
+  const uint32_t l1 = cvt_pack8(&y[0], r1), l2 = cvt_pack8(&y[0], r2);
+  const uint32_t h1 = cvt_pack8(&y[8], r1), h2 = cvt_pack8(&y[8], r2);
+  uint32_t l = l1, h = h1;
+  const bool exact = sigma > 0.0f && !(l1 == l2 && h1 == h2 && u >= 0x1p-125f);
+  if (__builtin_expect(exact, 0)) {
+    const E2m1Thresholds t(sigma, g);
+    l = e2m1_pack8(&y[0], t);
+    h = e2m1_pack8(&y[8], t);
+  }
+  l = clear_zero_signs(l);
+  h = clear_zero_signs(h);
   lo = sigma > 0.0f ? l : 0u;
   hi = sigma > 0.0f ? h : 0u;
 }
