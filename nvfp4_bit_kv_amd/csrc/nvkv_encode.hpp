@@ -252,16 +252,34 @@ constexpr int kMseMaxCand = 17;
 // Twice the E2M1 magnitude of a 3-bit magnitude code: 0, 1, 2, 3, 4, 6, 8, 12.
 __device__ __forceinline__ uint32_t e2m1_twice_mag(uint32_t m) { return (0xC8643210u >> (4u * m)) & 15u; }
 
-// 2P and 4 M2 over N elements of a block (|y| given in fp64) for scale sigma > 0.
+// 2P and 4 M2 over N elements of a block (|y| given in fp64) for scale sigma > 0.  The
+// magnitude codes come from the bracketing converter pass of encode_block_with when its two
+// brackets agree, else from the exact bound-based encoder.
 template <int N>
 __device__ __forceinline__ void mse_partials(const float (&y)[N], const double (&ay)[N], float sigma, float g,
                                              double& p2, uint32_t& m4) {
-  const E2m1Thresholds t(sigma, g);
+#pragma clang fp contract(off)
+  static_assert(N % 8 == 0, "whole packed words");
+  const float u = sigma * g;
+  const float R = __builtin_amdgcn_rcpf(u);
+  const float r1 = R * kBracketDown, r2 = R * kBracketUp;
+  uint32_t w[N / 8];
+  bool same = u >= 0x1p-125f;
+#pragma unroll
+  for (int j = 0; j < N / 8; ++j) {
+    w[j] = cvt_pack8(&y[8 * j], r1);
+    same &= w[j] == cvt_pack8(&y[8 * j], r2);
+  }
+  if (__builtin_expect(!same, 0)) {
+    const E2m1Thresholds t(sigma, g);
+#pragma unroll
+    for (int j = 0; j < N / 8; ++j) w[j] = e2m1_pack8(&y[8 * j], t);
+  }
   p2 = 0.0;
   m4 = 0u;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const uint32_t v2 = e2m1_twice_mag(e2m1_mag(fabsf(y[i]), t));
+    const uint32_t v2 = e2m1_twice_mag((w[i / 8] >> (4 * (i % 8))) & 7u);
     p2 = __builtin_fma(static_cast<double>(v2), ay[i], p2);   // exact (see above)
     m4 += v2 * v2;
   }
