@@ -107,7 +107,8 @@ typedef struct nvkv_layer {
   int32_t num_pages;          /* pages in k_data / v_data                                  */
   int32_t k_fmt;              /* NVKV_FMT_NVFP4 or NVKV_FMT_BF16                           */
   int32_t v_fmt;              /* NVKV_FMT_NVFP4                                            */
-  uint32_t k_flags;           /* NVKV_K_SMOOTH | NVKV_K_HADAMARD | NVKV_K_MSE_SCALE; 0 for BF16 keys */
+  uint32_t k_flags;           /* NVKV_K_SMOOTH | NVKV_K_HADAMARD | NVKV_K_MSE_SCALE | NVKV_K_KLT
+                                 (not HADAMARD with KLT); 0 for BF16 keys                  */
   int32_t reserved;           /* must be 0                                                 */
   void *k_data;               /* NVFP4 codes or BF16 rows, layout above                    */
   void *v_data;               /* NVFP4 codes                                               */
