@@ -268,6 +268,55 @@ def test_special_rows_bit_exact(lib):
     assert 0 in ks[:, 0, 0] and 0x7E in ks[:, 0, 0] and np.any((ks > 0) & (ks < 8))
 
 
+@pytest.mark.parametrize("flags", [1, 1 | 4])
+def test_near_midpoint_keys_bit_exact(lib, flags):
+    """Smoothed keys placed within a few ulp of every E2M1 midpoint of their block (the
+    encoder's converter brackets disagree there and the exact bound-based path decides), at
+    the midpoints themselves, and 64 ulp away (the brackets agree); also with the MSE-searched
+    scales.  The smoothing factors r are chosen per channel so that y = fl32(x * r) lands on
+    the target; the block maximum fixes sigma = 3."""
+    rng = np.random.default_rng(29)
+    hkv, N = 8, 16
+    g = np.float32(2.0 ** -7)
+    u = np.float32(3.0) * g                                     # sigma * g, exact
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    offs = [-64, -3, -2, -1, 0, 1, 2, 3, 64]
+    r = np.ones((hkv, 128), np.float32)
+    x = np.zeros((hkv, 128), np.float32)
+    k_idx = 0
+    for h in range(hkv):
+        for blk in range(8):
+            j0 = 16 * blk
+            x[h, j0] = np.float32(18.0) * g                       # block maximum 6 * sigma * g
+            for t in range(1, 16):
+                T = np.float32(mids[k_idx % 7]) * u               # exact midpoint threshold
+                target = (T.view(np.uint32) + np.int64(offs[k_idx % 9])).astype(np.uint32).view(np.float32)
+                X = S.bf16_to_f32(S.bf16_round(np.float32(rng.uniform(0.5, 4.0)) * np.ones(1, np.float32)))[0]
+                X = X if k_idx % 5 else -X
+                r[h, j0 + t] = np.float32(target / np.float64(abs(X)))
+                x[h, j0 + t] = X
+                k_idx += 1
+    kbits = np.broadcast_to(S.bf16_round(x)[None, None], (1, N, hkv, 128)).copy()
+    vbits = S.bf16_round(rng.standard_normal((1, N, hkv, 128)).astype(np.float32))
+    k32 = S.bf16_to_f32(kbits)
+    assert np.array_equal(k32[0, 0], x)
+    y = O.key_transform(k32, r[None, None], flags)
+    near = np.abs(np.abs(y[0, 0]) / np.float64(u) - np.array(mids)[:, None, None]).min(axis=0)
+    assert np.count_nonzero(near < 2.0 ** -21) > 200                   # many within the bracket margin
+    gg = np.array([g, g], np.float32)
+    kc, ks = O.quantize_keys(y, gg[0], flags)
+    vc, vs = O.quantize_rows(S.bf16_to_f32(vbits), gg[1])
+    pages = P.Pages(1, N, True)
+    s = (np.float32(1.0) / r).astype(np.float32)
+    cache = gpu_fill_cache(lib, kbits, vbits, hkv, flags, pages, torch.from_numpy(s).cuda(),
+                           torch.from_numpy(r).cuda(), gg)
+    gc, gs = P.rows_from_cache_vec(cache.k_data.cpu().numpy(), cache.k_scales.cpu().numpy(), pages, hkv, 0, N)
+    assert np.array_equal(gs, ks[0]) and np.array_equal(gc, kc[0])
+    gc, gs = P.rows_from_cache_vec(cache.v_data.cpu().numpy(), cache.v_scales.cpu().numpy(), pages, hkv, 0, N,
+                                   values=True)
+    assert np.array_equal(gs, vs[0]) and np.array_equal(gc, vc[0])
+
+
 def test_scale_code_at_every_e4m3_midpoint(lib):
     """Block absmax exactly at 6*g times each of the 126 E4M3 midpoints (ties: the even code
     wins), and one bf16 step above and below each, for two tensor scales; codes and scales
