@@ -414,11 +414,12 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn(PrefillArgs a) {
     }
     uint32_t* p_w = sm.loop.p[wave][0][0];
 
-    // iterations it = wave, wave + 4, ...; two register buffers, the next one in flight
+    // iterations it = wave, wave + 4, ...
     const int n_it = (t_end + kIterTok - 1) / kIterTok;
-    // One register buffer: the next iteration's loads are issued as soon as this one's
-    // operands are consumed.  Two buffers would push the kernel past 256 registers (one
-    // wavefront per SIMD instead of two) and cost 1.6x (measured).
+    // One register buffer: the next iteration's key loads are issued as soon as QK has
+    // consumed this one's keys, its value loads once the V operands are extracted (pf_iter's
+    // callbacks).  Two buffers would push the kernel past 256 registers (one wavefront per
+    // SIMD instead of two) and cost 1.6x (measured).
     IterLoads<KBF16> buf;
     HalfBase hb[2];
     int it = wave;
