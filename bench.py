@@ -913,7 +913,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4 cache (e2m1 + e4m3 scales); f16 MFMA on exact operands, f32 accumulate",
+        "dtype": "f16",
+        "arithmetic": "f16 MFMA on exact operand splits, f32 accumulate; codec in f32",
+        "cache_format": "nvfp4: e2m1 codes, e4m3 block scales per 16, f32 tensor scale",
         "data": "synthetic",
         "config": {
             "workload": wl.describe(),
