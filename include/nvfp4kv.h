@@ -91,8 +91,8 @@ enum { NVKV_K_SMOOTH = 1u, NVKV_K_HADAMARD = 2u, NVKV_K_MSE_SCALE = 4u, NVKV_K_K
 /* NVKV_K_KLT: static per-head KLT key basis ([cache post] cache-config table rows "K: static
  * per-head KLT" and "K: static KLT + smoothing"): keys are rotated z = B^T y after the optional
  * smoothing, queries q' = B^T (q * s), with B = layer->k_basis from nvkv_calibrate_key_basis.
- * Each z_i is the sequential fp32 sum over j = 0..127 of fl32(B[j][i] * y_j), every product and
- * partial sum rounded to fp32 (no fused multiply-add), so codes are reproducible bit for bit.
+ * Each z_i is the chain of fp32 fused multiply-adds z <- fl32(B[j][i] * y_j + z) over
+ * j = 0..127 from z = 0 (one rounding per step), so codes are reproducible bit for bit.
  * Not combined with NVKV_K_HADAMARD. */
 enum { NVKV_PART_CODES = 0, NVKV_PART_SCALES = 1 };
 

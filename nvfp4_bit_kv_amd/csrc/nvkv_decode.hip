@@ -324,8 +324,8 @@ __device__ __forceinline__ void new_token_transform(const DecodeArgs& a, int lan
     had_cross(y, lane, 16);                               // h = 64
   }
   if (a.k_flags & NVKV_K_KLT) {
-    // z = B^T y in the fixed rounding order of the append kernel (each output a sequential
-    // sum over j of rounded products), on the whole wavefront: the key row goes through LDS,
+    // z = B^T y in the fixed rounding order of the append kernel (each output a chain of
+    // fused multiply-adds over j), on the whole wavefront: the key row goes through LDS,
     // lane l forms z[2l] and z[2l + 1], and key lane L then reads back z[4L .. 4L + 3]
     if (!is_v) *reinterpret_cast<float4*>(&st.ky[4 * (lane & 31)]) = make_float4(y[0], y[1], y[2], y[3]);
     float z0 = 0.0f, z1 = 0.0f;
@@ -336,8 +336,8 @@ __device__ __forceinline__ void new_token_transform(const DecodeArgs& a, int lan
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float2 bj = *reinterpret_cast<const float2*>(basis_lds + (4 * j4 + u) * kHeadDim + 2 * lane);
-        z0 = z0 + bj.x * yv[u];
-        z1 = z1 + bj.y * yv[u];
+        z0 = __builtin_fmaf(bj.x, yv[u], z0);
+        z1 = __builtin_fmaf(bj.y, yv[u], z1);
       }
     }
     *reinterpret_cast<float2*>(&st.ky[2 * lane]) = make_float2(z0, z1);

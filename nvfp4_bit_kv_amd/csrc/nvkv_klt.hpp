@@ -5,8 +5,9 @@
 // smoothing is near-lossless, key rotations hurt", cache-config table rows "K: static
 // per-head KLT" and "K: static KLT + smoothing".  The basis B of a KV head is fp32 [128][128]
 // (element (j, i) at j*128 + i; column i = basis vector i).  Keys are rotated z = B^T y with a
-// fixed rounding order (rotate_cols), which is part of the bit-exact encoding; the query side
-// q' = B^T (q * s) is not an encoding step and may round in any order.
+// fixed rounding order (rotate_cols: a chain of fused multiply-adds), which is part of the
+// bit-exact encoding; the query side q' = B^T (q * s) is not an encoding step and may round in
+// any order.
 #pragma once
 
 #include "nvkv_device.hpp"
@@ -36,12 +37,12 @@ __device__ __forceinline__ void load_basis_quarter(const float* __restrict__ bas
   for (int k = 0; k < 16; ++k) dst[64 * k + lane] = v[k];
 }
 
-// z_k = sum over j = 0..127 of fl32(B[j][c0 + k] * row[j]), k < N (a multiple of 4, c0 a
-// multiple of 4), summed sequentially in j with every product and every partial sum rounded
-// to fp32: the key rotation's rounding order.  B and row may be in LDS or global memory.
+// z_k = sum over j = 0..127 of B[j][c0 + k] * row[j], k < N (a multiple of 4, c0 a multiple
+// of 4), as a chain of fp32 fused multiply-adds in j: z <- fl32(B[j][c0 + k] * row[j] + z)
+// from z = 0, one rounding per step: the key rotation's rounding order.  B and row may be in
+// LDS or global memory.
 template <int N>
 __device__ __forceinline__ void rotate_cols(const float* B, const float* row, int c0, float (&z)[N]) {
-#pragma clang fp contract(off)
 #pragma unroll
   for (int k = 0; k < N; ++k) z[k] = 0.0f;
 #pragma unroll 4
@@ -51,10 +52,10 @@ __device__ __forceinline__ void rotate_cols(const float* B, const float* row, in
 #pragma unroll
     for (int k = 0; k < N / 4; ++k) {
       const float4 b = bj[k];
-      z[4 * k + 0] = z[4 * k + 0] + b.x * yj;
-      z[4 * k + 1] = z[4 * k + 1] + b.y * yj;
-      z[4 * k + 2] = z[4 * k + 2] + b.z * yj;
-      z[4 * k + 3] = z[4 * k + 3] + b.w * yj;
+      z[4 * k + 0] = __builtin_fmaf(b.x, yj, z[4 * k + 0]);
+      z[4 * k + 1] = __builtin_fmaf(b.y, yj, z[4 * k + 1]);
+      z[4 * k + 2] = __builtin_fmaf(b.z, yj, z[4 * k + 2]);
+      z[4 * k + 3] = __builtin_fmaf(b.w, yj, z[4 * k + 3]);
     }
   }
 }

@@ -192,9 +192,9 @@ def key_transform(x: np.ndarray, r: np.ndarray | None, flags: int, basis: np.nda
 # columns in decreasing eigenvalue order, each signed so that its largest-magnitude entry is
 # positive (entries within a relative 1e-6 of the largest count as ties, and the first of
 # them decides, so that rounding noise cannot flip a sign); stored as fp32.  Keys are rotated z = B^T y with each
-# output a sequential fp32 sum over the input index, every product and every sum rounded to
-# fp32 (no fused multiply-add), so that codes are reproducible bit for bit; the query side
-# applies the same fp32 basis in fp64.  The Hadamard and KLT bases are not combined.
+# output a chain of fp32 fused multiply-adds over the input index (one rounding per step), so
+# that codes are reproducible bit for bit; the query side applies the same fp32 basis in
+# fp64.  The Hadamard and KLT bases are not combined.
 # ----------------------------------------------------------------------------------------
 KLT_SIGN_TIE = 1e-6     # entries within this relative distance of the largest count as ties
 
@@ -225,15 +225,35 @@ def klt_basis(k_win: np.ndarray, r: np.ndarray | None, k_flags: int, exclude_pos
     return basis, lam_out
 
 
+def fma_f32(a: np.ndarray, b: np.ndarray, c: np.ndarray) -> np.ndarray:
+    """fl32(a*b + c) with a single rounding (a fused multiply-add), for fp32 arrays.
+
+    The product of two fp32 values is exact in fp64 (48 significant bits).  The fp64 sum s is
+    rounded to nearest; its exact error e comes from the two-sum identity.  Where e != 0 and
+    s has an even last bit, s moves one step towards e: that makes s the round-to-odd value of
+    the exact sum, and a round-to-odd value with 53 >= 24 + 2 bits rounds to fp32 exactly as
+    the exact sum would.  Valid away from fp64 overflow, as everywhere in this oracle."""
+    p = np.asarray(a, dtype=np.float32).astype(np.float64) * np.asarray(b, dtype=np.float32).astype(np.float64)
+    c64 = np.asarray(c, dtype=np.float32).astype(np.float64)
+    p, c64 = np.broadcast_arrays(p, c64)
+    s = p + c64
+    bb = s - p
+    e = (p - (s - bb)) + (c64 - bb)
+    even = (s.view(np.int64) & 1) == 0
+    step = np.nextafter(s, np.where(e > 0, np.inf, -np.inf))
+    s = np.where((e != 0) & even, step, s)
+    return s.astype(np.float32)
+
+
 def rotate_fp32(y: np.ndarray, basis: np.ndarray) -> np.ndarray:
-    """z[..., h, i] = sum_j basis[h, j, i] * y[..., h, j], the sum taken sequentially over
-    j = 0..127 with every product and every partial sum rounded to fp32."""
+    """z[..., h, i] = sum_j basis[h, j, i] * y[..., h, j], taken as a chain of fused
+    multiply-adds over j = 0..127: z <- fl32(basis[h, j, i] * y_j + z) from z = 0, one rounding
+    per step."""
     y = np.asarray(y, dtype=np.float32)
     B = np.asarray(basis, dtype=np.float32)
     acc = np.zeros(y.shape, dtype=np.float32)
     for j in range(HEAD_DIM):
-        prod = (B[:, j, :] * y[..., :, j:j + 1]).astype(np.float32)
-        acc = (acc + prod).astype(np.float32)
+        acc = fma_f32(B[:, j, :], y[..., :, j:j + 1], acc)
     return acc
 
 

@@ -1,7 +1,8 @@
 """Pins of the oracle's static per-head KLT key basis (CPU only).
 
-* the key rotation's fixed fp32 order against an exact-rational emulation of the same
-  sequence of roundings (tests/_brute.py);
+* the key rotation's fixed order (a chain of fp32 fused multiply-adds) against an
+  exact-rational emulation of the same sequence of roundings (tests/_brute.py), and the fused
+  multiply-add itself against exact rationals;
 * a closed form: calibration windows built from the columns of the Sylvester Hadamard matrix,
   scaled by distinct factors and shifted by a common mean, have the normalised Hadamard
   columns as eigenvectors (the mean drops out of the centred covariance), with eigenvalues
@@ -24,7 +25,18 @@ from oracle import nvfp4_oracle as O
 from tests import _brute
 
 
+def _two_roundings(y, B):
+    """The same sums with the product and the addition rounded separately (what a chain
+    without fused multiply-adds gives), for the check that the pin tells the two apart."""
+    acc = np.zeros(y.shape, dtype=np.float32)
+    for j in range(128):
+        acc = (acc + (B[:, j, :] * y[..., :, j:j + 1]).astype(np.float32)).astype(np.float32)
+    return acc
+
+
 def test_rotation_order_vs_exact_rationals():
+    """Each output is the chain z <- fl32(B[j][i] * y_j + z) over j = 0..127 from z = 0: exact
+    rational products and sums with one rounding per step."""
     rng = np.random.default_rng(71)
     y = (rng.standard_normal((2, 1, 128)) * np.exp(rng.uniform(-4, 4, (2, 1, 128)))).astype(np.float32)
     B = (rng.standard_normal((1, 128, 128)) / np.sqrt(128)).astype(np.float32)
@@ -33,9 +45,24 @@ def test_rotation_order_vs_exact_rationals():
         for i in range(0, 128, 3):
             acc = Fraction(0)
             for j in range(128):
-                p = Fraction(float(_brute.fraction_to_f32(Fraction(float(B[0, j, i])) * Fraction(float(y[n, 0, j])))))
-                acc = Fraction(float(_brute.fraction_to_f32(acc + p)))
+                acc = Fraction(float(_brute.fraction_to_f32(Fraction(float(B[0, j, i])) * Fraction(float(y[n, 0, j]))
+                                                            + acc)))
             assert np.float32(float(acc)) == got[n, 0, i], (n, i)
+    assert not np.array_equal(_two_roundings(y, B), got)           # the pin separates the orders
+
+
+def test_fused_multiply_add_against_exact_rationals():
+    """fma_f32 against exact rational arithmetic, over random magnitudes and near-cancelling
+    sums (where the fp64 sum is inexact and its rounding direction matters)."""
+    rng = np.random.default_rng(73)
+    a = (rng.standard_normal(400) * np.exp(rng.uniform(-20, 20, 400))).astype(np.float32)
+    b = (rng.standard_normal(400) * np.exp(rng.uniform(-20, 20, 400))).astype(np.float32)
+    c = (rng.standard_normal(400) * np.exp(rng.uniform(-20, 20, 400))).astype(np.float32)
+    c[:200] = (-(a[:200].astype(np.float64) * b[:200]) * (1 + rng.uniform(-1e-6, 1e-6, 200))).astype(np.float32)
+    got = O.fma_f32(a, b, c)
+    for k in range(400):
+        want = _brute.fraction_to_f32(Fraction(float(a[k])) * Fraction(float(b[k])) + Fraction(float(c[k])))
+        assert got[k] == want, (k, a[k], b[k], c[k], got[k], want)
 
 
 def hadamard_windows(mu, scale):

@@ -176,6 +176,10 @@ def _rotate_transposed(y, basis):
     return ORIG_ROT(y, np.swapaxes(np.asarray(basis), 1, 2))
 
 
+def _rotate_two_roundings(y, basis):
+    return K._two_roundings(np.asarray(y, dtype=np.float32), np.asarray(basis, dtype=np.float32))
+
+
 def _query_basis_not_transposed(q, s, flags, basis=None):
     if flags & O.FLAG_KLT:
         basis = np.swapaxes(np.asarray(basis), -1, -2)
@@ -221,6 +225,7 @@ CASES = [
     ("klt_basis", _klt_largest_negative, [K.test_klt_basis_closed_form_hadamard_columns,
                                           K.test_diagonal_covariance_gives_an_exact_permutation]),
     ("rotate_fp32", _rotate_transposed, [K.test_rotation_order_vs_exact_rationals]),
+    ("rotate_fp32", _rotate_two_roundings, [K.test_rotation_order_vs_exact_rationals]),
     ("query_transform", _query_basis_not_transposed,
      [lambda: K.test_klt_keeps_scores_and_g_is_over_rotated_keys(O.FLAG_KLT)]),
 ]
