@@ -225,36 +225,42 @@ def klt_basis(k_win: np.ndarray, r: np.ndarray | None, k_flags: int, exclude_pos
     return basis, lam_out
 
 
-def fma_f32(a: np.ndarray, b: np.ndarray, c: np.ndarray) -> np.ndarray:
-    """fl32(a*b + c) with a single rounding (a fused multiply-add), for fp32 arrays.
+def _fma_f64_to_f32(p: np.ndarray, c64: np.ndarray) -> np.ndarray:
+    """fl32(p + c) for an exact fp64 product p and fp32 values c held in fp64.
 
-    The product of two fp32 values is exact in fp64 (48 significant bits).  The fp64 sum s is
-    rounded to nearest; its exact error e comes from the two-sum identity.  Where e != 0 and
-    s has an even last bit, s moves one step towards e: that makes s the round-to-odd value of
-    the exact sum, and a round-to-odd value with 53 >= 24 + 2 bits rounds to fp32 exactly as
-    the exact sum would.  Valid away from fp64 overflow, as everywhere in this oracle."""
-    p = np.asarray(a, dtype=np.float32).astype(np.float64) * np.asarray(b, dtype=np.float32).astype(np.float64)
-    c64 = np.asarray(c, dtype=np.float32).astype(np.float64)
-    p, c64 = np.broadcast_arrays(p, c64)
+    The fp64 sum s is rounded to nearest; its exact error e comes from the two-sum identity.
+    Where e != 0 and s has an even last bit, s moves one step towards e: that makes s the
+    round-to-odd value of the exact sum, and a round-to-odd value with 53 >= 24 + 2 bits rounds
+    to fp32 exactly as the exact sum would.  Valid away from fp64 overflow."""
     s = p + c64
     bb = s - p
     e = (p - (s - bb)) + (c64 - bb)
-    even = (s.view(np.int64) & 1) == 0
-    step = np.nextafter(s, np.where(e > 0, np.inf, -np.inf))
-    s = np.where((e != 0) & even, step, s)
+    fix = (e != 0) & ((s.view(np.int64) & 1) == 0)
+    if fix.any():
+        s = np.where(fix, np.nextafter(s, np.where(e > 0, np.inf, -np.inf)), s)
     return s.astype(np.float32)
+
+
+def fma_f32(a: np.ndarray, b: np.ndarray, c: np.ndarray) -> np.ndarray:
+    """fl32(a*b + c) with a single rounding (a fused multiply-add), for fp32 arrays: the
+    product of two fp32 values is exact in fp64 (48 significant bits), then one correctly
+    rounded addition (_fma_f64_to_f32)."""
+    p = np.asarray(a, dtype=np.float32).astype(np.float64) * np.asarray(b, dtype=np.float32).astype(np.float64)
+    c64 = np.asarray(c, dtype=np.float32).astype(np.float64)
+    p, c64 = np.broadcast_arrays(p, c64)
+    return _fma_f64_to_f32(p, c64)
 
 
 def rotate_fp32(y: np.ndarray, basis: np.ndarray) -> np.ndarray:
     """z[..., h, i] = sum_j basis[h, j, i] * y[..., h, j], taken as a chain of fused
     multiply-adds over j = 0..127: z <- fl32(basis[h, j, i] * y_j + z) from z = 0, one rounding
     per step."""
-    y = np.asarray(y, dtype=np.float32)
-    B = np.asarray(basis, dtype=np.float32)
-    acc = np.zeros(y.shape, dtype=np.float32)
+    y64 = np.asarray(y, dtype=np.float32).astype(np.float64)
+    B64 = np.asarray(basis, dtype=np.float32).astype(np.float64)
+    acc = np.zeros(y64.shape, dtype=np.float64)            # fp32 values held in fp64
     for j in range(HEAD_DIM):
-        acc = fma_f32(B[:, j, :], y[..., :, j:j + 1], acc)
-    return acc
+        acc = _fma_f64_to_f32(B64[:, j, :] * y64[..., :, j:j + 1], acc).astype(np.float64)
+    return acc.astype(np.float32)
 
 
 # ----------------------------------------------------------------------------------------
