@@ -97,6 +97,30 @@ def row_bytes(fmt):
     return 256 if fmt == 0 else 72
 
 
+# Algorithmic bytes of the decode step (what the method must move at least once).
+def decode_bytes(B, T, hkv, hq, k_fmt):
+    """One decode over the cache: every cached K and V row with its scales once, the query
+    (bf16) in and the output (fp32) out."""
+    return B * hkv * T * (row_bytes(k_fmt) + 72) + B * hq * (256 + 512)
+
+
+def append_bytes(B, hkv, k_fmt):
+    """Appending the new token of each sequence: bf16 K and V rows in, their cache rows out."""
+    return B * hkv * ((256 + row_bytes(k_fmt)) + (256 + 72))
+
+
+def decode_launch_bytes(B, T, hkv, hq, k_fmt, mode):
+    """One launch of the dominant kernel: the fused call (mode "fused") also appends the new
+    token; otherwise the launch is the decode alone."""
+    return decode_bytes(B, T, hkv, hq, k_fmt) + (append_bytes(B, hkv, k_fmt) if mode == "fused" else 0)
+
+
+def decode_step_bytes(B, T, hkv, hq, k_fmt, layers):
+    """One decode step: per layer the append of the new tokens and one decode, whether the
+    two run as one fused launch or as two calls (the append is counted once)."""
+    return layers * (decode_bytes(B, T, hkv, hq, k_fmt) + append_bytes(B, hkv, k_fmt))
+
+
 def f32_of(torch, t):
     """bf16 torch tensor (host) -> fp32 numpy array of the same values."""
     from synth import kv_inputs as S
@@ -248,21 +272,16 @@ class DecodeStep:
 
     # algorithmic bytes (what the method must move)
     def decode_bytes(self):
-        """One decode over the cache: every cached K and V row with its scales once, the query
-        (bf16) in and the output (fp32) out."""
-        per_tok = row_bytes(self.k_fmt) + 72
-        return self.B * self.hkv * self.T * per_tok + self.B * self.hq * (256 + 512)
+        return decode_bytes(self.B, self.T, self.hkv, self.hq, self.k_fmt)
 
     def launch_bytes(self):
-        """Bytes of one launch of the dominant kernel: the fused call also appends the new
-        token (bf16 K and V rows in, their codes and scales out)."""
-        return self.decode_bytes() + (self.append_bytes_per_layer() if self.mode == "fused" else 0)
+        return decode_launch_bytes(self.B, self.T, self.hkv, self.hq, self.k_fmt, self.mode)
 
     def append_bytes_per_layer(self):
-        return self.B * self.hkv * ((256 + row_bytes(self.k_fmt)) + (256 + 72))
+        return append_bytes(self.B, self.hkv, self.k_fmt)
 
     def step_bytes(self):
-        return self.L * (self.launch_bytes() + self.append_bytes_per_layer())
+        return decode_step_bytes(self.B, self.T, self.hkv, self.hq, self.k_fmt, self.L)
 
     def tokens_per_step(self):
         return self.B

@@ -50,8 +50,9 @@ Readings taken where the pages leave a step open (each is repeated in the design
   - KLT basis: eigenvectors of the centred covariance of the (smoothed) calibration keys over
     the smoothing's positions, decreasing eigenvalues, largest entry of each positive (ties
     within a relative 1e-6: the first), fp32;
-    keys rotated by a sequential fp32 sum without fused multiply-add; not combined with the
-    Hadamard basis.
+    keys rotated as z = B^T y with each output a chain of fp32 fused multiply-adds over the
+    input index, z <- fl32(B[j][i] * y_j + z) for j = 0..127 from z = 0, one rounding per
+    step; not combined with the Hadamard basis.
   - MSE-searched key scales: candidates are the absmax-to-6 code and every E4M3 code that
     puts the block maximum between 7/4 and 7 times the scale; the exact squared error
     decides, ties to the absmax-to-6 code, then to the smallest code.

@@ -39,11 +39,11 @@ def gpu_calibrate_basis(nk, kw, hkv, flags, r, exclude_pos0=True):
     return basis.cpu().numpy(), g.cpu().numpy()
 
 
-def oracle_klt_layer(name, flags, T=None):
+def oracle_klt_layer(name, flags, T=None, sink=True):
     """Oracle calibration (s, r, basis, g) and encoding of a workload layer (memoised)."""
-    key = (name, flags, T)
+    key = (name, flags, T, sink)
     if key not in _LAYERS:
-        c, k, v, kw, vw, q = P.workload(name, T=T)
+        c, k, v, kw, vw, q = P.workload(name, T=T, sink=sink)
         kwf, vwf = S.bf16_to_f32(kw), S.bf16_to_f32(vw)
         s, r, g = O.calibrate(kwf, vwf, True, flags)
         basis, lam = O.klt_basis(kwf, r if flags & O.FLAG_SMOOTH else None, flags)
