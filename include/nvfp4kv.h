@@ -250,6 +250,31 @@ NVKV_API nvkv_status nvkv_decode_append_attention_nvfp4(const nvkv_layer *layer,
                                         int32_t split_tokens, void *stream);
 
 /*
+ * Allocation-free form of nvkv_decode_append_attention_nvfp4, for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, semantics and output, minus the
+ * workspace: the cross-split state (arrival counters and split partials) lives in a static
+ * device array of the library, 512 KiB of counters + 7 MiB of partials, one per GPU, held
+ * until the process ends.  Nothing is allocated, by the library or by any routine it calls.
+ *   Limits: B * Hkv <= 2048, and the split partials of the call (8 + 512 bytes per (split,
+ *   query head), each array rounded up to 256 bytes) within 7 MiB: about 14,000 (split, query
+ *   head) pairs.  A call beyond them returns
+ *   NVKV_ERR_WORKSPACE before any HIP call.  Calls with one split per sequence use no scratch.
+ *   The first call on a device looks up the array's device address and clears its counters
+ *   with a kernel on `stream`; every completed call leaves them at zero again.
+ *   Every call on a GPU shares that GPU's array, which keeps the last call's contents: calls
+ *   that may overlap on one GPU (other streams, other threads) race and must be serialised by
+ *   the caller.
+ */
+NVKV_API nvkv_status nvkv_decode_append_attention_nvfp4_noalloc(const nvkv_layer *layer,
+                                        const uint16_t *q, const uint16_t *k_new,
+                                        const uint16_t *v_new, int32_t B, int32_t Hq,
+                                        const int32_t *page_table, int32_t max_pages_per_seq,
+                                        const int32_t *seq_lens, int32_t max_seq_len,
+                                        float sm_scale, float *out,
+                                        int32_t split_tokens, void *stream);
+
+/*
  * Causal multi-query attention over the packed cache: the last Tq positions of each sequence
  * attend to the cached keys up to and including their own position ([cache post] opening
  * paragraph: models are scored teacher-forced over full windows while attention reads the

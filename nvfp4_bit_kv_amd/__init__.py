@@ -11,7 +11,7 @@ without it.
 from ._native import (FMT_BF16, FMT_NVFP4, HEAD_DIM, K_HADAMARD, K_KLT, K_MSE_SCALE, K_SMOOTH, PART_CODES,  # noqa: F401
                       PART_SCALES, EXPORTED, LIB_PATH, Layer, NvkvError, cache_array_bytes,
                       cache_bytes_per_token, calibrate_key_basis, calibrate_key_basis_workspace_bytes,
-                      calibrate_key_smoothing, decode_append_attention_nvfp4,
+                      calibrate_key_smoothing, decode_append_attention_nvfp4, decode_append_attention_nvfp4_noalloc,
                       decode_attention_nvfp4,
                       decode_workspace_bytes, last_error, load, prefill_attention_nvfp4, quantize_append_kv,
                       status_string)

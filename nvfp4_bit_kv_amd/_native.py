@@ -23,7 +23,8 @@ HEAD_DIM = 128
 EXPORTED = ["nvkv_calibrate_key_smoothing", "nvkv_quantize_append_kv", "nvkv_decode_workspace_bytes",
             "nvkv_decode_attention_nvfp4", "nvkv_decode_append_attention_nvfp4", "nvkv_cache_array_bytes", "nvkv_cache_bytes_per_token",
             "nvkv_status_string", "nvkv_last_error", "nvkv_prefill_attention_nvfp4",
-            "nvkv_calibrate_key_basis_workspace_bytes", "nvkv_calibrate_key_basis"]
+            "nvkv_calibrate_key_basis_workspace_bytes", "nvkv_calibrate_key_basis",
+            "nvkv_decode_append_attention_nvfp4_noalloc"]
 
 
 class NvkvError(RuntimeError):
@@ -76,6 +77,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.nvkv_decode_append_attention_nvfp4.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, i32, i32, vp, i32, vp, i32,
                                                        f32, vp, vp, sz, i32, vp]
     lib.nvkv_decode_append_attention_nvfp4.restype = ctypes.c_int
+    lib.nvkv_decode_append_attention_nvfp4_noalloc.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, i32, i32, vp, i32,
+                                                               vp, i32, f32, vp, i32, vp]
+    lib.nvkv_decode_append_attention_nvfp4_noalloc.restype = ctypes.c_int
     lib.nvkv_prefill_attention_nvfp4.argtypes = [ctypes.POINTER(Layer), vp, i32, i32, i32, vp, i32, vp, i32, f32,
                                                  vp, vp]
     lib.nvkv_prefill_attention_nvfp4.restype = ctypes.c_int
@@ -157,6 +161,16 @@ def decode_append_attention_nvfp4(layer: Layer, q, k_new, v_new, B: int, Hq: int
                                                      max_seq_len, sm_scale, _ptr(out), _ptr(workspace),
                                                      workspace_bytes, split_tokens, _stream(stream)),
            "nvkv_decode_append_attention_nvfp4")
+
+
+def decode_append_attention_nvfp4_noalloc(layer: Layer, q, k_new, v_new, B: int, Hq: int, page_table,
+                                          max_pages_per_seq: int, seq_lens, max_seq_len: int, sm_scale: float,
+                                          out, split_tokens: int = 0, stream=None) -> None:
+    _check(load().nvkv_decode_append_attention_nvfp4_noalloc(ctypes.byref(layer), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                                             B, Hq, _ptr(page_table), max_pages_per_seq,
+                                                             _ptr(seq_lens), max_seq_len, sm_scale, _ptr(out),
+                                                             split_tokens, _stream(stream)),
+           "nvkv_decode_append_attention_nvfp4_noalloc")
 
 
 def prefill_attention_nvfp4(layer: Layer, q, B: int, Tq: int, Hq: int, page_table, max_pages_per_seq: int,

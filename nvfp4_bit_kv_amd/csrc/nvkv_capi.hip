@@ -150,10 +150,12 @@ size_t nvkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t m
 }
 
 namespace {
+// use_scratch: the allocation-free variant (the library's static per-device scratch instead of
+// a caller workspace).
 nvkv_status decode_common(const nvkv_layer* layer, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                           bool append, int32_t B, int32_t Hq, const int32_t* page_table, int32_t max_pages_per_seq,
                           const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, float* out, void* workspace,
-                          size_t workspace_bytes, int32_t split_tokens, void* stream) {
+                          size_t workspace_bytes, int32_t split_tokens, void* stream, bool use_scratch = false) {
   const nvkv_status st = check_layer(layer);
   if (st != NVKV_OK) return st;
   if (!q || !page_table || !seq_lens || !out) return fail(NVKV_ERR_NULL, "input/output pointer is NULL");
@@ -165,13 +167,28 @@ nvkv_status decode_common(const nvkv_layer* layer, const uint16_t* q, const uint
   if (split_tokens < 0 || split_tokens % 32 != 0) return fail(NVKV_ERR_SHAPE, "split_tokens must be a multiple of 32");
   if (!std::isfinite(sm_scale)) return fail(NVKV_ERR_SHAPE, "sm_scale must be finite");
   const nvkv::DecodePlan plan = nvkv::plan_decode(B, layer->num_kv_heads, max_seq_len, split_tokens, append);
-  if (plan.n_splits > 1) {
+  if (plan.n_splits > 1 && use_scratch) {
+    if (static_cast<int64_t>(B) * layer->num_kv_heads > static_cast<int64_t>(nvkv::kScratchUnits) ||
+        nvkv::decode_partial_bytes(B, layer->num_kv_heads, plan) > nvkv::kScratchPartialBytes)
+      return fail(NVKV_ERR_WORKSPACE, "the call needs more split state than the static scratch holds "
+                                      "(B * Hkv <= 2048 and at most 7 MiB of split partials)");
+  } else if (plan.n_splits > 1) {
     const size_t need = nvkv::decode_workspace_bytes(B, layer->num_kv_heads, plan);
     if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
       return fail(NVKV_ERR_WORKSPACE, "workspace missing, too small or not 256-byte aligned");
   }
   (void)hipGetLastError();
   const hipStream_t hs = static_cast<hipStream_t>(stream);
+  nvkv::DecodeWs ws{nullptr, nullptr, nullptr};
+  if (plan.n_splits > 1) {
+    if (use_scratch) {
+      const nvkv_status s0 = hip_status(nvkv::scratch_decode_workspace(B, layer->num_kv_heads, plan, hs, &ws),
+                                        "static scratch set-up");
+      if (s0 != NVKV_OK) return s0;
+    } else {
+      ws = nvkv::carve_decode_workspace(workspace, B, layer->num_kv_heads, plan);
+    }
+  }
   if (append && plan.pipe2) {
     // Long splits: the decode dominates and the fused kernel would give up a cache
     // wavefront, so the new tokens go in with the append kernel first (same effect).
@@ -183,12 +200,12 @@ nvkv_status decode_common(const nvkv_layer* layer, const uint16_t* q, const uint
     if (s1 != NVKV_OK) return s1;
     nvkv::DecodePlan dplan = nvkv::plan_decode(B, layer->num_kv_heads, max_seq_len, split_tokens, false);
     return hip_status(nvkv::launch_decode(*layer, q, nullptr, nullptr, B, Hq, page_table, max_pages_per_seq,
-                                          seq_lens, max_seq_len, sm_scale, out, workspace, dplan, hs),
+                                          seq_lens, max_seq_len, sm_scale, out, ws, dplan, hs),
                       "decode-append: decode launch");
   }
   return hip_status(nvkv::launch_decode(*layer, q, append ? k_new : nullptr, append ? v_new : nullptr, B, Hq,
                                         page_table, max_pages_per_seq, seq_lens, max_seq_len, sm_scale, out,
-                                        workspace, plan, hs),
+                                        ws, plan, hs),
                     append ? "decode-append launch" : "decode launch");
 }
 }  // namespace
@@ -210,6 +227,16 @@ nvkv_status nvkv_decode_append_attention_nvfp4(const nvkv_layer* layer, const ui
                                                int32_t split_tokens, void* stream) {
   return decode_common(layer, q, k_new, v_new, true, B, Hq, page_table, max_pages_per_seq, seq_lens, max_seq_len,
                        sm_scale, out, workspace, workspace_bytes, split_tokens, stream);
+}
+
+nvkv_status nvkv_decode_append_attention_nvfp4_noalloc(const nvkv_layer* layer, const uint16_t* q,
+                                                       const uint16_t* k_new, const uint16_t* v_new, int32_t B,
+                                                       int32_t Hq, const int32_t* page_table,
+                                                       int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                                       int32_t max_seq_len, float sm_scale, float* out,
+                                                       int32_t split_tokens, void* stream) {
+  return decode_common(layer, q, k_new, v_new, true, B, Hq, page_table, max_pages_per_seq, seq_lens, max_seq_len,
+                       sm_scale, out, nullptr, 0, split_tokens, stream, true);
 }
 
 nvkv_status nvkv_prefill_attention_nvfp4(const nvkv_layer* layer, const uint16_t* q, int32_t B, int32_t Tq,

@@ -35,6 +35,9 @@
 // Latency: the query row, page-table entries and the first two iterations' cache loads are
 // issued at kernel start, before the sequence length is known; later iterations are
 // software-pipelined two deep.
+#include <mutex>
+#include <unordered_map>
+
 #include "nvkv_device.hpp"
 #include "nvkv_encode.hpp"
 #include "nvkv_internal.hpp"
@@ -774,21 +777,92 @@ DecodePlan plan_decode(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t spli
 
 namespace {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+size_t counter_bytes(int32_t B, int32_t Hkv) {
+  return align256(static_cast<size_t>(B) * Hkv * kCounterStride * sizeof(unsigned));
 }
+size_t ml_bytes(int32_t B, int32_t Hkv, const DecodePlan& plan) {
+  return align256(static_cast<size_t>(B) * Hkv * plan.n_splits * 4 * 2 * sizeof(float));
+}
+}  // namespace
 
 // Workspace layout: [arrival counters: B*Hkv, 256 bytes apart][(m, l) per split and head]
 // [O per split and head].  The counters come first so that their place does not depend on the split
 // count: calls with different split counts may share a workspace.
-size_t decode_workspace_bytes(int32_t B, int32_t Hkv, const DecodePlan& plan) {
+size_t decode_partial_bytes(int32_t B, int32_t Hkv, const DecodePlan& plan) {
+  if (plan.n_splits <= 1) return 0;
   const size_t slots = static_cast<size_t>(B) * Hkv * plan.n_splits * 4;
-  return align256(static_cast<size_t>(B) * Hkv * kCounterStride * sizeof(unsigned)) + align256(slots * 2 * sizeof(float)) +
-         align256(slots * kHeadDim * sizeof(float));
+  return ml_bytes(B, Hkv, plan) + align256(slots * kHeadDim * sizeof(float));
+}
+
+size_t decode_workspace_bytes(int32_t B, int32_t Hkv, const DecodePlan& plan) {
+  return counter_bytes(B, Hkv) + decode_partial_bytes(B, Hkv, plan);
+}
+
+DecodeWs carve_decode_workspace(void* workspace, int32_t B, int32_t Hkv, const DecodePlan& plan) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  DecodeWs w;
+  w.counters = reinterpret_cast<unsigned*>(ws);
+  w.ml = reinterpret_cast<float*>(ws + counter_bytes(B, Hkv));
+  w.o = reinterpret_cast<float*>(ws + counter_bytes(B, Hkv) + ml_bytes(B, Hkv, plan));
+  return w;
+}
+
+// ---------------------------------------------------------------------------------------
+// Static scratch of the allocation-free entry point (for callers that cannot allocate).
+// One array per GPU (each device that loads the library holds its own copy until the process
+// ends).  Layout: [arrival counters: kScratchUnits, 256 bytes apart][partials].  The counter
+// region has a fixed size, so partials of one call never land on counters of another.  Every
+// call on a device shares its array: calls that overlap on one GPU race.
+// ---------------------------------------------------------------------------------------
+constexpr size_t kScratchCounterBytes = kScratchUnits * kCounterStride * sizeof(unsigned);
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchCounterBytes + kScratchPartialBytes];
+
+__global__ void k_clear_words(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+namespace {
+std::mutex g_scratch_mu;
+std::unordered_map<int, uint8_t*> g_scratch_addr;   // device -> device address of `scratch`
+}  // namespace
+
+hipError_t scratch_decode_workspace(int32_t B, int32_t Hkv, const DecodePlan& plan, hipStream_t stream,
+                                    DecodeWs* ws) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  uint8_t* base = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    auto it = g_scratch_addr.find(dev);
+    if (it != g_scratch_addr.end()) {
+      base = it->second;
+    } else {
+      // the array's name is a host-side stand-in: its device address comes from the runtime,
+      // once per device, with that device current
+      void* ptr = nullptr;
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      base = static_cast<uint8_t*>(ptr);
+      // the counters must start at zero (every completed call leaves them at zero); cleared by a
+      // kernel on the caller's stream, which a graph capture may record
+      const uint32_t words = static_cast<uint32_t>(kScratchCounterBytes / sizeof(uint32_t));
+      hipLaunchKernelGGL(k_clear_words, dim3(64), dim3(256), 0, stream, reinterpret_cast<uint32_t*>(base), words);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      g_scratch_addr.emplace(dev, base);
+    }
+  }
+  ws->counters = reinterpret_cast<unsigned*>(base);
+  ws->ml = reinterpret_cast<float*>(base + kScratchCounterBytes);
+  ws->o = reinterpret_cast<float*>(base + kScratchCounterBytes + ml_bytes(B, Hkv, plan));
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                          int32_t B, int32_t Hq, const int32_t* page_table, int32_t max_pages_per_seq,
-                         const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, float* out, void* workspace,
-                         const DecodePlan& plan, hipStream_t stream) {
+                         const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, float* out,
+                         const DecodeWs& ws, const DecodePlan& plan, hipStream_t stream) {
   DecodeArgs a{};
   a.k_new = k_new;
   a.v_new = v_new;
@@ -807,12 +881,9 @@ hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, const uint16_t*
   a.page_table = page_table;
   a.seq_lens = seq_lens;
   a.out = out;
-  const size_t slots = static_cast<size_t>(B) * L.num_kv_heads * plan.n_splits * 4;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const size_t cnt_bytes = align256(static_cast<size_t>(B) * L.num_kv_heads * kCounterStride * sizeof(unsigned));
-  a.counters = reinterpret_cast<unsigned*>(ws);
-  a.ws_ml = reinterpret_cast<float*>(ws + cnt_bytes);
-  a.ws_o = reinterpret_cast<float*>(ws + cnt_bytes + align256(slots * 2 * sizeof(float)));
+  a.counters = ws.counters;
+  a.ws_ml = ws.ml;
+  a.ws_o = ws.o;
   a.hkv = L.num_kv_heads;
   a.hq = Hq;
   a.page_size = L.page_size;

@@ -37,11 +37,34 @@ struct DecodePlan {
 DecodePlan plan_decode(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t split_tokens, bool append);
 size_t decode_workspace_bytes(int32_t B, int32_t Hkv, const DecodePlan& plan);
 
+// Where a decode call keeps its cross-split state: one arrival counter per (sequence, KV head),
+// 256 bytes apart (zero between calls), and the per-split partials (m, l) and O.
+struct DecodeWs {
+  unsigned* counters;
+  float* ml;
+  float* o;
+};
+// The layout inside a caller's workspace of decode_workspace_bytes(B, Hkv, plan) bytes.
+DecodeWs carve_decode_workspace(void* workspace, int32_t B, int32_t Hkv, const DecodePlan& plan);
+
+// The allocation-free variant keeps its cross-split state in a static device array of fixed
+// size, one per GPU: arrival counters for up to kScratchUnits (sequence, KV head) units, then
+// kScratchPartialBytes of partials.
+constexpr size_t kScratchUnits = 2048;
+constexpr size_t kScratchPartialBytes = size_t(7) << 20;
+// Bytes of partials a plan needs (0 with one split).
+size_t decode_partial_bytes(int32_t B, int32_t Hkv, const DecodePlan& plan);
+// The static scratch of the current device, carved for a call (B * Hkv <= kScratchUnits and
+// decode_partial_bytes <= kScratchPartialBytes, checked by the caller).  The first call on a
+// device looks up the array's device address and clears its counters on `stream`.
+hipError_t scratch_decode_workspace(int32_t B, int32_t Hkv, const DecodePlan& plan, hipStream_t stream,
+                                    DecodeWs* ws);
+
 // k_new / v_new non-null: fused append of the new token of each sequence (plan.append).
 hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                          int32_t B, int32_t Hq, const int32_t* page_table, int32_t max_pages_per_seq,
-                         const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, float* out, void* workspace,
-                         const DecodePlan& plan, hipStream_t stream);
+                         const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, float* out,
+                         const DecodeWs& ws, const DecodePlan& plan, hipStream_t stream);
 
 // Causal attention of the last Tq positions of each sequence over the cache (no workspace).
 hipError_t launch_prefill_attention(const nvkv_layer& L, const uint16_t* q, int32_t B, int32_t Tq, int32_t Hq,

@@ -28,7 +28,7 @@ def clib():
 
 def test_every_declared_symbol_is_exported(clib):
     decl = _declared_symbols()
-    assert len(decl) == 12, decl
+    assert len(decl) == 13, decl
     assert sorted(decl) == sorted(nk.EXPORTED)
     for name in decl:
         assert hasattr(clib, name), name
@@ -133,6 +133,28 @@ def test_decode_append_argument_errors(clib):
     need = nk.decode_workspace_bytes(4, 32, 8, 4096, 32)
     assert call(msl=4096, sp=32, wsb=need - 1) == 4
     assert call(lay=_layer(k_fmt=7)) == 3
+
+
+def test_decode_append_noalloc_argument_errors(clib):
+    """The allocation-free fused step validates like the fused step, and rejects calls whose
+    split state exceeds its static scratch (B * Hkv <= 2048, at most 7 MiB of partials)
+    before any HIP call."""
+    L = _layer()
+    f = clib.nvkv_decode_append_attention_nvfp4_noalloc
+    ok = dict(q=0x10, kn=0x10, vn=0x10, B=4, Hq=32, pt=0x10, mp=4, sl=0x10, msl=64, sm=0.1, out=0x10, sp=0)
+    def call(lay=L, **kw):
+        a = dict(ok, **kw)
+        return f(ctypes.byref(lay) if lay is not None else None, a["q"], a["kn"], a["vn"], a["B"], a["Hq"], a["pt"],
+                 a["mp"], a["sl"], a["msl"], a["sm"], a["out"], a["sp"], None)
+    assert call(lay=None) == 1
+    assert call(kn=None) == 1 and call(vn=None) == 1 and call(q=None) == 1 and call(out=None) == 1
+    assert call(B=0) == 2 and call(Hq=16) == 3 and call(sp=48) == 2 and call(sm=float("nan")) == 2
+    assert call(lay=_layer(k_fmt=7)) == 3
+    # 257 x 8 = 2056 (sequence, KV head) units with two splits each: more counters than the scratch holds
+    assert call(B=257, msl=64, sp=32, mp=4) == 4
+    # 64 x 8 units x 1024 splits x 4 heads x 520 B of partials: far beyond 7 MiB
+    assert call(B=64, msl=32768, sp=32, mp=2048) == 4
+    assert "static scratch" in nk.last_error()
 
 
 def test_prefill_attention_argument_errors(clib):
