@@ -66,6 +66,13 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (5 times): the reference kernel for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counts to bytes")
+    ap.add_argument("--trace-phases", action="store_true",
+                    help="decode workloads: also run the phase-stamped instance of the fused decode kernel "
+                         "(libnvkv_bench.so) over one step and print its phase timeline")
+    ap.add_argument("--trace-dump", default="",
+                    help="with --trace-phases: also save the raw stamps (uint64 [layers][workgroups][40]) to this .npy file")
+    ap.add_argument("--no-stream-reference", action="store_true",
+                    help="skip the plain streaming read of the same cache bytes (reference for stream_frac)")
     ap.add_argument("--separate", action="store_true",
                     help="decode step as two calls per layer (quantize_append_kv, then "
                          "decode_attention_nvfp4) instead of the fused decode_append_attention_nvfp4")
@@ -812,6 +819,149 @@ def decode_cpu_baseline(wl, budget_s=12.0):
                 oracle_effective_gbs=round(wl.step_bytes() / step_s / 1e9, 6))
 
 
+# ---------------------------------------------------------------------------------------
+# Measurement helpers (libnvkv_bench.so: a plain streaming-read kernel and the phase-stamped
+# decode instance; not the library's C ABI)
+# ---------------------------------------------------------------------------------------
+_BENCH_LIB = None
+
+
+def bench_lib():
+    global _BENCH_LIB
+    if _BENCH_LIB is None:
+        import ctypes
+        path = os.path.join(ROOT, "nvfp4_bit_kv_amd", "libnvkv_bench.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build with `python -m nvfp4_bit_kv_amd.build`")
+        lib = ctypes.CDLL(path)
+        vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+        lib.nvkvb_stream_read.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int, vp]
+        lib.nvkvb_stream_read.restype = ctypes.c_int
+        lib.nvkvb_decode_plan.argtypes = [i32, i32, i32, i32, i32, vp]
+        lib.nvkvb_decode_plan.restype = None
+        from nvfp4_bit_kv_amd import Layer
+        lib.nvkvb_decode_trace.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, i32, i32, i32, vp, i32, vp, i32, f32,
+                                           vp, vp, i32, vp, vp]
+        lib.nvkvb_decode_trace.restype = ctypes.c_int
+        _BENCH_LIB = lib
+    return _BENCH_LIB
+
+
+def stream_reference(torch, wl, reps=10, grids=(256, 512, 1024, 2048)):
+    """A plain streaming read of exactly the cache arrays one decode launch reads (codes and
+    scales of K and V of the layer), as a graph of one launch per layer and cache copy replayed
+    between HIP events; the fastest of a few grid sizes.  Returns (seconds per launch, bytes per
+    launch, grid)."""
+    import ctypes
+    lib = bench_lib()
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    best = None
+    for grid in grids:
+        keep = []
+
+        def launch_all(cp, grid=grid):
+            for l in range(wl.L):
+                cache, _ = wl.caches[cp][l]
+                arrs = [t for t in (cache.k_data, cache.k_scales, cache.v_data, cache.v_scales) if t is not None]
+                ptrs = (ctypes.c_void_p * len(arrs))(*[t.data_ptr() for t in arrs])
+                sizes = (ctypes.c_size_t * len(arrs))(*[t.numel() * t.element_size() for t in arrs])
+                keep.append((ptrs, sizes))
+                st = lib.nvkvb_stream_read(ptrs, sizes, len(arrs), sink.data_ptr(), grid,
+                                           torch.cuda.current_stream().cuda_stream)
+                if st != 0:
+                    raise RuntimeError(f"stream read launch failed: {st}")
+        graphs = [capture(torch, lambda cp=cp: launch_all(cp)) for cp in range(wl.copies)]
+        for gr in graphs:
+            gr.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for r in range(reps):
+            ev[r][0].record(stream)
+            graphs[r % len(graphs)].replay()
+            ev[r][1].record(stream)
+        torch.cuda.synchronize()
+        t = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3 / wl.L
+        if best is None or t < best[0]:
+            best = (t, grid)
+        del graphs
+    cache, _ = wl.caches[0][0]
+    nbytes = sum(t.numel() * t.element_size() for t in (cache.k_data, cache.k_scales, cache.v_data, cache.v_scales)
+                 if t is not None)
+    return best[0], nbytes, best[1]
+
+
+TRACE_SLOTS = 48
+TICK_US = 0.01            # s_memrealtime runs at 100 MHz
+
+
+def trace_phases(torch, wl, dump=""):
+    """Phase timeline of the fused decode launch: the phase-stamped instance of the kernel over
+    all layers of cache copy 0, captured as one graph of back-to-back launches (as timed) and
+    replayed twice; stamps of the second replay.  Reported per launch as medians over its
+    workgroups (times in microseconds after the launch's first workgroup started, and
+    per-workgroup durations of the phases), then the median and maximum over the launches."""
+    import ctypes
+    lib = bench_lib()
+    fused = wl.mode == "fused"
+    plan = (ctypes.c_int32 * 3)()
+    lib.nvkvb_decode_plan(wl.B, wl.hkv, wl.T, wl.split_tokens, int(fused), plan)
+    n_splits, waves, pipe2 = int(plan[0]), int(plan[1]), int(plan[2])
+    if fused and pipe2:
+        return {"skipped": "long splits: the fused call issues two launches"}
+    n_wg = n_splits * wl.hkv * wl.B
+    buf = torch.zeros((wl.L, n_wg, TRACE_SLOTS), dtype=torch.int64, device="cuda")
+
+    def run():
+        for l in range(wl.L):
+            cache, Ls = wl.caches[0][l]
+            st = lib.nvkvb_decode_trace(Ls, wl.q[l].data_ptr(), wl.k_new[l].data_ptr(), wl.v_new[l].data_ptr(),
+                                        int(fused), wl.B, wl.hq, wl.table.data_ptr(), wl.pps, wl.seq_lens.data_ptr(),
+                                        wl.T, SM_SCALE, wl.out[l].data_ptr(), wl.ws.data_ptr(), wl.split_tokens,
+                                        buf[l].data_ptr(), torch.cuda.current_stream().cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"traced decode launch failed: {st}")
+    g = capture(torch, run)
+    g.replay()
+    g.replay()
+    torch.cuda.synchronize()
+    raw = buf.cpu().numpy().view(np.uint64)
+    if dump:
+        np.save(dump, raw)
+    t = raw.astype(np.float64)                                         # [L][wg][slot]
+    med = lambda x: float(np.nanmedian(x)) if np.isfinite(x).any() else np.nan
+    rows = []
+    for l in range(wl.L):
+        tl = t[l]
+        t0 = tl[:, 0].min()
+        r = np.where(tl > 0, (tl - t0) * TICK_US, np.nan)
+        merger = (tl[:, 7].astype(np.uint64) & np.uint64(1)) == 1
+        data_first = np.nanmin(r[:, 16:32], axis=1)
+        data_last = np.nanmax(r[:, 16:32], axis=1)
+        done = np.nanmax(r[:, 32:48], axis=1)
+        last = np.nanmax(np.where(np.isfinite(r[:, 6]), r[:, 6], r[:, 4]))
+        rows.append(dict(
+            first_wg_to_last_wg_start=np.nanmax(r[:, 0]),
+            prologue_done=med(r[:, 1]), first_data=med(data_first), last_data=med(data_last),
+            compute_done=med(done), compute_done_last_wg=np.nanmax(done),
+            partials_issued=med(r[:, 8]), partials_acked=med(r[:, 3]), arrival_counted=med(r[:, 4]),
+            merger_loaded=med(r[merger, 9]), merger_folded=med(r[merger, 5]), end=last,
+            gap_to_next_launch=((t[l + 1][:, 0].min() - tl[:, 6].max()) * TICK_US if l + 1 < wl.L else np.nan),
+            d_compute=med(done - data_last), d_workgroup_merge=med(r[:, 8] - done), d_store_ack=med(r[:, 3] - r[:, 8]),
+            d_arrival=med(r[:, 4] - r[:, 3]), d_merger_load=med(r[merger, 9] - r[merger, 4]),
+            d_merger_fold_store=med(r[merger, 6] - r[merger, 9]),
+        ))
+    out = {"launches": wl.L, "workgroups": n_wg, "waves_per_workgroup": waves, "n_splits": n_splits,
+           "unit": "us; times after the first workgroup of the launch started, d_* are per-workgroup phase "
+                   "durations (s_memrealtime, 100 MHz); medians over a launch's workgroups, then median and "
+                   "max over launches"}
+    for k in rows[0]:
+        vals = np.array([r[k] for r in rows], dtype=np.float64)
+        vals = vals[np.isfinite(vals)]
+        out[k] = {"median": round(float(np.median(vals)), 3), "max": round(float(np.max(vals)), 3)} if vals.size else None
+    return out
+
+
 COPY_BYTES = 256 << 20
 
 
@@ -855,6 +1005,23 @@ def traffic_per_launch(wl):
     if rec.get("kernel_source_sha256") != kernel_source_hash() or rec.get("kernel") != wl.kernel_label:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def sq_counters(wl):
+    """VALU / MFMA activity of the dominant kernel from the committed rocprofv3 SQ-counter
+    summary of this workload (profiles/sq_<workload>.md), or None when there is none or the
+    kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"sq_{wl.name}.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        text = f.read()
+    if "```json" not in text:
+        return None
+    rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return {k: rec[k] for k in ("valu_busy", "mfma_busy", "valu_insts_per_wave", "mfma_insts_per_wave") if k in rec}
 
 
 def main():
@@ -915,6 +1082,20 @@ def main():
         sweep_splits(torch, wl, [int(x) for x in args.sweep_splits.split(",")])
     if args.copy_calibration:
         copy_calibration(torch)
+    stream_ref = None
+    if isinstance(wl, DecodeStep) and not args.no_stream_reference and not args.profile_pass:
+        print("[bench] plain streaming read of the same cache bytes", file=sys.stderr, flush=True)
+        st_s, st_bytes, st_grid = stream_reference(torch, wl)
+        st_gbs = st_bytes / st_s / 1e9
+        stream_ref = {"kernel": "k_stream_read (libnvkv_bench.so): every 16-byte word of the layer's K/V codes and "
+                                "scales read once, non-temporal, one launch per layer, graph of back-to-back launches",
+                      "bytes_per_launch": st_bytes, "avg_launch_us": round(st_s * 1e6, 3),
+                      "achieved_gbs": round(st_gbs, 2), "grid": st_grid}
+    phases = None
+    if args.trace_phases and isinstance(wl, DecodeStep):
+        print("[bench] phase-stamped decode instance", file=sys.stderr, flush=True)
+        phases = trace_phases(torch, wl, args.trace_dump)
+        print("[bench] phase timeline: " + json.dumps(phases), file=sys.stderr, flush=True)
     print("[bench] oracle check / cpu baseline", file=sys.stderr, flush=True)
     check = None if args.no_check else wl.check()
     base = None if args.no_cpu_baseline else wl.cpu_baseline()
@@ -954,6 +1135,10 @@ def main():
             **({"flops_per_launch": wl.launch_flops()} if mfma else {}),
         },
         "cpu_baseline": base,
+        "stream_reference": stream_ref,
+        "stream_frac": (round(achieved / stream_ref["achieved_gbs"], 4) if stream_ref and not mfma else None),
+        "sq_counters": sq_counters(wl),
+        "phase_timeline": phases,
         "graph_replay_matches_eager": replay_ok,
         "timing_protocol": protocol,
         "separate_calls_ms_per_step": separate_ms,

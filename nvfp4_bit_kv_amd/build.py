@@ -29,7 +29,13 @@ SOURCES = {
     "nvkv_klt.hip": ["-ffp-contract=off"],
     "nvkv_decode.hip": ["-fno-honor-nans"],
     "nvkv_prefill.hip": ["-fno-honor-nans"],
+    "nvkv_bench.hip": [],
 }
+# The library proper, and the bench's measurement helpers (a plain streaming-read kernel and
+# the phase-stamped decode instance; linked with the same decode object, loaded only by the bench).
+LIB_OBJECTS = ["nvkv_capi.hip", "nvkv_quantize.hip", "nvkv_klt.hip", "nvkv_decode.hip", "nvkv_prefill.hip"]
+BENCH_LIB = os.path.join(PKG, "libnvkv_bench.so")
+BENCH_OBJECTS = ["nvkv_bench.hip", "nvkv_decode.hip"]
 
 
 def _hipcc() -> str:
@@ -63,14 +69,16 @@ def build(verbose: bool = False) -> str:
     if failed:
         msg = "\n".join(f"--- {s} ---\n{o}" for s, o in failed)
         raise RuntimeError(f"hipcc failed:\n{msg}")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}")
-    os.replace(tmp, LIB)
+    obj_of = {src: os.path.join(BUILD, src.replace(".hip", ".o")) for src in SOURCES}
+    for lib, members in ((LIB, LIB_OBJECTS), (BENCH_LIB, BENCH_OBJECTS)):
+        tmp = lib + ".tmp"
+        cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *[obj_of[m] for m in members], "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stdout}")
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -77,7 +77,58 @@ struct DecodeArgs {
   uint8_t* v_codes_w;
   uint8_t* v_scales_w;
   const float* basis;         // KLT basis [Hkv][128][128] (NVKV_K_KLT), staged in dynamic LDS
+  uint64_t* trace;            // phase stamps of the measurement instance (TRACE), else unused
 };
+
+// Phase stamps of the measurement instance k_decode<..., TRACE = true>: s_memrealtime values
+// (a 100 MHz counter common to the whole chip) per workgroup, kTraceSlots apart, in the
+// linear workgroup order split + n_splits * (h + Hkv * b).  Slots:
+//   0 entry; 1 query prologue barrier passed; 2 first workgroup (LDS) merge barrier passed;
+//   3 split partials acknowledged (after the workgroup barrier); 4 arrival counter returned;
+//   5 merging workgroup: splits loaded and folded, output stores issued; 6 output stores
+//   complete; 7 identity: bit 0 = merging workgroup, bits 8..39 = HW_ID, bits 40..47 =
+//   XCC_ID; 8 split partial stores issued; 9 merging workgroup: split partials in registers;
+//   16 + w: wavefront w's first cache data in registers; 32 + w: wavefront w's loop done
+//   (w < 16).  Slots a workgroup never reaches stay 0.
+constexpr int kTraceSlots = 48;
+struct TraceStamps {
+  uint64_t entry = 0, prologue = 0, lds_merge = 0, acked = 0, counted = 0, folded = 0, stored = 0, ident = 0;
+  uint64_t issue = 0, loaded = 0;
+  uint64_t data = 0, done = 0;     // this wavefront's
+};
+// the scheduling barriers keep the stamp where it is written relative to the code around it
+__device__ __forceinline__ uint64_t stamp_now() {
+  __builtin_amdgcn_sched_barrier(0);
+  const uint64_t t = __builtin_amdgcn_s_memrealtime();
+  __builtin_amdgcn_sched_barrier(0);
+  return t;
+}
+__device__ __forceinline__ uint64_t hw_identity() {
+  uint32_t hw, xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  return (static_cast<uint64_t>(hw) << 8) | (static_cast<uint64_t>(xcc & 0xFFu) << 40);
+}
+__device__ __forceinline__ void trace_write(const DecodeArgs& a, const TraceStamps& t, int wave, int tid) {
+  const int64_t wg = blockIdx.x + static_cast<int64_t>(gridDim.x) * (blockIdx.y + static_cast<int64_t>(gridDim.y) * blockIdx.z);
+  uint64_t* r = a.trace + wg * kTraceSlots;
+  if ((tid & 63) == 0 && wave < 16) {
+    r[16 + wave] = t.data;
+    r[32 + wave] = t.done;
+  }
+  if (tid == 0) {
+    r[0] = t.entry;
+    r[1] = t.prologue;
+    r[2] = t.lds_merge;
+    r[3] = t.acked;
+    r[4] = t.counted;
+    r[5] = t.folded;
+    r[6] = t.stored;
+    r[7] = t.ident;
+    r[8] = t.issue;
+    r[9] = t.loaded;
+  }
+}
 
 // Online-softmax state of one wavefront.  Lane (c, g) serves query head g: its running max,
 // its share of the denominator and the PV accumulator rows 4g..4g+3 = (head g, term 0..3).
@@ -212,8 +263,9 @@ constexpr int kMaxSplits = 1024;
 // otherwise queue on one or two cache lines (measured: 0.8 us per launch at 4 x 2304).
 constexpr int kCounterStride = 64;
 
-template <int G>
-__device__ __forceinline__ void merge_splits(const DecodeArgs& a, int64_t unit, int i, int d0, float gv) {
+template <int G, bool TRACE = false>
+__device__ __forceinline__ void merge_splits(const DecodeArgs& a, int64_t unit, int i, int d0, float gv,
+                                             uint64_t* loaded = nullptr) {
   const int n = a.n_splits;
   float M = -INFINITY, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
   for (int s0 = 0; s0 < n; s0 += G) {
@@ -224,22 +276,30 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs& a, int64_t unit, 
       const int64_t slot = (unit * n + sp) * 4 + i;
       ml[k] = load_coherent_f2(a.ws_ml + slot * 2);
       o[k] = load_coherent_f2(a.ws_o + slot * kHeadDim + d0);
-      if (s0 + k >= n) ml[k].y = 0.0f;                // padding entry: no weight
+      if (s0 + k >= n) ml[k] = make_float2(-INFINITY, 0.0f);   // padding entry: no weight
     }
+    if constexpr (TRACE) {
+      if (s0 == 0) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        *loaded = __builtin_amdgcn_s_memrealtime();
+      }
+    }
+    // a split without tokens carries m = -inf and l = 0; raw exp2 gives exp2(-inf) = 0 and
+    // weights in (0, 1]
     float mx = M;
 #pragma unroll
-    for (int k = 0; k < G; ++k) mx = ml[k].y > 0.0f ? fmaxf(mx, ml[k].x) : mx;
-    if (mx == -INFINITY) continue;                     // nothing in this group or before
-    const float sc = exp2f(M - mx);                    // 0 while M is still -inf
+    for (int k = 0; k < G; ++k) mx = fmaxf(mx, ml[k].x);
+    const float mr = mx == -INFINITY ? 0.0f : mx;
+    const float sc = __builtin_amdgcn_exp2f(M - mr);   // 0 while M is still -inf
     L *= sc;
     o0 *= sc;
     o1 *= sc;
 #pragma unroll
     for (int k = 0; k < G; ++k) {
-      const float w = ml[k].y > 0.0f ? exp2f(ml[k].x - mx) : 0.0f;
-      L += w * ml[k].y;
-      o0 += w * o[k].x;
-      o1 += w * o[k].y;
+      const float w = __builtin_amdgcn_exp2f(ml[k].x - mr);
+      L = __builtin_fmaf(w, ml[k].y, L);
+      o0 = __builtin_fmaf(w, o[k].x, o0);
+      o1 = __builtin_fmaf(w, o[k].y, o1);
     }
     M = mx;
   }
@@ -483,8 +543,12 @@ __device__ __forceinline__ void new_token_update(const NewTokenStage& st, const 
 // wavefronts read the split without that position.
 // KLT: compiled with the KLT key basis (basis staging and both rotations); the other
 // instances carry none of that code.
-template <bool KBF16, bool PIPE2, bool APPEND, bool KLT>
+// TRACE: the measurement instance, which also records the phase stamps above (and waits for
+// its first cache data explicitly before the first iteration, to stamp its arrival).
+template <bool KBF16, bool PIPE2, bool APPEND, bool KLT, bool TRACE = false>
 __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
+  TraceStamps ts;
+  if constexpr (TRACE) ts.entry = stamp_now();
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -589,6 +653,7 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
     if (lane == 0) q_descale[wave] = descale;
   }
   __syncthreads();
+  if constexpr (TRACE) ts.prologue = stamp_now();
 
   SoftmaxState st;
   st.m_ref = -INFINITY;
@@ -612,6 +677,12 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
     // Software pipeline: two register buffers hold the next two iterations' cache data and
     // the page entries of the iteration after them are already loaded, so neither the
     // vector loads nor the page lookups sit on the critical path.
+    if constexpr (TRACE) {
+      if (t0 < t_read) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        ts.data = stamp_now();
+      }
+    }
     if constexpr (!PIPE2) {
       while (t0 < t_read) {
         valid_tokens(hb0, t0, t_read, c, vm);
@@ -642,28 +713,50 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
         pnext = load_pages(a, ptab, t0 + 2 * step, t_read);
       }
     }
+    if constexpr (TRACE) ts.done = stamp_now();
     if (owns_new && app_wave) {
+      // the extra wavefront is the youngest on its SIMD: raised issue priority keeps it from
+      // waiting behind the cache wavefronts there, whose workgroup merge waits for it
+      __builtin_amdgcn_s_setprio(2);
       const bool ok = static_cast<uint32_t>(new_pg) < static_cast<uint32_t>(a.num_pages);
       if (!nt_early) new_token_transform<KBF16>(a, lane, nreg, nt_stage, basis_dyn, ny);
       new_token_encode<KBF16>(a, h, lane, nreg, ny, new_pg, new_off, ok, nt_stage);
       if (ok) new_token_update<KBF16>(nt_stage, q_lds, q_descale, lane, ln, st);
+      __builtin_amdgcn_s_setprio(0);
     }
   }
 
   // ---------------- wavefront partials -> LDS -> workgroup partial ----------------
-  const float l_tot = row16_sum(st.l_acc);
-  if (c == 0) {
-    red_m[wave][g] = st.m_ref;
-    red_l[wave][g] = l_tot;
-  }
+  // Every wavefront publishes (m, l, o) per head; the slots of wavefronts that do not exist
+  // are filled with empty entries (m = -inf, l = 0, o = 0) by the existing ones, so the owner
+  // threads combine a fixed number of slots without selects, in a fixed order (the result is
+  // the same on every run).  The combination is VALU work on the owner wavefronts only (one
+  // per SIMD), so it is kept short: raw exp2 (exp2(-inf) = 0; weights lie in (0, 1]).
   {
+    constexpr int kRed = PIPE2 ? 8 : kMaxWaves;
+    const float l_tot = row16_sum(st.l_acc);
+    if (c == 0) {
+      red_m[wave][g] = st.m_ref;
+      red_l[wave][g] = l_tot;
+    }
     float4* dst = reinterpret_cast<float4*>(&red_o[wave][g][8 * c]);
     dst[0] = make_float4(st.acc[0][0] + st.acc[0][1], st.acc[1][0] + st.acc[1][1],
                          st.acc[2][0] + st.acc[2][1], st.acc[3][0] + st.acc[3][1]);
     dst[1] = make_float4(st.acc[4][0] + st.acc[4][1], st.acc[5][0] + st.acc[5][1],
                          st.acc[6][0] + st.acc[6][1], st.acc[7][0] + st.acc[7][1]);
+    // empty entries in slots nw .. kRed-1: wavefront w fills slots nw + w, 2 nw + w, ...
+    for (int zs = nw + wave; zs < kRed; zs += nw) {
+      float4* z = reinterpret_cast<float4*>(&red_o[zs][g][8 * c]);
+      z[0] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      z[1] = z[0];
+      if (c == 0) {
+        red_m[zs][g] = -INFINITY;
+        red_l[zs][g] = 0.0f;
+      }
+    }
   }
   __syncthreads();
+  if constexpr (TRACE) ts.lds_merge = stamp_now();
 
   // threads 0..255 own (head i, dims d0, d0+1) in the merges; the others only take part in
   // the barriers
@@ -672,8 +765,6 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   const int d0 = 2 * (tid & 63);
   float M = -INFINITY, Lw = 0.0f, o0 = 0.0f, o1 = 0.0f;
   if (owner) {
-    // Every wavefront's entries are read at once and without branches (a loop of dependent
-    // LDS reads costs a round trip per read); entries of wavefronts >= nw are replaced.
     constexpr int kRed = PIPE2 ? 8 : kMaxWaves;
     float mw[kRed], lw[kRed];
     float2 ow[kRed];
@@ -683,22 +774,15 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
       lw[w] = red_l[w][i];
       ow[w] = *reinterpret_cast<const float2*>(&red_o[w][i][d0]);
     }
-    __builtin_amdgcn_sched_barrier(0);      // keep the reads together, ahead of the arithmetic
-#pragma unroll
-    for (int w = 0; w < kRed; ++w) {
-      const bool in = w < nw;
-      mw[w] = (in && lw[w] > 0.0f) ? mw[w] : -INFINITY;
-      lw[w] = in ? lw[w] : 0.0f;
-      ow[w] = in ? ow[w] : make_float2(0.0f, 0.0f);
-    }
 #pragma unroll
     for (int w = 0; w < kRed; ++w) M = fmaxf(M, mw[w]);
+    const float Mr = M == -INFINITY ? 0.0f : M;          // all empty: every weight is 0
 #pragma unroll
     for (int w = 0; w < kRed; ++w) {
-      const float wt = lw[w] > 0.0f ? exp2f(mw[w] - M) : 0.0f;
-      Lw += wt * lw[w];
-      o0 += wt * ow[w].x;
-      o1 += wt * ow[w].y;
+      const float wt = __builtin_amdgcn_exp2f(mw[w] - Mr);
+      Lw = __builtin_fmaf(wt, lw[w], Lw);
+      o0 = __builtin_fmaf(wt, ow[w].x, o0);
+      o1 = __builtin_fmaf(wt, ow[w].y, o1);
     }
   }
   if (a.n_splits == 1) {
@@ -707,6 +791,12 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
       float* out_row = a.out + (static_cast<int64_t>(b) * a.hq + 4 * h + i) * kHeadDim + d0;
       *reinterpret_cast<float2*>(out_row) = make_float2(o0 * f, o1 * f);
     }
+    if constexpr (TRACE) {
+      ts.ident = hw_identity() | 1u;
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      ts.stored = stamp_now();
+      trace_write(a, ts, wave, tid);
+    }
     return;
   }
   // ---- cross-workgroup merge: the last workgroup of (b, h) to arrive combines the splits ----
@@ -714,6 +804,31 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   // no cache writeback or invalidate is needed (a device-scope fence would write back and
   // invalidate the whole L2 of the die).  Each wavefront waits until its stores have
   // completed before the workgroup barrier; only then does one thread count the arrival.
+  //
+  // Why this is ordered without release/acquire (all accesses involved are relaxed atomics at
+  // agent scope, which the language model alone would not order across locations):
+  //  1. The partial stores are agent-scope atomic stores: on gfx950 a store with sc1 set.  It
+  //     is written through the die's L2 to the device coherence point, and its completion is
+  //     reported only once it is performed there.
+  //  2. s_waitcnt vmcnt(0) waits for every vector memory operation of the wavefront, stores
+  //     included (gfx9-family parts count stores in vmcnt; there is no separate store counter).
+  //     After it, this wavefront's partials are visible to any agent-scope load on any die.
+  //  3. The workgroup barrier (with its workgroup-scope fences, which also stop the compiler
+  //     from moving memory operations across it) puts every wavefront's wait before the
+  //     arrival RMW of thread 0.  The RMW is an agent-scope atomic performed at the coherence
+  //     point, so the arrivals of one (b, h) are totally ordered: the workgroup that reads
+  //     n_splits - 1 arrived after every other workgroup's stores had completed.
+  //  4. The merging workgroup's loads are issued after the barrier that publishes mrg_last, and
+  //     are agent-scope atomic loads (sc1): they are served from the coherence point, not from
+  //     a line its own die's L2 may hold from earlier, so they return the partials.
+  //  5. The counter is reset by the merging workgroup; the next launch reads it after the
+  //     kernel boundary, which orders all of this launch's memory operations before it.
+  // What would break it: plain stores or loads for the partials (they stay in, or are served
+  // from, one die's write-back L2); a part whose store completion does not mean device
+  // visibility, or that counts stores separately from vmcnt; an RMW issued before the barrier
+  // or from a wavefront that has not waited.  The portable form, a release RMW and an acquire
+  // load, costs a write-back and invalidate of the whole L2 per workgroup.
+  if constexpr (TRACE) ts.issue = stamp_now();
   if (owner) {
     const int64_t slot = (unit * a.n_splits + split) * 4 + i;
     store_coherent_f2(a.ws_o + slot * kHeadDim + d0, o0, o1);
@@ -721,19 +836,34 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
+  if constexpr (TRACE) ts.acked = stamp_now();
   if (tid == 0) {
     const unsigned prev =
         __hip_atomic_fetch_add(a.counters + unit * kCounterStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     mrg_last = (prev == static_cast<unsigned>(a.n_splits - 1)) ? 1 : 0;
+    if constexpr (TRACE) ts.counted = stamp_now();
   }
   __syncthreads();
-  if (!mrg_last || !owner) return;
+  if (!mrg_last || !owner) {
+    if constexpr (TRACE) {
+      ts.ident = hw_identity() | (mrg_last ? 1u : 0u);
+      trace_write(a, ts, wave, tid);
+    }
+    return;
+  }
   // groups of 8 splits when that covers them all (16-entry groups would be half padding)
   if (a.n_splits <= 8)
-    merge_splits<8>(a, unit, i, d0, gv);
+    merge_splits<8, TRACE>(a, unit, i, d0, gv, &ts.loaded);
   else
-    merge_splits<16>(a, unit, i, d0, gv);
+    merge_splits<16, TRACE>(a, unit, i, d0, gv, &ts.loaded);
+  if constexpr (TRACE) ts.folded = stamp_now();
   if (tid == 0) __hip_atomic_store(a.counters + unit * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if constexpr (TRACE) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    ts.stored = stamp_now();
+    ts.ident = hw_identity() | 1u;
+    trace_write(a, ts, wave, tid);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -862,7 +992,7 @@ hipError_t scratch_decode_workspace(int32_t B, int32_t Hkv, const DecodePlan& pl
 hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                          int32_t B, int32_t Hq, const int32_t* page_table, int32_t max_pages_per_seq,
                          const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, float* out,
-                         const DecodeWs& ws, const DecodePlan& plan, hipStream_t stream) {
+                         const DecodeWs& ws, const DecodePlan& plan, hipStream_t stream, uint64_t* trace) {
   DecodeArgs a{};
   a.k_new = k_new;
   a.v_new = v_new;
@@ -897,13 +1027,19 @@ hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, const uint16_t*
   a.k_flags = L.k_flags;
   a.sm_scale = sm_scale;
   a.basis = L.k_basis;
+  a.trace = trace;
   const dim3 grid(plan.n_splits, L.num_kv_heads, B);
   const dim3 block(64 * plan.waves);
   const bool bf = L.k_fmt == NVKV_FMT_BF16;
   using Kernel = void (*)(DecodeArgs);
   const bool klt = !bf && (L.k_flags & NVKV_K_KLT);
   Kernel kern;
-  if (klt) {
+  if (trace) {
+    // the measurement instances: NVFP4 keys without the KLT basis
+    if (bf || klt) return hipErrorNotSupported;
+    if (plan.append) kern = plan.pipe2 ? k_decode<false, true, true, false, true> : k_decode<false, false, true, false, true>;
+    else kern = plan.pipe2 ? k_decode<false, true, false, false, true> : k_decode<false, false, false, false, true>;
+  } else if (klt) {
     if (plan.append) kern = plan.pipe2 ? k_decode<false, true, true, true> : k_decode<false, false, true, true>;
     else kern = plan.pipe2 ? k_decode<false, true, false, true> : k_decode<false, false, false, true>;
   } else if (plan.append) {

@@ -61,10 +61,12 @@ hipError_t scratch_decode_workspace(int32_t B, int32_t Hkv, const DecodePlan& pl
                                     DecodeWs* ws);
 
 // k_new / v_new non-null: fused append of the new token of each sequence (plan.append).
+// trace non-null: the measurement instance, which also writes phase stamps (kTraceSlots per
+// workgroup, see nvkv_decode.hip); NVFP4 keys without the KLT basis only.
 hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                          int32_t B, int32_t Hq, const int32_t* page_table, int32_t max_pages_per_seq,
                          const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, float* out,
-                         const DecodeWs& ws, const DecodePlan& plan, hipStream_t stream);
+                         const DecodeWs& ws, const DecodePlan& plan, hipStream_t stream, uint64_t* trace = nullptr);
 
 // Causal attention of the last Tq positions of each sequence over the cache (no workspace).
 hipError_t launch_prefill_attention(const nvkv_layer& L, const uint16_t* q, int32_t B, int32_t Tq, int32_t Hq,

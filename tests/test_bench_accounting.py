@@ -34,3 +34,18 @@ def test_step36_figures():
     assert bench.decode_step_bytes(4, 2304, 8, 32, 1, 36) == 386_500_608
     # bf16 keys: 256 B key rows
     assert bench.decode_bytes(4, 2304, 8, 32, 0) == 4 * 8 * 2304 * (256 + 72) + 98_304
+
+
+def test_measurement_library_exports_and_plan():
+    """The bench's measurement helpers (libnvkv_bench.so: streaming read, phase-stamped decode)
+    load without a GPU, export their three calls, and report the library's own split plan:
+    batch 4 x 2304 over 8 KV heads -> 8 splits of 288 tokens, 9 cache wavefronts + 1 append."""
+    import ctypes
+    lib = bench.bench_lib()
+    for name in ("nvkvb_stream_read", "nvkvb_decode_plan", "nvkvb_decode_trace"):
+        assert hasattr(lib, name)
+    out = (ctypes.c_int32 * 3)()
+    lib.nvkvb_decode_plan(4, 8, 2304, 0, 1, out)
+    assert list(out) == [8, 10, 0]
+    lib.nvkvb_decode_plan(64, 8, 32768, 0, 1, out)
+    assert list(out) == [1, 8, 1]
