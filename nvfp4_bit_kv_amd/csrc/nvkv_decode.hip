@@ -87,7 +87,8 @@ struct DecodeArgs {
 //   3 split partials acknowledged (after the workgroup barrier); 4 arrival counter returned;
 //   5 merging workgroup: splits loaded and folded, output stores issued; 6 output stores
 //   complete; 7 identity: bit 0 = merging workgroup, bits 8..39 = HW_ID, bits 40..47 =
-//   XCC_ID; 8 split partial stores issued; 9 merging workgroup: split partials in registers;
+//   XCC_ID, bits 48..63 = split index; 8 split partial stores issued; 9 merging workgroup:
+//   split partials in registers;
 //   16 + w: wavefront w's first cache data in registers; 32 + w: wavefront w's loop done
 //   (w < 16).  Slots a workgroup never reaches stay 0.
 constexpr int kTraceSlots = 48;
@@ -549,7 +550,22 @@ template <bool KBF16, bool PIPE2, bool APPEND, bool KLT, bool TRACE = false>
 __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   TraceStamps ts;
   if constexpr (TRACE) ts.entry = stamp_now();
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // Workgroups are dealt to the 8 dies (XCDs) round robin by linear id, so the ids are
+  // remapped to give the splits of one (sequence, KV head) consecutive ids within one die's
+  // share: their merge traffic then stays on one die where possible.  A bijection for any
+  // grid; correctness does not depend on where workgroups run.
+  int split, h, b;
+  {
+    const uint32_t n_split = gridDim.x, n_head = gridDim.y;
+    const uint32_t total = n_split * n_head * gridDim.z;
+    const uint32_t L = blockIdx.x + n_split * (blockIdx.y + n_head * blockIdx.z);
+    const uint32_t q8 = total >> 3, r8 = total & 7u, x = L & 7u;
+    const uint32_t G = x * q8 + (x < r8 ? x : r8) + (L >> 3);
+    const uint32_t unit_g = G / n_split;
+    split = static_cast<int>(G - unit_g * n_split);
+    h = static_cast<int>(unit_g % n_head);
+    b = static_cast<int>(unit_g / n_head);
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
@@ -792,7 +808,7 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
       *reinterpret_cast<float2*>(out_row) = make_float2(o0 * f, o1 * f);
     }
     if constexpr (TRACE) {
-      ts.ident = hw_identity() | 1u;
+      ts.ident = hw_identity() | 1u | (static_cast<uint64_t>(split) << 48);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       ts.stored = stamp_now();
       trace_write(a, ts, wave, tid);
@@ -846,7 +862,7 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   __syncthreads();
   if (!mrg_last || !owner) {
     if constexpr (TRACE) {
-      ts.ident = hw_identity() | (mrg_last ? 1u : 0u);
+      ts.ident = hw_identity() | (mrg_last ? 1u : 0u) | (static_cast<uint64_t>(split) << 48);
       trace_write(a, ts, wave, tid);
     }
     return;
@@ -861,7 +877,7 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   if constexpr (TRACE) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     ts.stored = stamp_now();
-    ts.ident = hw_identity() | 1u;
+    ts.ident = hw_identity() | 1u | (static_cast<uint64_t>(split) << 48);
     trace_write(a, ts, wave, tid);
   }
 }
