@@ -70,7 +70,7 @@ def parse():
                     help="decode workloads: also run the phase-stamped instance of the fused decode kernel "
                          "(libnvkv_bench.so) over one step and print its phase timeline")
     ap.add_argument("--trace-dump", default="",
-                    help="with --trace-phases: also save the raw stamps (uint64 [layers][workgroups][40]) to this .npy file")
+                    help="with --trace-phases: also save the raw stamps (uint64 [layers][workgroups][48]) to this .npy file")
     ap.add_argument("--no-stream-reference", action="store_true",
                     help="skip the plain streaming read of the same cache bytes (reference for stream_frac)")
     ap.add_argument("--separate", action="store_true",
