@@ -550,17 +550,17 @@ template <bool KBF16, bool PIPE2, bool APPEND, bool KLT, bool TRACE = false>
 __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   TraceStamps ts;
   if constexpr (TRACE) ts.entry = stamp_now();
-  // Workgroups are dealt to the 8 dies (XCDs) round robin by linear id, so the ids are
-  // remapped to give the splits of one (sequence, KV head) consecutive ids within one die's
-  // share: their merge traffic then stays on one die where possible.  A bijection for any
-  // grid; correctness does not depend on where workgroups run.
+  // Workgroups are dealt to the 8 dies (XCDs) round robin by linear id, so with several
+  // splits the ids are remapped to give the splits of one (sequence, KV head) consecutive ids
+  // within one die's share: their merge traffic then stays on one die where possible.  A
+  // bijection for any grid; correctness does not depend on where workgroups run.
   int split, h, b;
   {
     const uint32_t n_split = gridDim.x, n_head = gridDim.y;
     const uint32_t total = n_split * n_head * gridDim.z;
     const uint32_t L = blockIdx.x + n_split * (blockIdx.y + n_head * blockIdx.z);
     const uint32_t q8 = total >> 3, r8 = total & 7u, x = L & 7u;
-    const uint32_t G = x * q8 + (x < r8 ? x : r8) + (L >> 3);
+    const uint32_t G = n_split > 1 ? x * q8 + (x < r8 ? x : r8) + (L >> 3) : L;
     const uint32_t unit_g = G / n_split;
     split = static_cast<int>(G - unit_g * n_split);
     h = static_cast<int>(unit_g % n_head);
@@ -1051,9 +1051,10 @@ hipError_t launch_decode(const nvkv_layer& L, const uint16_t* q, const uint16_t*
   const bool klt = !bf && (L.k_flags & NVKV_K_KLT);
   Kernel kern;
   if (trace) {
-    // the measurement instances: NVFP4 keys without the KLT basis
-    if (bf || klt) return hipErrorNotSupported;
-    if (plan.append) kern = plan.pipe2 ? k_decode<false, true, true, false, true> : k_decode<false, false, true, false, true>;
+    // the measurement instances: NVFP4 keys; with the KLT basis the fused short-split form only
+    if (bf || (klt && (!plan.append || plan.pipe2))) return hipErrorNotSupported;
+    if (klt) kern = k_decode<false, false, true, true, true>;
+    else if (plan.append) kern = plan.pipe2 ? k_decode<false, true, true, false, true> : k_decode<false, false, true, false, true>;
     else kern = plan.pipe2 ? k_decode<false, true, false, false, true> : k_decode<false, false, false, false, true>;
   } else if (klt) {
     if (plan.append) kern = plan.pipe2 ? k_decode<false, true, true, true> : k_decode<false, false, true, true>;

@@ -313,22 +313,110 @@ __device__ __forceinline__ double mse_code_criterion(const float (&y)[kBlock], c
   return mse_criterion(s, g, p2, m4);
 }
 
+// Integer form of 2P for the one-lane search.  With E = floor(log2 A), every element that
+// can take a nonzero code under a scale u >= A/8 has |y_j| > u/4 >= A/32 >= 2^(E-5), so
+// |y_j| = Y_j 2^(E-28) with an integer Y_j < 2^29 (smaller elements keep code 0 and their
+// truncated Y_j is multiplied by 0).  The codes' twice-magnitudes k_j (0..12) are packed four
+// to a dword in the order of the packed nibble words (dword 0: elements 0, 2, 4, 6; 1: 1, 3,
+// 5, 7; 2: 8, 10, 12, 14; 3: 9, 11, 13, 15), and Y_j is split into bytes regrouped the same
+// way, so 2P = sum over bytes b of 2^(8b) sum_j k_j byte_b(Y_j) comes from 16 four-way byte
+// dot products (each partial sum below 2^16, the total below 2^40: exact in fp64), and 4 M2 =
+// sum k_j^2 from 4 more.  The result equals mse_partials' exactly.
+struct MseAligned {
+  uint32_t yb[4][4];    // [dword d][byte b]: byte b of Y_j for the four elements of dword d
+  int shift;            // E - 28
+};
+
+__device__ __forceinline__ void mse_align(const float (&y)[kBlock], float A, MseAligned& m) {
+  const int E = __builtin_amdgcn_frexp_expf(A) - 1;          // A in [2^E, 2^(E+1))
+  uint32_t Y[kBlock];
+#pragma unroll
+  for (int i = 0; i < kBlock; ++i) Y[i] = static_cast<uint32_t>(__builtin_ldexpf(fabsf(y[i]), 28 - E));
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int e0 = 8 * (d >> 1) + (d & 1);                  // elements e0, e0 + 2, e0 + 4, e0 + 6
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      // bytes b of two elements side by side, then the two pairs side by side
+      const uint32_t sel = static_cast<uint32_t>(b) | (static_cast<uint32_t>(b + 4) << 8);
+      const uint32_t lo = __builtin_amdgcn_perm(Y[e0 + 2], Y[e0], sel);
+      const uint32_t hi = __builtin_amdgcn_perm(Y[e0 + 6], Y[e0 + 4], sel);
+      m.yb[d][b] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    }
+  }
+  m.shift = E - 28;
+}
+
+// 2P and 4 M2 of one candidate from its packed codes (nibble i = element i, words w0, w1).
+__device__ __forceinline__ void mse_partials_aligned(uint32_t w0, uint32_t w1, const MseAligned& m, double& p2,
+                                                     uint32_t& m4) {
+  // twice-magnitude of each 3-bit magnitude code by a byte table lookup: 0 1 2 3 4 6 8 12
+  const uint32_t kd[4] = {__builtin_amdgcn_perm(0x0C080604u, 0x03020100u, w0 & 0x07070707u),
+                          __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, (w0 >> 4) & 0x07070707u),
+                          __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, w1 & 0x07070707u),
+                          __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, (w1 >> 4) & 0x07070707u)};
+  uint32_t q = 0u;
+  uint32_t pb[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    q = __builtin_amdgcn_udot4(kd[d], kd[d], q, false);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) pb[b] = __builtin_amdgcn_udot4(kd[d], m.yb[d][b], pb[b], false);
+  }
+  m4 = q;
+  const uint32_t lo = pb[0] + (pb[1] << 8), hi = pb[2] + (pb[3] << 8);     // each below 2^25
+  p2 = __builtin_ldexp(__builtin_fma(static_cast<double>(hi), 65536.0, static_cast<double>(lo)), m.shift);
+}
+
+// Criterion J of code c (c >= 1, u = g sigma_c >= A/8) from the aligned block.
+__device__ __forceinline__ double mse_code_criterion_aligned(const float (&y)[kBlock], const MseAligned& m, uint32_t c,
+                                                             float g) {
+#pragma clang fp contract(off)
+  const float s = e4m3_value(c);
+  const float u = s * g;
+  const float R = __builtin_amdgcn_rcpf(u);
+  const float r1 = R * kBracketDown, r2 = R * kBracketUp;
+  uint32_t w0 = cvt_pack8(&y[0], r1), w1 = cvt_pack8(&y[8], r1);
+  const bool same = u >= 0x1p-125f && w0 == cvt_pack8(&y[0], r2) && w1 == cvt_pack8(&y[8], r2);
+  if (__builtin_expect(!same, 0)) {
+    const E2m1Thresholds t(s, g);
+    w0 = e2m1_pack8(&y[0], t);
+    w1 = e2m1_pack8(&y[8], t);
+  }
+  double p2;
+  uint32_t m4;
+  mse_partials_aligned(w0, w1, m, p2, m4);
+  return mse_criterion(s, g, p2, m4);
+}
+
 // Search for a block held by one lane: S0 first, then the run in increasing code order, a
-// candidate replacing the best only when strictly better.
+// candidate replacing the best only when strictly better.  The run's codes all have
+// g sigma >= A/7, so they take the integer form; S0 does too unless its scale is below A/8
+// (a saturated block), where it takes the fp64 form.
 __device__ __forceinline__ uint32_t mse_scale_code(const float (&y)[kBlock], float A, float g, uint32_t S0) {
 #pragma clang fp contract(off)
-  double ay[kBlock];
-#pragma unroll
-  for (int i = 0; i < kBlock; ++i) ay[i] = static_cast<double>(fabsf(y[i]));
+  MseAligned m;
+  mse_align(y, A, m);
   uint32_t best = S0;
-  double best_j = S0 ? mse_code_criterion(y, ay, S0, g) : 0.0;
+  double best_j = 0.0;
+  if (S0) {
+    const float s0 = e4m3_value(S0);
+    if (__builtin_fmaf(-8.0f * s0, g, A) <= 0.0f) {      // A <= 8 g sigma_0, exactly
+      best_j = mse_code_criterion_aligned(y, m, S0, g);
+    } else {
+      double ay[kBlock];
+#pragma unroll
+      for (int i = 0; i < kBlock; ++i) ay[i] = static_cast<double>(fabsf(y[i]));
+      best_j = mse_code_criterion(y, ay, S0, g);
+    }
+  }
   uint32_t c = mse_first_code(S0, A, g);
   for (int k = 0; k < kMseMaxCand; ++k, ++c) {
     if (c > 126u) break;
     const float s = e4m3_value(c);
     if (mse_above(s, A, g)) break;                 // this code and every larger one
     if (mse_below(s, A, g) || c == S0) continue;
-    const double j = mse_code_criterion(y, ay, c, g);
+    const double j = mse_code_criterion_aligned(y, m, c, g);
     if (j < best_j) {
       best_j = j;
       best = c;
@@ -406,19 +494,23 @@ __device__ __forceinline__ uint32_t encode_block_mse(const float (&y)[kBlock], f
   return S;
 }
 
-// Load this lane's 16 bf16 elements as fp32.
-__device__ __forceinline__ void load_block_bf16(const uint16_t* __restrict__ src, float (&y)[kBlock],
-                                                uint4& raw0, uint4& raw1) {
-#pragma clang fp contract(off)
-  const uint4* p = reinterpret_cast<const uint4*>(src);
-  raw0 = p[0];
-  raw1 = p[1];
+// The 16 bf16 elements of a block, held as two 16-byte words, as fp32 (exact).
+__device__ __forceinline__ void unpack_bf16_block(const uint4& raw0, const uint4& raw1, float (&y)[kBlock]) {
   const uint32_t w[8] = {raw0.x, raw0.y, raw0.z, raw0.w, raw1.x, raw1.y, raw1.z, raw1.w};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     y[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
     y[2 * i + 1] = bf16_to_f32(w[i] >> 16);
   }
+}
+
+// Load this lane's 16 bf16 elements as fp32.
+__device__ __forceinline__ void load_block_bf16(const uint16_t* __restrict__ src, float (&y)[kBlock],
+                                                uint4& raw0, uint4& raw1) {
+  const uint4* p = reinterpret_cast<const uint4*>(src);
+  raw0 = p[0];
+  raw1 = p[1];
+  unpack_bf16_block(raw0, raw1, y);
 }
 
 }  // namespace nvkv

@@ -11,21 +11,26 @@
 // 8 blocks of a row 8 lanes apart (lane = 8 * block + token); the calibration kernels put
 // them in 8 consecutive lanes (8 rows per wavefront, 32 per workgroup).  The only cross-lane
 // traffic is the Hadamard butterfly's three block-pair stages.
+#include <algorithm>
+
 #include "nvkv_encode.hpp"
 #include "nvkv_internal.hpp"
 #include "nvkv_klt.hpp"
 
 namespace nvkv {
 
-// Append layout: a wavefront takes 8 consecutive new tokens of one KV head per pass, lane
-// = 8 * block + token, and makes kPasses passes; a workgroup is 4 wavefronts.  The
-// smoothing factors of a lane's block are loaded once and serve every pass.  Adjacent lanes
-// hold adjacent tokens, so the scale bytes and value words of a token quad are written by
-// adjacent lanes to adjacent bytes.
-constexpr int kTokPerPass = 8;
-constexpr int kPasses = 4;
+// Append layout: a wavefront takes 32 consecutive new tokens of one KV head; lane = 8 * block
+// + quad, and the lane encodes its block of tokens 4 * quad + t, t = 0..3 (one token quad),
+// in four passes.  All eight row loads of a lane are issued before the first encode.  When a
+// quad's four slots are consecutive and quad-aligned (pages filled in order, as in a
+// prefill), the lane writes the quad's four scale bytes as one word and, for the
+// quad-interleaved value codes, its two 16-byte code runs; otherwise each token is stored on
+// its own.  The smoothing factors of a lane's block are loaded once.  A workgroup is 4
+// wavefronts.
+constexpr int kQuad = 4;
 constexpr int kAppendWaves = 4;
-constexpr int kTokPerWg = kTokPerPass * kPasses * kAppendWaves;
+constexpr int kTokPerWave = 8 * kQuad;
+constexpr int kTokPerWg = kTokPerWave * kAppendWaves;
 
 struct AppendArgs {
   const uint16_t* src;        // bf16 [N][Hkv][128]
@@ -36,6 +41,7 @@ struct AppendArgs {
   uint32_t flags;             // key transform flags (0 for V)
   int32_t fmt;                // NVKV_FMT_*
   int32_t quad_words;         // 1: codes in the quad-interleaved word layout (NVFP4 values)
+  int32_t wide_stores;        // 1: scales 4-byte and codes 16-byte aligned (quad stores allowed)
   const float* basis;         // KLT basis [Hkv][128][128] (keys with NVKV_K_KLT), else unused
 };
 
@@ -65,26 +71,54 @@ __device__ __forceinline__ int32_t append_slot(const AppendPair& p, int n) {
   return (pg < 0 || s64 >= p.max_slot) ? -1 : static_cast<int32_t>(s64);
 }
 
-// grid: x = token chunks of kTokPerWg, y = KV head (y < Hkv: keys, else values).  MSE:
-// compiled with the key block-scale search (which needs more registers than the plain
-// encoder, so the plain launch does not carry it).  KLT: compiled with the key basis
-// rotation (the head's basis in LDS, each wavefront's 8 rows staged in LDS).
-template <bool MSE, bool KLT>
-__global__ void __launch_bounds__(256) k_quantize_append(AppendPair p) {
-  const int which = static_cast<int>(blockIdx.y) >= p.hkv ? 1 : 0;
-  const AppendArgs a = which ? p.a[1] : p.a[0];   // uniform select, no dynamic indexing
-  const int h = static_cast<int>(blockIdx.y) - (which ? p.hkv : 0);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int blk = lane >> 3, tok = lane & 7;
-  __shared__ __attribute__((aligned(16))) float basis_lds[KLT ? kBasisFloats : 4];
-  __shared__ __attribute__((aligned(16))) float row_lds[KLT ? kAppendWaves : 1][KLT ? kTokPerPass : 1][kHeadDim];
-  const bool klt = KLT && a.fmt != NVKV_FMT_BF16 && (a.flags & NVKV_K_KLT);   // uniform per workgroup
-  if constexpr (KLT) {
-    if (klt) load_basis_lds(a.basis + static_cast<int64_t>(h) * kBasisFloats, basis_lds, threadIdx.x, 256);
-    __syncthreads();
+// One wavefront's share of a (K or V, head) pair of rows in the plain layout: tokens
+// n_first .. n_first + 31, lane = 8 * block + quad.  Tokens past the end compute on a clamped
+// copy (every lane takes part in the cross-lane steps) and store nothing.
+struct QuadLoads {
+  uint4 raw[kQuad][2];        // the lane's block of the quad's four rows (bf16)
+  int32_t slot[kQuad];        // their cache slots (-1: past the end)
+};
+
+// The independent loads of append_quads: the quad's rows and slots.
+__device__ __forceinline__ void quads_load(const AppendPair& p, const AppendArgs& a, int h, int n_first, int lane,
+                                           QuadLoads& L) {
+  const int blk = lane >> 3, qd = lane & 7;
+  const int nq = n_first + kQuad * qd;                  // this lane's token quad
+#pragma unroll
+  for (int t = 0; t < kQuad; ++t) {
+    const int n = nq + t < p.n_tokens ? nq + t : p.n_tokens - 1;
+    const uint4* src = reinterpret_cast<const uint4*>(a.src + (static_cast<int64_t>(n) * p.hkv + h) * kHeadDim +
+                                                      blk * kBlock);
+    L.raw[t][0] = src[0];
+    L.raw[t][1] = src[1];
+    L.slot[t] = nq + t < p.n_tokens ? append_slot(p, n) : -1;
   }
-  const bool smooth = a.fmt != NVKV_FMT_BF16 && (a.flags & 1u);
+}
+
+// The encode and stores of append_quads, from its loads.
+template <bool MSE>
+__device__ __forceinline__ void quads_finish(const AppendPair& p, const AppendArgs& a, int h, int lane,
+                                             const QuadLoads& L) {
+  const int blk = lane >> 3;
+  const auto& raw = L.raw;
+  const auto& slot = L.slot;
+  bool ok[kQuad];
+#pragma unroll
+  for (int t = 0; t < kQuad; ++t) ok[t] = slot[t] >= 0 && static_cast<int64_t>(slot[t]) < p.max_slot;
+  if (a.fmt == NVKV_FMT_BF16) {  // BF16 keys: plain copy of the rows
+#pragma unroll
+    for (int t = 0; t < kQuad; ++t) {
+      if (!ok[t]) continue;
+      const int32_t page = slot[t] / p.page_size, off = slot[t] - page * p.page_size;
+      const int64_t ri = (static_cast<int64_t>(page) * p.hkv + h) * p.page_size + off;
+      uint4* dst = reinterpret_cast<uint4*>(a.codes + ri * (kHeadDim * 2) + blk * 32);
+      dst[0] = raw[t][0];
+      dst[1] = raw[t][1];
+    }
+    return;
+  }
   float r[kBlock];
+  const bool smooth = (a.flags & 1u) != 0;
   if (smooth) {
     const float4* rp = reinterpret_cast<const float4*>(a.inv_smooth + h * kHeadDim + blk * kBlock);
 #pragma unroll
@@ -96,61 +130,194 @@ __global__ void __launch_bounds__(256) k_quantize_append(AppendPair p) {
       r[4 * q + 3] = v.w;
     }
   }
-  const float gsc = a.fmt == NVKV_FMT_BF16 ? 1.0f : *a.gscale;
-  const int n_wave = static_cast<int>(blockIdx.x) * kTokPerWg + wave * (kTokPerPass * kPasses);
+  const float gsc = *a.gscale;
+  uint32_t lo[kQuad], hi[kQuad], S[kQuad];
 #pragma unroll
-  for (int pass = 0; pass < kPasses; ++pass) {   // unrolled: a pass's loads overlap the previous encode
-    const int n0 = n_wave + pass * kTokPerPass;
-    if (n0 >= p.n_tokens) break;                        // uniform
-    // tokens past the end compute on a clamped copy (every lane takes part in the
-    // cross-lane steps) and store nothing
-    const int n = n0 + tok < p.n_tokens ? n0 + tok : p.n_tokens - 1;
-    const bool live = n0 + tok < p.n_tokens;
-    // independent loads first (row block, slot); the slot check comes after
+  for (int t = 0; t < kQuad; ++t) {
     float y[kBlock];
-    uint4 raw0, raw1;
-    load_block_bf16(a.src + (static_cast<int64_t>(n) * p.hkv + h) * kHeadDim + blk * kBlock, y, raw0, raw1);
-    const int32_t slot = append_slot(p, n);
-    const bool ok = live && slot >= 0 && static_cast<int64_t>(slot) < p.max_slot;
-    const int32_t page = ok ? slot / p.page_size : 0;
-    const int32_t off = ok ? slot - page * p.page_size : 0;
-    const int64_t row_index = (static_cast<int64_t>(page) * p.hkv + h) * p.page_size + off;
-    if (a.fmt == NVKV_FMT_BF16) {  // BF16 keys: plain copy of the row
-      if (ok) {
-        uint4* dst = reinterpret_cast<uint4*>(a.codes + row_index * (kHeadDim * 2) + blk * 32);
-        dst[0] = raw0;
-        dst[1] = raw1;
-      }
-      continue;
-    }
+    unpack_bf16_block(raw[t][0], raw[t][1], y);
     if (smooth) {
 #pragma unroll
       for (int i = 0; i < kBlock; ++i) y[i] = y[i] * r[i];
     }
     if (a.flags & 2u) hadamard_row<8>(y, blk);
-    if constexpr (KLT) {
-      if (klt) {   // z = B^T y: the row through LDS, this lane's 16 outputs in the fixed order
-        float4* dst = reinterpret_cast<float4*>(&row_lds[wave][tok][blk * kBlock]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dst[q] = make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
-        rotate_cols<kBlock>(basis_lds, row_lds[wave][tok], blk * kBlock, y);
-      }
-    }
-    uint32_t lo, hi;
-    const uint32_t S = (MSE && (a.flags & NVKV_K_MSE_SCALE)) ? encode_block_mse(y, gsc, lo, hi)
-                                                             : encode_block(y, gsc, lo, hi);
-    if (!ok) continue;
+    S[t] = (MSE && (a.flags & NVKV_K_MSE_SCALE)) ? encode_block_mse(y, gsc, lo[t], hi[t])
+                                                 : encode_block(y, gsc, lo[t], hi[t]);
+  }
+  const bool quad = a.wide_stores && ok[0] && ok[1] && ok[2] && ok[3] && (slot[0] & 3) == 0 &&
+                    slot[1] == slot[0] + 1 && slot[2] == slot[0] + 2 && slot[3] == slot[0] + 3;
+  if (quad) {   // page_size is a multiple of 16, so an aligned quad lies in one page
+    const int32_t page = slot[0] / p.page_size, off = slot[0] - page * p.page_size;
+    const int64_t ri = (static_cast<int64_t>(page) * p.hkv + h) * p.page_size + off;
     if (!a.quad_words) {
-      *reinterpret_cast<uint2*>(a.codes + row_index * 64 + blk * 8) = make_uint2(lo, hi);
+#pragma unroll
+      for (int t = 0; t < kQuad; ++t)
+        *reinterpret_cast<uint2*>(a.codes + (ri + t) * 64 + blk * 8) = make_uint2(lo[t], hi[t]);
+    } else {
+      // word 2blk of the quad's tokens: 16 bytes at 32 blk of the quad's 256-byte group,
+      // word 2blk+1 the next 16
+      uint4* wq = reinterpret_cast<uint4*>(a.codes + ri * 64 + 32 * blk);
+      wq[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      wq[1] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    }
+    const int64_t sbase = (static_cast<int64_t>(page) * p.hkv + h) * p.page_size * 8;
+    *reinterpret_cast<uint32_t*>(a.scales + sbase + ((off >> 2) * 8 + blk) * 4) =
+        S[0] | (S[1] << 8) | (S[2] << 16) | (S[3] << 24);
+    return;
+  }
+#pragma unroll
+  for (int t = 0; t < kQuad; ++t) {
+    if (!ok[t]) continue;
+    const int32_t page = slot[t] / p.page_size, off = slot[t] - page * p.page_size;
+    const int64_t ri = (static_cast<int64_t>(page) * p.hkv + h) * p.page_size + off;
+    if (!a.quad_words) {
+      *reinterpret_cast<uint2*>(a.codes + ri * 64 + blk * 8) = make_uint2(lo[t], hi[t]);
     } else {
       // words 2blk, 2blk+1 of token `off`: byte ((off/4)*16 + w)*16 + (off%4)*4 of the
       // (page, head) block, which starts at the same place as in the row-major layout
-      uint8_t* wq = a.codes + (row_index - (off & 3)) * 64 + 32 * blk + 4 * (off & 3);
-      *reinterpret_cast<uint32_t*>(wq) = lo;
-      *reinterpret_cast<uint32_t*>(wq + 16) = hi;
+      uint8_t* wq = a.codes + (ri - (off & 3)) * 64 + 32 * blk + 4 * (off & 3);
+      *reinterpret_cast<uint32_t*>(wq) = lo[t];
+      *reinterpret_cast<uint32_t*>(wq + 16) = hi[t];
     }
     const int64_t sbase = (static_cast<int64_t>(page) * p.hkv + h) * p.page_size * 8;
-    a.scales[sbase + ((off >> 2) * 8 + blk) * 4 + (off & 3)] = static_cast<uint8_t>(S);
+    a.scales[sbase + ((off >> 2) * 8 + blk) * 4 + (off & 3)] = static_cast<uint8_t>(S[t]);
+  }
+}
+
+template <bool MSE>
+__device__ __forceinline__ void append_quads(const AppendPair& p, const AppendArgs& a, int h, int n_first,
+                                             int lane) {
+  QuadLoads L;
+  quads_load(p, a, h, n_first, lane, L);
+  quads_finish<MSE>(p, a, h, lane, L);
+}
+
+// grid: x = token chunks of kTokPerWg, y = KV head row (< Hkv: keys, else values).  MSE:
+// compiled with the key block-scale search (which needs more registers than the plain
+// encoder, so the plain launch does not carry it).
+template <bool MSE>
+__global__ void __launch_bounds__(256) k_quantize_append(AppendPair p) {
+  const int row = static_cast<int>(blockIdx.y);
+  const int which = row >= p.hkv ? 1 : 0;
+  const AppendArgs a = which ? p.a[1] : p.a[0];   // uniform select, no dynamic indexing
+  const int h = row - (which ? p.hkv : 0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n_first = static_cast<int>(blockIdx.x) * kTokPerWg + wave * kTokPerWave;
+  if (n_first >= p.n_tokens) return;                   // uniform per wavefront
+  append_quads<MSE>(p, a, h, n_first, lane);
+}
+
+// KLT keys ([cache post] cache-config table, KLT rows).  A workgroup of 8 wavefronts owns
+// one head and walks its 128-token chunks with the head's basis resident in LDS (64 KB), so
+// the basis is read from memory once per workgroup.  Per chunk:
+//   staging: wavefront w converts tokens 64 (w & 1) .. + 63, dims 32 (w >> 1) .. + 31 to
+//     y = fl32(x r) and writes them element-major, ybuf[j][token] (64 KB);
+//   rotation: lane (column group cb, token quad tq) forms z for 8 columns 8 cb .. 8 cb + 7 and
+//     the quad's 4 tokens as rotate_cols does, z <- fl32(B[j][col] y_j + z) over j = 0..127,
+//     from one 16-byte read of y and two of B per j: 32 multiply-adds per 48 bytes read;
+//   encode: the two lanes of a block (cb = 2b, 2b + 1, adjacent lanes) swap halves so that
+//     each holds the block's 16 columns for two of the quad's tokens, then encode and store.
+// The next chunk's key rows are loaded during the rotation, and wavefronts 0..3 load the
+// chunk's value rows before it and encode them after it (the plain quad path), so the
+// memory traffic overlaps the multiply-adds.
+constexpr int kKltWaves = 8;
+constexpr int kKltTok = 128;
+constexpr int kKltResidentWgs = 256;      // one per CU
+
+__device__ __forceinline__ float swap_adjacent_lanes(float v) {   // lane l <-> lane l ^ 1
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+template <bool MSE>
+__global__ void __launch_bounds__(64 * kKltWaves) k_quantize_append_klt(AppendPair p) {
+  const int h = static_cast<int>(blockIdx.y);
+  const AppendArgs& ka = p.a[0];
+  const AppendArgs& va = p.a[1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __shared__ __attribute__((aligned(16))) float basis_lds[kBasisFloats];
+  __shared__ __attribute__((aligned(16))) float ybuf[kHeadDim][kKltTok];
+  load_basis_lds(ka.basis + static_cast<int64_t>(h) * kBasisFloats, basis_lds, tid, 64 * kKltWaves);
+  const int st_tok = 64 * (wave & 1) + lane, st_d0 = 32 * (wave >> 1);     // staging role
+  const int cb = 8 * (wave & 1) + (lane & 7), tq = 8 * (wave >> 1) + (lane >> 3);   // rotation role
+  const bool odd = (cb & 1) != 0;
+  const bool smooth = (ka.flags & 1u) != 0;
+  const float gk = *ka.gscale;
+  const int n_chunks = (p.n_tokens + kKltTok - 1) / kKltTok;
+  uint4 kraw[4];
+  auto load_keys = [&](int chunk) {
+    const int n0 = chunk * kKltTok + st_tok;
+    const int n = n0 < p.n_tokens ? n0 : p.n_tokens - 1;
+    const uint4* src = reinterpret_cast<const uint4*>(ka.src + (static_cast<int64_t>(n) * p.hkv + h) * kHeadDim + st_d0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kraw[i] = src[i];
+  };
+  int chunk = static_cast<int>(blockIdx.x);
+  if (chunk < n_chunks) load_keys(chunk);
+  for (; chunk < n_chunks; chunk += static_cast<int>(gridDim.x)) {
+    const int base = chunk * kKltTok;
+    QuadLoads vl;
+    if (wave < 4) quads_load(p, va, h, base + kTokPerWave * wave, lane, vl);
+    // staging (the first chunk's barrier also publishes the basis)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w[4] = {kraw[i].x, kraw[i].y, kraw[i].z, kraw[i].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = st_d0 + 8 * i + e;
+        float y = bf16_to_f32(e & 1 ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu));
+        if (smooth) y = y * ka.inv_smooth[h * kHeadDim + d];
+        ybuf[d][st_tok] = y;
+      }
+    }
+    __syncthreads();
+    if (chunk + static_cast<int>(gridDim.x) < n_chunks) load_keys(chunk + static_cast<int>(gridDim.x));
+    float z[kQuad][8];
+#pragma unroll
+    for (int t = 0; t < kQuad; ++t)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) z[t][k] = 0.0f;
+#pragma unroll 4
+    for (int j = 0; j < kHeadDim; ++j) {
+      const float4 yq = *reinterpret_cast<const float4*>(&ybuf[j][kQuad * tq]);
+      const float4 b0 = *reinterpret_cast<const float4*>(&basis_lds[j * kHeadDim + 8 * cb]);
+      const float4 b1 = *reinterpret_cast<const float4*>(&basis_lds[j * kHeadDim + 8 * cb + 4]);
+      const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      const float yv[4] = {yq.x, yq.y, yq.z, yq.w};
+#pragma unroll
+      for (int t = 0; t < kQuad; ++t)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) z[t][k] = __builtin_fmaf(bv[k], yv[t], z[t][k]);
+    }
+    __syncthreads();                      // ybuf is free for the next chunk
+    // halves: the even lane keeps tokens 0, 1 of the quad, the odd lane tokens 2, 3
+    float blkz[2][kBlock];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float keep = odd ? z[2 + u][k] : z[u][k];
+        const float recv = swap_adjacent_lanes(odd ? z[u][k] : z[2 + u][k]);
+        blkz[u][k] = odd ? recv : keep;           // columns 16b .. 16b + 7
+        blkz[u][k + 8] = odd ? keep : recv;       // columns 16b + 8 .. 16b + 15
+      }
+    const int b = cb >> 1;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int n = base + kQuad * tq + (odd ? 2 : 0) + u;
+      uint32_t lo, hi;
+      const uint32_t S = (MSE && (ka.flags & NVKV_K_MSE_SCALE)) ? encode_block_mse(blkz[u], gk, lo, hi)
+                                                                : encode_block(blkz[u], gk, lo, hi);
+      const int32_t slot = n < p.n_tokens ? append_slot(p, n) : -1;
+      if (slot >= 0 && static_cast<int64_t>(slot) < p.max_slot) {
+        const int32_t page = slot / p.page_size, off = slot - page * p.page_size;
+        const int64_t ri = (static_cast<int64_t>(page) * p.hkv + h) * p.page_size + off;
+        *reinterpret_cast<uint2*>(ka.codes + ri * 64 + b * 8) = make_uint2(lo, hi);
+        const int64_t sbase = (static_cast<int64_t>(page) * p.hkv + h) * p.page_size * 8;
+        ka.scales[sbase + ((off >> 2) * 8 + b) * 4 + (off & 3)] = static_cast<uint8_t>(S);
+      }
+    }
+    if (wave < 4 && base + kTokPerWave * wave < p.n_tokens) quads_finish<false>(p, va, h, lane, vl);
   }
 }
 
@@ -248,11 +415,15 @@ hipError_t launch_quantize_append_rows(const nvkv_layer& L, const uint16_t* k_ne
                                        const int32_t* slots, int32_t N, const int32_t* page_table,
                                        const int32_t* seq_lens, int32_t max_pages_per_seq, int32_t seq_cap,
                                        hipStream_t stream) {
+  auto wide = [](const void* codes, const void* scales) {
+    return static_cast<int32_t>((reinterpret_cast<uintptr_t>(codes) & 15u) == 0 &&
+                                (reinterpret_cast<uintptr_t>(scales) & 3u) == 0);
+  };
   AppendPair p{};
   p.a[0] = AppendArgs{k_new, static_cast<uint8_t*>(L.k_data), L.k_scales, L.k_inv_smooth, L.global_scale + 0,
-                      L.k_fmt == NVKV_FMT_NVFP4 ? L.k_flags : 0u, L.k_fmt, 0, L.k_basis};
+                      L.k_fmt == NVKV_FMT_NVFP4 ? L.k_flags : 0u, L.k_fmt, 0, wide(L.k_data, L.k_scales), L.k_basis};
   p.a[1] = AppendArgs{v_new, static_cast<uint8_t*>(L.v_data), L.v_scales, nullptr, L.global_scale + 1, 0u,
-                      L.v_fmt, 1, nullptr};
+                      L.v_fmt, 1, wide(L.v_data, L.v_scales), nullptr};
   p.slots = slots;
   p.page_table = page_table;
   p.seq_lens = seq_lens;
@@ -262,12 +433,20 @@ hipError_t launch_quantize_append_rows(const nvkv_layer& L, const uint16_t* k_ne
   p.hkv = L.num_kv_heads;
   p.page_size = L.page_size;
   p.max_slot = static_cast<int64_t>(L.num_pages) * L.page_size;
-  const dim3 grid((N + kTokPerWg - 1) / kTokPerWg, 2 * L.num_kv_heads);
+  const unsigned chunks = static_cast<unsigned>((N + kTokPerWg - 1) / kTokPerWg);
   const bool mse = p.a[0].flags & NVKV_K_MSE_SCALE, klt = p.a[0].flags & NVKV_K_KLT;
   using Kernel = void (*)(AppendPair);
-  const Kernel kern = klt ? (mse ? k_quantize_append<true, true> : k_quantize_append<false, true>)
-                          : (mse ? k_quantize_append<true, false> : k_quantize_append<false, false>);
-  hipLaunchKernelGGL(kern, grid, dim3(64 * kAppendWaves), 0, stream, p);
+  if (klt) {
+    // one resident workgroup per CU (the basis and the staged rows fill its LDS), each
+    // walking the chunks of one head
+    const int kchunks = (N + kKltTok - 1) / kKltTok;
+    const int per_head = std::max(1, std::min(kchunks, kKltResidentWgs / L.num_kv_heads));
+    const Kernel kk = mse ? k_quantize_append_klt<true> : k_quantize_append_klt<false>;
+    hipLaunchKernelGGL(kk, dim3(per_head, L.num_kv_heads), dim3(64 * kKltWaves), 0, stream, p);
+  } else {
+    const Kernel kk = mse ? k_quantize_append<true> : k_quantize_append<false>;
+    hipLaunchKernelGGL(kk, dim3(chunks, 2 * L.num_kv_heads), dim3(64 * kAppendWaves), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

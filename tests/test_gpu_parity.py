@@ -398,6 +398,52 @@ def test_append_canaries_and_skipped_slots(lib):
                         assert same
 
 
+def test_append_unaligned_arrays(lib):
+    """Scale arrays at odd byte addresses and code arrays off 16-byte alignment (allowed by
+    the layout) take the per-token stores: bytes identical to the oracle's, with page-ordered
+    slots that would otherwise use the word-wide quad stores, and a ragged token count."""
+    rng = np.random.default_rng(41)
+    hkv, N = 2, 77
+    pages = P.Pages(2, 48, True, spare=1)
+    flags = 1
+    cache = lib.CacheLayer(pages.num_pages, pages.page_size, hkv, k_flags=flags, fill=0)
+    sm = (1.0 + rng.random((hkv, 128))).astype(np.float32)
+    cache.smooth.copy_(torch.from_numpy(sm))
+    r = (np.float32(1.0) / sm).astype(np.float32)
+    cache.inv_smooth.copy_(torch.from_numpy(r))
+    cache.gscale.copy_(torch.tensor([0.004, 0.003], dtype=torch.float32))
+    L = cache.struct()
+    nbytes = {name: getattr(cache, name).numel() for name in ("k_data", "k_scales", "v_data", "v_scales")}
+    offs = {"k_data": 8, "k_scales": 1, "v_data": 4, "v_scales": 3}
+    bufs = {name: torch.zeros(nbytes[name] + 64, dtype=torch.uint8, device="cuda") for name in offs}
+    for name, off in offs.items():
+        setattr(L, name, bufs[name].data_ptr() + off)
+    k = S.bf16_round(rng.standard_normal((N, hkv, 128)).astype(np.float32))
+    v = S.bf16_round(rng.standard_normal((N, hkv, 128)).astype(np.float32))
+    slots = np.concatenate([pages.slots(0, 0, 40), pages.slots(1, 0, N - 40)])
+    lib.quantize_append_kv(L, P.to_dev_u16(k), P.to_dev_u16(v), P.to_dev_i32(slots), N)
+    torch.cuda.synchronize()
+    got = {name: bufs[name].cpu().numpy()[off:off + nbytes[name]] for name, off in offs.items()}
+    for name, off in offs.items():      # nothing outside the arrays
+        full = bufs[name].cpu().numpy()
+        assert not full[:off].any() and not full[off + nbytes[name]:].any(), name
+    y = O.key_transform(S.bf16_to_f32(k)[None], r[None, None], flags)[0]
+    kc, ks = O.quantize_rows(y, np.float32(0.004))
+    vc, vs = O.quantize_rows(S.bf16_to_f32(v), np.float32(0.003))
+    ps = pages.page_size
+    for n, slot in enumerate(slots):
+        pg, t = int(slot) // ps, int(slot) % ps
+        for h in range(hkv):
+            blk = (pg * hkv + h) * ps
+            for w in range(16):
+                for by in range(4):
+                    assert got["k_data"][blk * 64 + 64 * t + 4 * w + by] == kc[n, h, 4 * w + by]
+                    assert got["v_data"][blk * 64 + ((t // 4) * 16 + w) * 16 + (t % 4) * 4 + by] == vc[n, h, 4 * w + by]
+            for b8 in range(8):
+                assert got["k_scales"][blk * 8 + ((t // 4) * 8 + b8) * 4 + t % 4] == ks[n, h, b8]
+                assert got["v_scales"][blk * 8 + ((t // 4) * 8 + b8) * 4 + t % 4] == vs[n, h, b8]
+
+
 def test_cache_byte_positions(lib):
     """Codes and scales sit where the header's layout formulas put them, checked byte by byte
     with the formulas written out (keys row-major, values quad-interleaved, scales
