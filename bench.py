@@ -951,6 +951,9 @@ def trace_phases(torch, wl, dump=""):
             d_arrival=med(r[:, 4] - r[:, 3]), d_merger_load=med(r[merger, 9] - r[merger, 4]),
             d_merger_fold_store=med(r[merger, 6] - r[merger, 9]),
         ))
+        if np.isfinite(r[:, 10]).any():     # the KLT basis stamps of wavefront 0
+            rows[-1].update(basis_quarter_staged=med(r[:, 10]), basis_barrier=med(r[:, 11]),
+                            query_transformed=med(r[:, 12]))
     out = {"launches": wl.L, "workgroups": n_wg, "waves_per_workgroup": waves, "n_splits": n_splits,
            "unit": "us; times after the first workgroup of the launch started, d_* are per-workgroup phase "
                    "durations (s_memrealtime, 100 MHz); medians over a launch's workgroups, then median and "

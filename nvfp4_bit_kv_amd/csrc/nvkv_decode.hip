@@ -88,13 +88,15 @@ struct DecodeArgs {
 //   5 merging workgroup: splits loaded and folded, output stores issued; 6 output stores
 //   complete; 7 identity: bit 0 = merging workgroup, bits 8..39 = HW_ID, bits 40..47 =
 //   XCC_ID, bits 48..63 = split index; 8 split partial stores issued; 9 merging workgroup:
-//   split partials in registers;
+//   split partials in registers; with the KLT basis (wavefront 0): 10 its quarter of the
+//   basis staged, 11 the basis barrier passed, 12 its query head transformed;
 //   16 + w: wavefront w's first cache data in registers; 32 + w: wavefront w's loop done
 //   (w < 16).  Slots a workgroup never reaches stay 0.
 constexpr int kTraceSlots = 48;
 struct TraceStamps {
   uint64_t entry = 0, prologue = 0, lds_merge = 0, acked = 0, counted = 0, folded = 0, stored = 0, ident = 0;
   uint64_t issue = 0, loaded = 0;
+  uint64_t basis = 0, basis_bar = 0, query = 0;
   uint64_t data = 0, done = 0;     // this wavefront's
 };
 // the scheduling barriers keep the stamp where it is written relative to the code around it
@@ -128,6 +130,9 @@ __device__ __forceinline__ void trace_write(const DecodeArgs& a, const TraceStam
     r[7] = t.ident;
     r[8] = t.issue;
     r[9] = t.loaded;
+    r[10] = t.basis;
+    r[11] = t.basis_bar;
+    r[12] = t.query;
   }
 }
 
@@ -599,6 +604,9 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) float basis_dyn[];
   const bool klt = KLT && !KBF16 && (a.k_flags & NVKV_K_KLT);
   if (klt && wave < 4) load_basis_quarter(a.basis + static_cast<int64_t>(h) * kBasisFloats, basis_dyn, wave, lane);
+  if constexpr (TRACE) {
+    if (klt) ts.basis = stamp_now();
+  }
 
   // ---- start every independent memory access first: query row, sequence length, pages ----
   const bool q_wave = wave < 4;                 // wavefronts 0..3 prepare query heads 4h..4h+3
@@ -653,6 +661,9 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
 
   // ---------------- query prologue: wavefront w < 4 prepares query head 4h + w ----------------
   if (klt) __syncthreads();                    // the basis is in LDS
+  if constexpr (TRACE) {
+    if (klt) ts.basis_bar = stamp_now();
+  }
   // the new token's key transform: with the KLT rotation the idle extra wavefront does it
   // during the query prologue, otherwise after it
   float ny[4];
@@ -667,6 +678,7 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
     reinterpret_cast<uint32_t*>(q_lds[wave][2])[lane] = w2;
     reinterpret_cast<uint32_t*>(q_lds[wave][3])[lane] = 0u;
     if (lane == 0) q_descale[wave] = descale;
+    if constexpr (TRACE) ts.query = stamp_now();
   }
   __syncthreads();
   if constexpr (TRACE) ts.prologue = stamp_now();

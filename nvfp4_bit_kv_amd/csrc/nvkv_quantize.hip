@@ -235,13 +235,19 @@ __global__ void __launch_bounds__(64 * kKltWaves) k_quantize_append_klt(AppendPa
   const AppendArgs& va = p.a[1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  __shared__ __attribute__((aligned(16))) float basis_lds[kBasisFloats];
-  __shared__ __attribute__((aligned(16))) float ybuf[kHeadDim][kKltTok];
+  // one LDS object, the basis first: every rotation read is then a base register plus a
+  // constant offset below 64 KiB
+  __shared__ __attribute__((aligned(16))) float lds[kBasisFloats + kHeadDim * kKltTok];
+  float* const basis_lds = lds;
+  float (*const ybuf)[kKltTok] = reinterpret_cast<float (*)[kKltTok]>(lds + kBasisFloats);
   load_basis_lds(ka.basis + static_cast<int64_t>(h) * kBasisFloats, basis_lds, tid, 64 * kKltWaves);
   const int st_tok = 64 * (wave & 1) + lane, st_d0 = 32 * (wave >> 1);     // staging role
   const int cb = 8 * (wave & 1) + (lane & 7), tq = 8 * (wave >> 1) + (lane >> 3);   // rotation role
   const bool odd = (cb & 1) != 0;
-  const bool smooth = (ka.flags & 1u) != 0;
+  // the smoothing factors of the wavefront's 32 staging dims (1 without smoothing: x * 1 = x)
+  float rs[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) rs[i] = (ka.flags & 1u) ? ka.inv_smooth[h * kHeadDim + st_d0 + i] : 1.0f;
   const float gk = *ka.gscale;
   const int n_chunks = (p.n_tokens + kKltTok - 1) / kKltTok;
   uint4 kraw[4];
@@ -264,10 +270,8 @@ __global__ void __launch_bounds__(64 * kKltWaves) k_quantize_append_klt(AppendPa
       const uint32_t w[4] = {kraw[i].x, kraw[i].y, kraw[i].z, kraw[i].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int d = st_d0 + 8 * i + e;
-        float y = bf16_to_f32(e & 1 ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu));
-        if (smooth) y = y * ka.inv_smooth[h * kHeadDim + d];
-        ybuf[d][st_tok] = y;
+        const float x = bf16_to_f32(e & 1 ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu));
+        ybuf[st_d0 + 8 * i + e][st_tok] = x * rs[8 * i + e];
       }
     }
     __syncthreads();
@@ -277,13 +281,21 @@ __global__ void __launch_bounds__(64 * kKltWaves) k_quantize_append_klt(AppendPa
     for (int t = 0; t < kQuad; ++t)
 #pragma unroll
       for (int k = 0; k < 8; ++k) z[t][k] = 0.0f;
-#pragma unroll 4
+    // software pipelined: the reads of step j + 2 are issued before the multiply-adds of step j
+    float4 yq[3], b0[3], b1[3];
+    auto read_step = [&](int j, int slot) {
+      yq[slot] = *reinterpret_cast<const float4*>(&ybuf[j][kQuad * tq]);
+      b0[slot] = *reinterpret_cast<const float4*>(&basis_lds[j * kHeadDim + 8 * cb]);
+      b1[slot] = *reinterpret_cast<const float4*>(&basis_lds[j * kHeadDim + 8 * cb + 4]);
+    };
+    read_step(0, 0);
+    read_step(1, 1);
+#pragma unroll
     for (int j = 0; j < kHeadDim; ++j) {
-      const float4 yq = *reinterpret_cast<const float4*>(&ybuf[j][kQuad * tq]);
-      const float4 b0 = *reinterpret_cast<const float4*>(&basis_lds[j * kHeadDim + 8 * cb]);
-      const float4 b1 = *reinterpret_cast<const float4*>(&basis_lds[j * kHeadDim + 8 * cb + 4]);
-      const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-      const float yv[4] = {yq.x, yq.y, yq.z, yq.w};
+      if (j + 2 < kHeadDim) read_step(j + 2, (j + 2) % 3);
+      const int c = j % 3;
+      const float bv[8] = {b0[c].x, b0[c].y, b0[c].z, b0[c].w, b1[c].x, b1[c].y, b1[c].z, b1[c].w};
+      const float yv[4] = {yq[c].x, yq[c].y, yq[c].z, yq[c].w};
 #pragma unroll
       for (int t = 0; t < kQuad; ++t)
 #pragma unroll
