@@ -398,16 +398,31 @@ __device__ __forceinline__ void new_token_transform(const DecodeArgs& a, int lan
     // lane l forms z[2l] and z[2l + 1], and key lane L then reads back z[4L .. 4L + 3]
     if (!is_v) *reinterpret_cast<float4*>(&st.ky[4 * (lane & 31)]) = make_float4(y[0], y[1], y[2], y[3]);
     float z0 = 0.0f, z1 = 0.0f;
-#pragma unroll 4
+    // the reads of step j4 + 1 go out before the multiply-adds of step j4 (the two chains
+    // are latency-bound otherwise)
+    float4 y4 = *reinterpret_cast<const float4*>(&st.ky[0]);
+    float2 bj[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) bj[u] = *reinterpret_cast<const float2*>(basis_lds + u * kHeadDim + 2 * lane);
+#pragma unroll
     for (int j4 = 0; j4 < kHeadDim / 4; ++j4) {
-      const float4 y4 = *reinterpret_cast<const float4*>(&st.ky[4 * j4]);
+      float4 y4n = y4;
+      float2 bn[4] = {bj[0], bj[1], bj[2], bj[3]};
+      if (j4 + 1 < kHeadDim / 4) {
+        y4n = *reinterpret_cast<const float4*>(&st.ky[4 * (j4 + 1)]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          bn[u] = *reinterpret_cast<const float2*>(basis_lds + (4 * (j4 + 1) + u) * kHeadDim + 2 * lane);
+      }
       const float yv[4] = {y4.x, y4.y, y4.z, y4.w};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const float2 bj = *reinterpret_cast<const float2*>(basis_lds + (4 * j4 + u) * kHeadDim + 2 * lane);
-        z0 = __builtin_fmaf(bj.x, yv[u], z0);
-        z1 = __builtin_fmaf(bj.y, yv[u], z1);
+        z0 = __builtin_fmaf(bj[u].x, yv[u], z0);
+        z1 = __builtin_fmaf(bj[u].y, yv[u], z1);
       }
+      y4 = y4n;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) bj[u] = bn[u];
     }
     *reinterpret_cast<float2*>(&st.ky[2 * lane]) = make_float2(z0, z1);
     const float4 zk = *reinterpret_cast<const float4*>(&st.ky[4 * (lane & 31)]);
@@ -598,16 +613,11 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   const const_i32_ptr ptab = __builtin_bit_cast(const_i32_ptr, a.page_table) + static_cast<int64_t>(b) * a.max_pages_per_seq;
 
   // KLT key basis of this head into dynamic LDS (followed by a 128-float slot per query
-  // wavefront for the rotation) by the four query wavefronts, a quarter each;
+  // wavefront for the rotation) by the four query wavefronts, a quarter each (below);
   // their loads go out before their cache loads, so waiting for them does not wait for the
   // cache, and the other wavefronts issue their cache loads at once
   extern __shared__ __attribute__((aligned(16))) float basis_dyn[];
   const bool klt = KLT && !KBF16 && (a.k_flags & NVKV_K_KLT);
-  if (klt && wave < 4) load_basis_quarter(a.basis + static_cast<int64_t>(h) * kBasisFloats, basis_dyn, wave, lane);
-  if constexpr (TRACE) {
-    if (klt) ts.basis = stamp_now();
-  }
-
   // ---- start every independent memory access first: query row, sequence length, pages ----
   const bool q_wave = wave < 4;                 // wavefronts 0..3 prepare query heads 4h..4h+3
   const int hq_w = 4 * h + (q_wave ? wave : 0);
@@ -621,6 +631,11 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
   // the value is first needed after the loads of the first iterations have been issued
   const int seq_len_in = a.seq_lens[b];
   const int t_begin = split * a.split_tokens;
+  // the basis quarter after the query row, so the query's latency hides under the basis copy
+  if (klt && wave < 4) load_basis_quarter(a.basis + static_cast<int64_t>(h) * kBasisFloats, basis_dyn, wave, lane);
+  if constexpr (TRACE) {
+    if (klt) ts.basis = stamp_now();
+  }
 
   // First two iterations of this wavefront: addresses and loads are issued before the
   // sequence length arrives, bounded by the kernel arguments only (t_lim >= t_end), so the

@@ -254,16 +254,30 @@ __device__ __forceinline__ float query_terms(uint32_t qw, float2 sv, uint32_t k_
       // 2l, 2l + 1 as four interleaved partial sums each
       *reinterpret_cast<float2*>(row_lds + 2 * lane) = make_float2(x0, x1);
       float y0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, y1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 8
+      // the reads of step j4 + 1 go out before the multiply-adds of step j4
+      float4 q4 = *reinterpret_cast<const float4*>(row_lds);
+      float2 bj[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) bj[u] = *reinterpret_cast<const float2*>(basis_lds + u * kHeadDim + 2 * lane);
+#pragma unroll
       for (int j4 = 0; j4 < kHeadDim / 4; ++j4) {
-        const float4 q4 = *reinterpret_cast<const float4*>(row_lds + 4 * j4);
+        float4 q4n = q4;
+        float2 bn[4] = {bj[0], bj[1], bj[2], bj[3]};
+        if (j4 + 1 < kHeadDim / 4) {
+          q4n = *reinterpret_cast<const float4*>(row_lds + 4 * (j4 + 1));
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            bn[u] = *reinterpret_cast<const float2*>(basis_lds + (4 * (j4 + 1) + u) * kHeadDim + 2 * lane);
+        }
         const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float2 bj = *reinterpret_cast<const float2*>(basis_lds + (4 * j4 + u) * kHeadDim + 2 * lane);
-          y0[u] = __builtin_fmaf(bj.x, qv[u], y0[u]);
-          y1[u] = __builtin_fmaf(bj.y, qv[u], y1[u]);
+          y0[u] = __builtin_fmaf(bj[u].x, qv[u], y0[u]);
+          y1[u] = __builtin_fmaf(bj[u].y, qv[u], y1[u]);
         }
+        q4 = q4n;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) bj[u] = bn[u];
       }
       x0 = (y0[0] + y0[1]) + (y0[2] + y0[3]);
       x1 = (y1[0] + y1[1]) + (y1[2] + y1[3]);
