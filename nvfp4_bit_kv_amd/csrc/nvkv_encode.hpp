@@ -92,6 +92,37 @@ __device__ __forceinline__ uint32_t e4m3_scale_code(float A, float g) {
   return static_cast<uint32_t>(c + (up ? 1 : 0) - (down ? 1 : 0));
 }
 
+// The same decision with the two neighbouring midpoints read from a table of 6x midpoints,
+// t6[k] = 3 (v_k + v_{k+1}) for k = 0..125 (the values e4m3_mid_passed forms, so the result
+// is the same bit for bit); the kernels that encode many blocks keep the table in LDS.
+__device__ __forceinline__ void fill_e4m3_tables(float* val, float* t6, int tid, int nthreads) {
+#pragma clang fp contract(off)
+  for (int k = tid; k < 127; k += nthreads) {
+    val[k] = e4m3_value(static_cast<uint32_t>(k));
+    if (k < 126) t6[k] = 3.0f * (e4m3_value(static_cast<uint32_t>(k)) + e4m3_value(static_cast<uint32_t>(k + 1)));
+  }
+}
+
+__device__ __forceinline__ bool e4m3_mid_passed_t(uint32_t k, float A, float g, const float* t6) {
+#pragma clang fp contract(off)
+  const float d = __builtin_fmaf(-t6[k], g, A);
+  return (d > 0.0f) | ((d == 0.0f) & (((k + 1) & 1u) == 0u));
+}
+
+__device__ __forceinline__ uint32_t e4m3_scale_code_t(float A, float g, const float* t6) {
+#pragma clang fp contract(off)
+  const float x = A * __builtin_amdgcn_rcpf(6.0f * g);
+  const int c_sub = static_cast<int>(__builtin_rintf(x * 512.0f));
+  const uint32_t rn = (__float_as_uint(x) + 0x80000u) >> 20;
+  const int c_norm = rn > 1086u ? 126 : static_cast<int>(rn) - 960;
+  int c = x < 0.015625f ? c_sub : c_norm;
+  c = c > 126 ? 126 : c;
+  const uint32_t cu = static_cast<uint32_t>(c);
+  const bool up = (c < 126) & e4m3_mid_passed_t(cu < 125u ? cu : 125u, A, g, t6);
+  const bool down = (!up) & (c > 0) & !e4m3_mid_passed_t(cu > 0u ? cu - 1u : 0u, A, g, t6);
+  return static_cast<uint32_t>(c + (up ? 1 : 0) - (down ? 1 : 0));
+}
+
 // Per-block E2M1 decision bounds.  The midpoints of the magnitude grid {0, .5, 1, 1.5, 2,
 // 3, 4, 6} are t = .25, .75, 1.25, 1.75, 2.5, 3.5, 5, and the exact threshold of midpoint k is
 // T_k = t_k sigma g.  A tie goes to the even code: up at odd k (0.75, 1.75, 3.5: the value
@@ -194,10 +225,9 @@ constexpr float kBracketUp = 1.0f + 0x1p-20f;
 // monotonic, so when the converter gives both brackets the same code that code is RNE(Q),
 // exactly the decision of the bound-based encoder.  Where they differ (Q within about 2^-20
 // of a midpoint, a few elements in a million) the block takes the exact bound-based encoder.
-__device__ __forceinline__ void encode_block_with(const float (&y)[kBlock], float g, uint32_t S, uint32_t& lo,
-                                                  uint32_t& hi) {
+__device__ __forceinline__ void encode_block_sigma(const float (&y)[kBlock], float g, float sigma, uint32_t& lo,
+                                                   uint32_t& hi) {
 #pragma clang fp contract(off)
-  const float sigma = e4m3_value(S);
   const float u = sigma * g;
   const float R = __builtin_amdgcn_rcpf(u);
   const float r1 = R * kBracketDown, r2 = R * kBracketUp;
@@ -216,6 +246,11 @@ __device__ __forceinline__ void encode_block_with(const float (&y)[kBlock], floa
   hi = sigma > 0.0f ? h : 0u;
 }
 
+__device__ __forceinline__ void encode_block_with(const float (&y)[kBlock], float g, uint32_t S, uint32_t& lo,
+                                                  uint32_t& hi) {
+  encode_block_sigma(y, g, e4m3_value(S), lo, hi);
+}
+
 __device__ __forceinline__ float block_absmax(const float (&y)[kBlock]) {
   float A = 0.0f;
 #pragma unroll
@@ -228,6 +263,14 @@ __device__ __forceinline__ uint32_t encode_block(const float (&y)[kBlock], float
                                                  uint32_t& hi) {
   const uint32_t S = e4m3_scale_code(block_absmax(y), g);
   encode_block_with(y, g, S, lo, hi);
+  return S;
+}
+
+// The same with the E4M3 values (val[c], c = 0..126) and 6x midpoints (t6) read from tables.
+__device__ __forceinline__ uint32_t encode_block_t(const float (&y)[kBlock], float g, const float* val,
+                                                   const float* t6, uint32_t& lo, uint32_t& hi) {
+  const uint32_t S = e4m3_scale_code_t(block_absmax(y), g, t6);
+  encode_block_sigma(y, g, val[S], lo, hi);
   return S;
 }
 

@@ -60,34 +60,4 @@ __device__ __forceinline__ void rotate_cols(const float* B, const float* row, in
   }
 }
 
-// rotate_cols for four rows at once: z[t][k] = sum over j of B[j][c0 + k] * Y[j][t0 + t],
-// Y element-major with row stride ystride (floats), each z[t][k] the same chain of fp32 fused
-// multiply-adds in j as rotate_cols, so the result is identical bit for bit.  A basis read
-// serves four rows.
-template <int N>
-__device__ __forceinline__ void rotate_cols_quad(const float* B, const float* Y, int ystride, int t0, int c0,
-                                                 float (&z)[4][N]) {
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int k = 0; k < N; ++k) z[t][k] = 0.0f;
-#pragma unroll 2
-  for (int j = 0; j < kHeadDim; ++j) {
-    const float4 y = *reinterpret_cast<const float4*>(Y + j * ystride + t0);
-    const float4* bj = reinterpret_cast<const float4*>(B + j * kHeadDim + c0);
-#pragma unroll
-    for (int k = 0; k < N / 4; ++k) {
-      const float4 b = bj[k];
-      const float bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        z[0][4 * k + i] = __builtin_fmaf(bv[i], y.x, z[0][4 * k + i]);
-        z[1][4 * k + i] = __builtin_fmaf(bv[i], y.y, z[1][4 * k + i]);
-        z[2][4 * k + i] = __builtin_fmaf(bv[i], y.z, z[2][4 * k + i]);
-        z[3][4 * k + i] = __builtin_fmaf(bv[i], y.w, z[3][4 * k + i]);
-      }
-    }
-  }
-}
-
 }  // namespace nvkv

@@ -96,9 +96,10 @@ __device__ __forceinline__ void quads_load(const AppendPair& p, const AppendArgs
 }
 
 // The encode and stores of append_quads, from its loads.
-template <bool MSE>
+// TAB: block-scale decisions from the E4M3 tables in LDS (tval, tt6), else computed in registers.
+template <bool MSE, bool TAB>
 __device__ __forceinline__ void quads_finish(const AppendPair& p, const AppendArgs& a, int h, int lane,
-                                             const QuadLoads& L) {
+                                             const QuadLoads& L, const float* tval, const float* tt6) {
   const int blk = lane >> 3;
   const auto& raw = L.raw;
   const auto& slot = L.slot;
@@ -141,8 +142,12 @@ __device__ __forceinline__ void quads_finish(const AppendPair& p, const AppendAr
       for (int i = 0; i < kBlock; ++i) y[i] = y[i] * r[i];
     }
     if (a.flags & 2u) hadamard_row<8>(y, blk);
-    S[t] = (MSE && (a.flags & NVKV_K_MSE_SCALE)) ? encode_block_mse(y, gsc, lo[t], hi[t])
-                                                 : encode_block(y, gsc, lo[t], hi[t]);
+    if (MSE && (a.flags & NVKV_K_MSE_SCALE))
+      S[t] = encode_block_mse(y, gsc, lo[t], hi[t]);
+    else if (TAB)
+      S[t] = encode_block_t(y, gsc, tval, tt6, lo[t], hi[t]);
+    else
+      S[t] = encode_block(y, gsc, lo[t], hi[t]);
   }
   const bool quad = a.wide_stores && ok[0] && ok[1] && ok[2] && ok[3] && (slot[0] & 3) == 0 &&
                     slot[1] == slot[0] + 1 && slot[2] == slot[0] + 2 && slot[3] == slot[0] + 3;
@@ -186,10 +191,10 @@ __device__ __forceinline__ void quads_finish(const AppendPair& p, const AppendAr
 
 template <bool MSE>
 __device__ __forceinline__ void append_quads(const AppendPair& p, const AppendArgs& a, int h, int n_first,
-                                             int lane) {
+                                             int lane, const float* tval, const float* tt6) {
   QuadLoads L;
   quads_load(p, a, h, n_first, lane, L);
-  quads_finish<MSE>(p, a, h, lane, L);
+  quads_finish<MSE, true>(p, a, h, lane, L, tval, tt6);
 }
 
 // grid: x = token chunks of kTokPerWg, y = KV head row (< Hkv: keys, else values).  MSE:
@@ -202,9 +207,13 @@ __global__ void __launch_bounds__(256) k_quantize_append(AppendPair p) {
   const AppendArgs a = which ? p.a[1] : p.a[0];   // uniform select, no dynamic indexing
   const int h = row - (which ? p.hkv : 0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // E4M3 values and 6x midpoints for the block-scale decisions
+  __shared__ float tval[128], tt6[128];
+  fill_e4m3_tables(tval, tt6, threadIdx.x, 64 * kAppendWaves);
+  __syncthreads();
   const int n_first = static_cast<int>(blockIdx.x) * kTokPerWg + wave * kTokPerWave;
   if (n_first >= p.n_tokens) return;                   // uniform per wavefront
-  append_quads<MSE>(p, a, h, n_first, lane);
+  append_quads<MSE>(p, a, h, n_first, lane, tval, tt6);
 }
 
 // KLT keys ([cache post] cache-config table, KLT rows).  A workgroup of 8 wavefronts owns
@@ -329,7 +338,8 @@ __global__ void __launch_bounds__(64 * kKltWaves) k_quantize_append_klt(AppendPa
         ka.scales[sbase + ((off >> 2) * 8 + b) * 4 + (off & 3)] = static_cast<uint8_t>(S);
       }
     }
-    if (wave < 4 && base + kTokPerWave * wave < p.n_tokens) quads_finish<false>(p, va, h, lane, vl);
+    if (wave < 4 && base + kTokPerWave * wave < p.n_tokens)
+      quads_finish<false, false>(p, va, h, lane, vl, nullptr, nullptr);
   }
 }
 
