@@ -71,6 +71,10 @@ def parse():
                          "(libnvkv_bench.so) over one step and print its phase timeline")
     ap.add_argument("--trace-dump", default="",
                     help="with --trace-phases: also save the raw stamps (uint64 [layers][workgroups][48]) to this .npy file")
+    ap.add_argument("--append-kernel", default="library", choices=("library", "rowwave"),
+                    help="prefill workloads: time the library's quantize_append_kv (library) or the comparison "
+                         "layout of one wavefront per (token, KV head) row (rowwave, libnvkv_bench.so; plain "
+                         "and Hadamard key options only)")
     ap.add_argument("--no-stream-reference", action="store_true",
                     help="skip the plain streaming read of the same cache bytes (reference for stream_frac)")
     ap.add_argument("--separate", action="store_true",
@@ -315,7 +319,7 @@ class PrefillAppend:
     metric = "NVFP4-KV quantize/append: achieved HBM GB/s (% of peak) and tokens/s"
     kernel_label = "k_quantize_append (quantize_append_kv of batch 16 x 8192 new tokens), per layer"
 
-    def __init__(self, name):
+    def __init__(self, name, append_kernel="library"):
         import torch
         import nvfp4_bit_kv_amd as nk
         from synth import kv_inputs as S
@@ -325,6 +329,12 @@ class PrefillAppend:
         self.name, self.variant, self.c = name, v, c
         self.B, self.T, self.hkv, self.L = c["B"], c["T"], c["hkv"], c["layers"]
         self.flags = v["flags"]
+        self.append_kernel = append_kernel
+        if append_kernel == "rowwave":
+            if self.flags & ~3:
+                sys.exit("--append-kernel rowwave takes the plain and Hadamard key options only")
+            self.kernel_label = ("k_append_rowwave (quantize_append_kv of batch 16 x 8192 new tokens, one "
+                                 "wavefront per (token, KV head) row; comparison layout), per layer")
         self.copies = 1
         B, T, hkv = self.B, self.T, self.hkv
         self.pps = T // PAGE
@@ -349,6 +359,15 @@ class PrefillAppend:
         self._calib = None
 
     def step(self, cp):
+        if self.append_kernel == "rowwave":
+            lib, stream = bench_lib(), self.torch.cuda.current_stream().cuda_stream
+            for l in range(self.L):
+                cache, Ls = self.caches[l]
+                st = lib.nvkvb_quantize_append_rowwave(Ls, self.k[l].data_ptr(), self.v[l].data_ptr(),
+                                                       self.slots.data_ptr(), self.N, stream)
+                if st != 0:
+                    raise RuntimeError(f"row-wave append launch failed: {st}")
+            return
         for l in range(self.L):
             cache, Ls = self.caches[l]
             self.nk.quantize_append_kv(Ls, self.k[l], self.v[l], self.slots, self.N)
@@ -843,6 +862,8 @@ def bench_lib():
         lib.nvkvb_decode_trace.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, i32, i32, i32, vp, i32, vp, i32, f32,
                                            vp, vp, i32, vp, vp]
         lib.nvkvb_decode_trace.restype = ctypes.c_int
+        lib.nvkvb_quantize_append_rowwave.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, i32, vp]
+        lib.nvkvb_quantize_append_rowwave.restype = ctypes.c_int
         _BENCH_LIB = lib
     return _BENCH_LIB
 
@@ -981,23 +1002,30 @@ def copy_calibration(torch):
 
 
 def kernel_source_hash():
-    """sha256 over the sources of the decode/append kernels (the traffic figures in profiles/
-    hold for this exact source)."""
+    """sha256 over the sources of the decode, append and prefill-attention kernels and of the
+    bench's own kernels (the counter records in profiles/ hold for this exact source)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nvfp4_bit_kv_amd", "csrc")
     for name in ("nvkv_decode.hip", "nvkv_encode.hpp", "nvkv_device.hpp", "nvkv_quantize.hip", "nvkv_tiles.hpp",
-                 "nvkv_klt.hpp"):
+                 "nvkv_klt.hpp", "nvkv_prefill.hip", "nvkv_bench.hip"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def profile_name(wl):
+    """Name of the workload's records in profiles/: the workload name, with the append kernel
+    appended when the bench times the comparison layout instead of the library's."""
+    ak = getattr(wl, "append_kernel", "library")
+    return wl.name if ak == "library" else f"{wl.name}-{ak}"
 
 
 def traffic_per_launch(wl):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3 FETCH_SIZE +
     WRITE_SIZE summary of this workload, or None when there is none or the kernel sources
     changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.md")
+    path = os.path.join(ROOT, "profiles", f"traffic_{profile_name(wl)}.md")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -1014,7 +1042,7 @@ def sq_counters(wl):
     """VALU / MFMA activity of the dominant kernel from the committed rocprofv3 SQ-counter
     summary of this workload (profiles/sq_<workload>.md), or None when there is none or the
     kernel sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"sq_{wl.name}.md")
+    path = os.path.join(ROOT, "profiles", f"sq_{profile_name(wl)}.md")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -1044,7 +1072,7 @@ def main():
     if VARIANTS[args.workload].get("attention"):
         wl = PrefillAttention(args.workload)
     elif VARIANTS[args.workload]["cfg"] == "prefill":
-        wl = PrefillAppend(args.workload)
+        wl = PrefillAppend(args.workload, args.append_kernel)
     else:
         wl = DecodeStep(args.workload, args.copies, args.split_tokens, fused=not args.separate)
 
@@ -1124,6 +1152,7 @@ def main():
             "workload": wl.describe(),
             "global_batch": c["B"], "seq_len": c["T"], "layers": c["layers"], "parallelism": "none (1 GPU)",
             "split_tokens": args.split_tokens or "auto",
+            "append_kernel": getattr(wl, "append_kernel", "library"),
         },
         "tokens_per_s": round(wl.tokens_per_step() / step_s, 2),
         "hbm_frac_of_step": round(gbs / HBM_PEAK_GBS, 4),

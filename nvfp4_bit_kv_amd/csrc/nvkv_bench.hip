@@ -2,10 +2,13 @@
 //   - a plain streaming read of given device arrays (the reference point for what one launch
 //     can stream at the size of a decode launch's bytes);
 //   - the phase-stamped instance of the decode kernels (the same kernel sources, compiled with
-//     the stamps of k_decode<..., TRACE>), for a timeline of where a launch spends its time.
-// Both return a hipError_t as int.
+//     the stamps of k_decode<..., TRACE>), for a timeline of where a launch spends its time;
+//   - quantize_append_kv in the layout of one wavefront per (token, KV head) row, the
+//     comparison point for the library's layout of one lane per 16-element block.
+// All return a hipError_t as int.
 #include <hip/hip_runtime.h>
 
+#include "nvkv_encode.hpp"
 #include "nvkv_internal.hpp"
 
 #define NVKVB_API extern "C" __attribute__((visibility("default")))
@@ -47,6 +50,93 @@ __global__ void __launch_bounds__(256) k_stream_read(StreamArgs a) {
     }
   }
   if (acc == 0x9E3779B9u) a.sink[gid & 255u] = acc;
+}
+
+// quantize_append_kv with one wavefront per (token, KV head) row ([cache post] opening
+// paragraph: 16-element blocks along head_dim with an E4M3 scale each; cache-config table:
+// smoothing and the Hadamard-128 basis on keys).  Lane l holds elements 2l and 2l + 1, so a
+// block is 8 consecutive lanes: the block maximum is a 3-step lane-xor reduction, the
+// Hadamard stages 2..64 are lane-xor exchanges, and lane l's two E2M1 codes form byte l of
+// the row.  Each lane decides its own two codes exactly (converter brackets, the bound-based
+// encoder where they differ), so the bytes equal the library kernel's.  Four rows (one
+// token's consecutive heads) per workgroup; grid y: 0 keys, 1 values.
+struct RowWaveArgs {
+  const uint16_t* src[2];     // k_new, v_new: bf16 [N][Hkv][128]
+  uint8_t* codes[2];          // key codes (row-major), value codes (quad-interleaved words)
+  uint8_t* scales[2];
+  const float* inv_smooth;    // r [Hkv][128] (keys with smoothing)
+  const float* gscale;        // [2] = {g_K, g_V}
+  const int32_t* slots;       // [N]
+  uint32_t kflags;            // key transform: 1 smoothing, 2 Hadamard
+  int32_t n_rows;             // N * Hkv
+  int32_t hkv;
+  int32_t page_size;
+  int64_t max_slot;
+};
+
+__global__ void __launch_bounds__(256) k_append_rowwave(RowWaveArgs a) {
+#pragma clang fp contract(off)
+  const int which = static_cast<int>(blockIdx.y);
+  const int lane = threadIdx.x & 63;
+  const int row = static_cast<int>(blockIdx.x) * 4 + static_cast<int>(threadIdx.x >> 6);
+  if (row >= a.n_rows) return;                                   // uniform per wavefront
+  const int n = row / a.hkv, h = row - n * a.hkv;
+  const uint16_t* src = which ? a.src[1] : a.src[0];
+  const uint32_t pair = reinterpret_cast<const uint32_t*>(src + static_cast<int64_t>(row) * nvkv::kHeadDim)[lane];
+  float y0 = __uint_as_float(pair << 16), y1 = __uint_as_float(pair & 0xFFFF0000u);
+  const uint32_t fl = which ? 0u : a.kflags;
+  if (fl & 1u) {
+    const float2 r = reinterpret_cast<const float2*>(a.inv_smooth + h * nvkv::kHeadDim)[lane];
+    y0 = y0 * r.x;
+    y1 = y1 * r.y;
+  }
+  if (fl & 2u) {                       // (y_i, y_i+s) <- (y_i + y_i+s, y_i - y_i+s), s = 1 .. 64
+    const float t0 = y0 + y1, t1 = y0 - y1;
+    y0 = t0;
+    y1 = t1;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const float p0 = __shfl_xor(y0, m, 64), p1 = __shfl_xor(y1, m, 64);
+      const bool upper = (lane & m) != 0;
+      y0 = upper ? p0 - y0 : y0 + p0;
+      y1 = upper ? p1 - y1 : y1 + p1;
+    }
+  }
+  float A = fmaxf(fabsf(y0), fabsf(y1));
+  A = fmaxf(A, __shfl_xor(A, 1, 64));
+  A = fmaxf(A, __shfl_xor(A, 2, 64));
+  A = fmaxf(A, __shfl_xor(A, 4, 64));
+  const float g = a.gscale[which];
+  const uint32_t S = nvkv::e4m3_scale_code(A, g);
+  const float sigma = nvkv::e4m3_value(S);
+  const float u = sigma * g;
+  const float R = __builtin_amdgcn_rcpf(u);
+  const float r1 = R * nvkv::kBracketDown, r2 = R * nvkv::kBracketUp;
+  const uint32_t b1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y0 * r1, y1 * r1, 1.0f, 0) & 0xFFu;
+  const uint32_t b2 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y0 * r2, y1 * r2, 1.0f, 0) & 0xFFu;
+  uint32_t byte = b1;
+  if (__builtin_expect(sigma > 0.0f && !(b1 == b2 && u >= 0x1p-125f), 0)) {
+    const nvkv::E2m1Thresholds t(sigma, g);
+    byte = nvkv::e2m1_nibble(y0, t) | (nvkv::e2m1_nibble(y1, t) << 4);
+  }
+  byte = sigma > 0.0f ? (nvkv::clear_zero_signs(byte) & 0xFFu) : 0u;
+  // four bytes to lanes 4k (dword k of the row: elements 8k .. 8k + 7)
+  uint32_t w = byte | (static_cast<uint32_t>(__shfl_down(static_cast<int>(byte), 1, 64)) << 8);
+  w = w | (static_cast<uint32_t>(__shfl_down(static_cast<int>(w), 2, 64)) << 16);
+  const int32_t slot = a.slots[n];
+  if (slot < 0 || static_cast<int64_t>(slot) >= a.max_slot) return;
+  const int32_t page = slot / a.page_size, off = slot - page * a.page_size;
+  const int64_t ri = (static_cast<int64_t>(page) * a.hkv + h) * a.page_size + off;
+  if ((lane & 3) == 0) {
+    const int k = lane >> 2;
+    uint8_t* dst = which ? a.codes[1] + (ri - (off & 3)) * 64 + 16 * k + 4 * (off & 3) : a.codes[0] + ri * 64 + 4 * k;
+    *reinterpret_cast<uint32_t*>(dst) = w;
+  }
+  if ((lane & 7) == 0) {
+    const int64_t sbase = (static_cast<int64_t>(page) * a.hkv + h) * a.page_size * 8;
+    (which ? a.scales[1] : a.scales[0])[sbase + ((off >> 2) * 8 + (lane >> 3)) * 4 + (off & 3)] =
+        static_cast<uint8_t>(S);
+  }
 }
 
 }  // namespace
@@ -95,4 +185,39 @@ NVKVB_API int nvkvb_decode_trace(const nvkv_layer* layer, const uint16_t* q, con
   return static_cast<int>(nvkv::launch_decode(*layer, q, append ? k_new : nullptr, append ? v_new : nullptr, B, Hq,
                                               page_table, max_pages_per_seq, seq_lens, max_seq_len, sm_scale, out,
                                               ws, plan, static_cast<hipStream_t>(stream), trace));
+}
+
+// quantize_append_kv of N tokens with one wavefront per (token, KV head) row (k_append_rowwave):
+// NVFP4 keys and values, key flags within NVKV_K_SMOOTH | NVKV_K_HADAMARD, slots given; code
+// arrays 4-byte aligned.  Bytes identical to nvkv_quantize_append_kv's.
+NVKVB_API int nvkvb_quantize_append_rowwave(const nvkv_layer* layer, const uint16_t* k_new, const uint16_t* v_new,
+                                            const int32_t* slots, int32_t N, void* stream) {
+  if (!layer || !k_new || !v_new || !slots || N < 0) return static_cast<int>(hipErrorInvalidValue);
+  if (layer->k_fmt != NVKV_FMT_NVFP4 || layer->v_fmt != NVKV_FMT_NVFP4 || layer->head_dim != nvkv::kHeadDim ||
+      (layer->k_flags & ~(NVKV_K_SMOOTH | NVKV_K_HADAMARD)) != 0u || layer->page_size < 16 ||
+      layer->page_size % 16 != 0 || layer->num_kv_heads < 1)
+    return static_cast<int>(hipErrorNotSupported);
+  if (((reinterpret_cast<uintptr_t>(layer->k_data) | reinterpret_cast<uintptr_t>(layer->v_data)) & 3u) != 0)
+    return static_cast<int>(hipErrorInvalidValue);
+  if (N == 0) return static_cast<int>(hipSuccess);
+  const int64_t rows = static_cast<int64_t>(N) * layer->num_kv_heads;
+  if (rows > (int64_t{1} << 30)) return static_cast<int>(hipErrorInvalidValue);
+  RowWaveArgs a{};
+  a.src[0] = k_new;
+  a.src[1] = v_new;
+  a.codes[0] = static_cast<uint8_t*>(layer->k_data);
+  a.codes[1] = static_cast<uint8_t*>(layer->v_data);
+  a.scales[0] = layer->k_scales;
+  a.scales[1] = layer->v_scales;
+  a.inv_smooth = layer->k_inv_smooth;
+  a.gscale = layer->global_scale;
+  a.slots = slots;
+  a.kflags = layer->k_flags;
+  a.n_rows = static_cast<int32_t>(rows);
+  a.hkv = layer->num_kv_heads;
+  a.page_size = layer->page_size;
+  a.max_slot = static_cast<int64_t>(layer->num_pages) * layer->page_size;
+  hipLaunchKernelGGL(k_append_rowwave, dim3(static_cast<uint32_t>((rows + 3) / 4), 2), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return static_cast<int>(hipGetLastError());
 }

@@ -193,6 +193,10 @@ __device__ __forceinline__ void pf_iter(const IterLoads<KBF16>& L, const bool (&
                                         AfterV&& after_v) {
   const int c = ln.c, g = ln.g;
   // ---- QK ----
+  // The MFMA phases (QK, PV) run at raised issue priority: the wavefront in such a phase
+  // keeps the matrix pipe fed while the other wavefront of the SIMD fills the issue slots
+  // in between with its softmax and operand work.
+  __builtin_amdgcn_s_setprio(1);
   floatx4 sacc[2][2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
@@ -226,6 +230,7 @@ __device__ __forceinline__ void pf_iter(const IterLoads<KBF16>& L, const bool (&
       }
     }
   }
+  __builtin_amdgcn_s_setprio(0);
   after_k();
   // ---- scores (masked to -inf where needed) and the lazy running max.  The row descale
   // (a power of two) is folded into the exponent's FMA and into each row's raw threshold, so
@@ -311,10 +316,12 @@ __device__ __forceinline__ void pf_iter(const IterLoads<KBF16>& L, const bool (&
     od[p] = nib_odd(L.vd[2 * p], L.vd[2 * p + 1]);
   }
   after_v();
+  __builtin_amdgcn_s_setprio(1);
   pf_pv<0>(ev, od, sig, ap, st);
   pf_pv<1>(ev, od, sig, ap, st);
   pf_pv<2>(ev, od, sig, ap, st);
   pf_pv<3>(ev, od, sig, ap, st);
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Two workgroups per CU, so two wavefronts per SIMD: registers are capped at 256 (launch

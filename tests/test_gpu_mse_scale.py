@@ -8,7 +8,10 @@ Corner blocks (tensor scale g = 2^-7, so every constructed value is exact in bf1
 * an all-zero block; a block past 7 * 448 * g (only the saturated absmax code qualifies);
 * a block whose absmax-to-6 scale underflows to 0 while the smallest E4M3 scale keeps it;
 * a block whose absmax code lies outside the search interval and still wins;
-* random blocks spanning the E4M3 subnormal scales, clustered blocks and one-outlier blocks.
+* random blocks spanning the E4M3 subnormal scales, clustered blocks and one-outlier blocks;
+* tie-heavy blocks: every element a signed E2M1 midpoint times the scale of a code c of the
+  search run (times 2^-1, 1 or 2, so that the quotients of the codes c - 8, c and c + 8 land
+  on midpoints as well), some of them one bf16 ulp off.
 """
 import numpy as np
 import pytest
@@ -39,6 +42,10 @@ def corner_rows(hkv: int, n: int, seed: int = 3) -> np.ndarray:
         blocks[i, 0, 5] = rng.choice([-1, 1], 16) * (2.5 + 0.3 * rng.random(16)) * G * 40
         blocks[i, 0, 6] = rng.standard_normal(16) * 0.05 * G * 40
         blocks[i, 0, 6, rng.integers(16)] = 3.0 * G * 40
+        sig = float(O.e4m3_decode(int(rng.integers(40, 88))))    # normal scale, 4 significant bits
+        mids = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], 16) * rng.choice([0.5, 1.0, 2.0], 16)
+        ulp = rng.choice([-1, 0, 0, 1], 16) * 2.0 ** -7              # one bf16 ulp at [1, 2), or none
+        blocks[i, 0, 7] = rng.choice([-1, 1], 16) * mids * sig * G * (1.0 + ulp)
     return S.bf16_round(rows)
 
 
