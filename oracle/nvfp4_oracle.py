@@ -370,51 +370,112 @@ def mse_candidate_mask(A: np.ndarray, g64, c: int) -> np.ndarray:
     return (MSE_RATIO_LO * u <= A) & (A <= MSE_RATIO_HI * u)
 
 
-def mse_criterion(absy: np.ndarray, c: np.ndarray, g64) -> np.ndarray:
-    """J_c with  sum_j (y_j - y_hat_j)^2 = sum_j y_j^2 + g * J_c  for blocks |y| [n][16]
-    encoded with scale codes c [n]; the first sum does not depend on c, so the smallest J
-    is the smallest squared error.
+def mse_block_sse(absy: np.ndarray, c: np.ndarray, g64) -> np.ndarray:
+    """Squared FP4 error sum_j (|y_j| - y_hat_j)^2 of blocks |y| [n][16] encoded with scale
+    codes c [n], y_hat_j = m_j g sigma_c with m_j the round-to-nearest E2M1 magnitude of
+    |y_j| / (g sigma_c) (0 when sigma_c = 0), in fp64.
 
-    With u = g sigma_c and FP4 magnitudes m_j (y_hat_j = m_j u, same sign as y_j):
-      sum (y - m u)^2 - sum y^2 = u^2 M2 - 2 u P = g * sigma_c (g sigma_c M2 - 2 P),
-      P = sum m_j |y_j|,  M2 = sum m_j^2.
-    Every step is exact in fp64, so J is the exact real number: m_j |y_j| != 0 needs
-    |y_j| >= u/4 while |y_j| <= A <= 9u for every block that has more than one candidate,
-    so the terms of P lie within 37 bits of each other; 4 M2 is an integer below 2^12;
-    g sigma_c M2 has at most 24 + 4 + 12 bits; their difference at most 42; times the 4-bit
-    sigma_c at most 46."""
+    For every block that has more than one candidate each difference is exact in fp64: a
+    nonzero m_j needs |y_j| >= u/4 (u = g sigma_c) while |y_j| <= A <= 7u, and y_hat_j has at
+    most 3 + 4 + 24 significant bits, so both operands lie within 35 bits; a zero m_j leaves
+    |y_j|.  Each square rounds once and the sum of 16 non-negative terms at most 15 times,
+    so the result is within MSE_SSE_REL_ERR (relative) of the exact sum."""
     c = np.asarray(c, dtype=np.int64)
     sigma = E4M3_GRID[c]
     unit = (sigma * g64)[:, None] * np.ones_like(absy)
     mag = rne_grid_index(absy, unit, E2M1_MAG_GRID)
     mag = np.where((sigma == 0.0)[:, None], 0, mag)
-    m = E2M1_MAG_GRID[mag]
-    P = (m * absy).sum(axis=-1)
-    M2 = (m * m).sum(axis=-1)
-    return sigma * (g64 * sigma * M2 - 2.0 * P)
+    d = absy - E2M1_MAG_GRID[mag] * unit
+    return (d * d).sum(axis=-1)
+
+
+MSE_SSE_REL_ERR = 2.0 ** -48
+
+
+def mse_block_sse_exact(absy_row: np.ndarray, codes, g64) -> list:
+    """The same squared errors of one block under each of `codes` (None for a code < 0), exact:
+    |y_j| (an fp32 value) and y_hat_j = m_j * (g sigma_c) (at most 3 + 4 + 24 significant
+    bits, so exact in fp64) are dyadic rationals, which are put over one power-of-two
+    denominator D for all codes; each error is returned as the integer D^2 * sum_j
+    (|y_j| - y_hat_j)^2, so the errors of the codes compare exactly."""
+    absy_row = np.asarray(absy_row, np.float64)
+    yhat = []
+    for c in codes:
+        c = int(c)
+        if c < 0:
+            yhat.append(None)
+            continue
+        unit = float(E4M3_GRID[c]) * float(g64)
+        if unit == 0.0:
+            yhat.append(np.zeros(BLOCK))
+        else:
+            mag = rne_grid_index(absy_row[None], np.full((1, BLOCK), unit), E2M1_MAG_GRID)[0]
+            yhat.append(E2M1_MAG_GRID[mag] * unit)
+    ratios_y = [float(v).as_integer_ratio() for v in absy_row]
+    ratios_h = [None if h is None else [float(v).as_integer_ratio() for v in h] for h in yhat]
+    den = max([q for _, q in ratios_y] + [q for r in ratios_h if r is not None for _, q in r])
+    ys = [p_ * (den // q) for p_, q in ratios_y]
+    out = []
+    for r in ratios_h:
+        out.append(None if r is None else sum((y - p_ * (den // q)) ** 2 for y, (p_, q) in zip(ys, r)))
+    return out
+
+
+def mse_candidates(A: np.ndarray, g64, s0: np.ndarray) -> np.ndarray:
+    """Candidate codes of each block [n][1 + the longest run]: column 0 the absmax-to-6 code
+    s0, then every other code c >= 1 with 7/4 <= A/(g sigma_c) <= 7 in increasing order (one
+    run of at most 17 codes); -1 pads."""
+    masks = [(c, mse_candidate_mask(A, g64, c) & (s0 != c)) for c in range(1, len(E4M3_GRID))]
+    width = 1 + int(np.max(sum(mk.astype(np.int64) for _, mk in masks), initial=0))
+    cand = np.full((A.shape[0], width), -1, dtype=np.int64)
+    cand[:, 0] = s0
+    cnt = np.ones(A.shape[0], dtype=np.int64)
+    for c, mk in masks:
+        idx = np.nonzero(mk)[0]
+        cand[idx, cnt[idx]] = c
+        cnt[idx] += 1
+    return cand
+
+
+def mse_pick(cand: np.ndarray, err) -> int:
+    """Column of the chosen candidate among the valid columns of one block, from their squared
+    errors (any exactly ordered numbers): the smallest error; ties keep column 0 (the
+    absmax-to-6 code), then the smallest code."""
+    cols = [k for k in range(cand.shape[0]) if cand[k] >= 0]
+    return min(cols, key=lambda k: (err[k], -1 if k == 0 else int(cand[k])))
 
 
 def mse_scale_codes(y32: np.ndarray, g: float) -> np.ndarray:
-    """E4M3 scale code per block ([..., 8]) minimising the block's squared FP4 error over
-    the candidates described above; the absmax-to-6 code is evaluated first and then the
-    other candidates in increasing code order, and a candidate replaces the best so far only
-    when its error is strictly smaller."""
+    """E4M3 scale code per block ([..., 8]) with the smallest squared FP4 error over the
+    candidates described above (ties: the absmax-to-6 code, then the smallest code).  The
+    errors are evaluated in fp64 (mse_block_sse); a block whose best error is not ahead of
+    every other candidate's by more than the fp64 error bound is decided on the exact
+    rational errors."""
     y32 = np.asarray(y32, dtype=np.float32)
     lead = y32.shape[:-1]
     absy = np.abs(y32.astype(np.float64)).reshape(-1, BLOCK)
     g64 = np.float64(np.float32(g))
     A = absy.max(axis=-1)
     s0 = absmax_scale_codes(A, g64)
-    best = s0.copy()
-    best_j = mse_criterion(absy, s0, g64)
-    for c in range(1, len(E4M3_GRID)):
-        idx = np.nonzero(mse_candidate_mask(A, g64, c) & (s0 != c))[0]
-        if idx.size == 0:
-            continue
-        j = mse_criterion(absy[idx], np.full(idx.size, c), g64)
-        win = j < best_j[idx]
-        best[idx[win]] = c
-        best_j[idx[win]] = j[win]
+    cand = mse_candidates(A, g64, s0)
+    n, K = cand.shape
+    sse = np.full((n, K), np.inf)
+    for k in range(K):
+        idx = np.nonzero(cand[:, k] >= 0)[0]
+        if idx.size:
+            sse[idx, k] = mse_block_sse(absy[idx], cand[idx, k], g64)
+    # fp64 decision: the smallest error, ties to column 0 and then the smallest code
+    m = sse.min(axis=1)
+    rank = np.where(np.arange(K)[None, :] == 0, -1, cand)
+    kbest = np.where(sse == m[:, None], rank, np.iinfo(np.int64).max).argmin(axis=1)
+    rows = np.arange(n)
+    best = cand[rows, kbest]
+    # blocks where another candidate is within the rounding bound of the best are decided on
+    # the exact rational errors
+    close = sse <= (m * (1.0 + 4 * MSE_SSE_REL_ERR))[:, None]
+    close[rows, kbest] = False
+    for i in np.nonzero(close.any(axis=1))[0]:
+        best[i] = cand[i, mse_pick(cand[i], mse_block_sse_exact(absy[i], cand[i], g64))]
     return best.reshape(lead + (N_BLOCKS,))
 
 
