@@ -199,9 +199,10 @@ __device__ __forceinline__ void append_quads(const AppendPair& p, const AppendAr
 
 // grid: x = token chunks of kTokPerWg, y = KV head row (< Hkv: keys, else values).  MSE:
 // compiled with the key block-scale search (which needs more registers than the plain
-// encoder, so the plain launch does not carry it).
+// encoder, so the plain launch does not carry it).  Four workgroups per CU: the search
+// instance fits 128 registers without spills, four wavefronts per SIMD instead of three.
 template <bool MSE>
-__global__ void __launch_bounds__(256) k_quantize_append(AppendPair p) {
+__global__ void __launch_bounds__(256, 4) k_quantize_append(AppendPair p) {
   const int row = static_cast<int>(blockIdx.y);
   const int which = row >= p.hkv ? 1 : 0;
   const AppendArgs a = which ? p.a[1] : p.a[0];   // uniform select, no dynamic indexing
