@@ -497,6 +497,7 @@ __device__ __forceinline__ uint32_t mse_scale_code_row(const float* row, float g
   int best_rank = 0x7FFFFFFF;
   uint32_t best = S0;
   static_assert(3 * 8 >= kMseMaxCand + 1, "three entries per lane cover the list");
+#pragma unroll
   for (int t = 0; t < 3; ++t) {
     const int v = sub + 8 * t;
     const uint32_t c = v == 0 ? S0 : first + static_cast<uint32_t>(v - 1);
