@@ -975,6 +975,11 @@ def trace_phases(torch, wl, dump=""):
         if np.isfinite(r[:, 10]).any():     # the KLT basis stamps of wavefront 0
             rows[-1].update(basis_quarter_staged=med(r[:, 10]), basis_barrier=med(r[:, 11]),
                             query_transformed=med(r[:, 12]))
+        own = np.isfinite(r[:, 13])          # the workgroups whose split holds the new token
+        if own.any():
+            rows[-1].update(new_token_begun=med(r[own, 13]), new_token_encoded=med(r[own, 14]),
+                            new_token_folded_in=med(r[own, 15]), owner_partials_issued=med(r[own, 8]),
+                            d_new_token_encode=med(r[own, 14] - r[own, 13]))
     out = {"launches": wl.L, "workgroups": n_wg, "waves_per_workgroup": waves, "n_splits": n_splits,
            "unit": "us; times after the first workgroup of the launch started, d_* are per-workgroup phase "
                    "durations (s_memrealtime, 100 MHz); medians over a launch's workgroups, then median and "

@@ -704,6 +704,34 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
 #pragma unroll
   for (int v = 0; v < 8; ++v) st.acc[v] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // The new token first, right after the query barrier: the extra wavefront needs none of the
+  // cache wavefronts' set-up below, and its encode (with MSE-searched key scales, the search)
+  // is what the split's partials wait for.
+  if (owns_new && app_wave) {
+    // the extra wavefront is the youngest on its SIMD: raised issue priority keeps it from
+    // waiting behind the cache wavefronts there, whose workgroup merge waits for it
+    __builtin_amdgcn_s_setprio(2);
+    uint64_t nt_begin = 0, nt_encoded = 0;
+    if constexpr (TRACE) nt_begin = stamp_now();
+    const bool ok = static_cast<uint32_t>(new_pg) < static_cast<uint32_t>(a.num_pages);
+    if (!nt_early) new_token_transform<KBF16>(a, lane, nreg, nt_stage, basis_dyn, ny);
+    new_token_encode<KBF16>(a, h, lane, nreg, ny, new_pg, new_off, ok, nt_stage);
+    if constexpr (TRACE) nt_encoded = stamp_now();
+    if (ok) new_token_update<KBF16>(nt_stage, q_lds, q_descale, lane, ln, st);
+    __builtin_amdgcn_s_setprio(0);
+    if constexpr (TRACE) {
+      // the new-token wavefront's own stamps, slots 13-15 of its workgroup's record
+      const uint64_t nt_done = stamp_now();
+      if (lane == 0) {
+        uint64_t* r = a.trace + (blockIdx.x + static_cast<int64_t>(gridDim.x) *
+                                                 (blockIdx.y + static_cast<int64_t>(gridDim.y) * blockIdx.z)) * kTraceSlots;
+        r[13] = nt_begin;
+        r[14] = nt_encoded;
+        r[15] = nt_done;
+      }
+    }
+  }
+
   if (!empty) {
     // A operand of QK (Q'): lane (c, g) = row c = (head c>>2, term c&3); instruction u, item
     // e <-> dim 32g + 8u + e (the same dim order as the key codes a lane loads).
@@ -757,16 +785,6 @@ __global__ void __launch_bounds__(PIPE2 ? 512 : 1024) k_decode(DecodeArgs a) {
       }
     }
     if constexpr (TRACE) ts.done = stamp_now();
-    if (owns_new && app_wave) {
-      // the extra wavefront is the youngest on its SIMD: raised issue priority keeps it from
-      // waiting behind the cache wavefronts there, whose workgroup merge waits for it
-      __builtin_amdgcn_s_setprio(2);
-      const bool ok = static_cast<uint32_t>(new_pg) < static_cast<uint32_t>(a.num_pages);
-      if (!nt_early) new_token_transform<KBF16>(a, lane, nreg, nt_stage, basis_dyn, ny);
-      new_token_encode<KBF16>(a, h, lane, nreg, ny, new_pg, new_off, ok, nt_stage);
-      if (ok) new_token_update<KBF16>(nt_stage, q_lds, q_descale, lane, ln, st);
-      __builtin_amdgcn_s_setprio(0);
-    }
   }
 
   // ---------------- wavefront partials -> LDS -> workgroup partial ----------------
