@@ -215,6 +215,32 @@ __device__ __forceinline__ uint32_t cvt_pack8(const float* y, float Rs) {
 constexpr float kBracketDown = 1.0f - 0x1p-20f;
 constexpr float kBracketUp = 1.0f + 0x1p-20f;
 
+// Midpoint screen, for a block that is encoded under many scales.  The E2M1 rounding
+// midpoints are 1/4, 3/4, 5/4, 7/4, 5/2, 7/2 and 5: an odd number up to 7 times a power of
+// two.  An E4M3 value has at most 4 significant bits, so every midpoint of the quotient
+// |y| / (sigma g), over every scale sigma, is a point |y| / g = N with N of at most 7
+// significant bits.  W = fl(|y| rcp(g) + tiny) is within 3 * 2^-24 (relative) of |y| / g (the
+// reciprocal 1 ulp, the multiply-add half an ulp).  When the 17 significand bits of W below
+// its top 7 are at least kScreenUlps = 16 away from 0 and from 2^17, W is at least 16 ulps
+// from every number with 7 significant bits, which is at least 16 * 2^-24 relative; then
+// |y| / (sigma g) stays at least 12 * 2^-24 (relative) away from every midpoint of every scale,
+// twice the 6 * 2^-24 error of the converter's quotient |y| R, so that quotient rounds like
+// the exact one.  An element that can take a nonzero code under a scale has W >= sigma / 4 >=
+// 2^-11, far above the tiny addend (2^-126); a zero element gives W = tiny, whose low bits
+// pass.  The screen fails for about one block in 250 of generic data (and for data on a
+// coarse grid relative to g); those blocks keep the bracketed pass.
+constexpr uint32_t kScreenUlps = 16u;
+__device__ __forceinline__ bool clear_of_midpoints(const float (&y)[kBlock], float rg) {
+  constexpr float kTiny = 0x1.008p-126f;                 // normal; low 17 bits 0x4000
+  bool clear = true;
+#pragma unroll
+  for (int i = 0; i < kBlock; ++i) {
+    const uint32_t b = __float_as_uint(__builtin_fmaf(fabsf(y[i]), rg, kTiny));
+    clear &= (b << 15) + (kScreenUlps << 15) >= ((2u * kScreenUlps) << 15);
+  }
+  return clear;
+}
+
 // Encode one block with a given scale code S: writes the 16 nibbles packed in two dwords
 // (byte k = nibble 2k | nibble 2k+1 << 4); a zero scale gives an all-zero block.
 //
@@ -412,15 +438,21 @@ __device__ __forceinline__ void mse_partials_aligned(uint32_t w0, uint32_t w1, c
 }
 
 // Criterion J of code c (c >= 1, u = g sigma_c >= A/8) from the aligned block.
+// A block that passed the midpoint screen (clear) takes one converter pass.
 __device__ __forceinline__ double mse_code_criterion_aligned(const float (&y)[kBlock], const MseAligned& m, uint32_t c,
-                                                             float g) {
+                                                             float g, bool clear) {
 #pragma clang fp contract(off)
   const float s = e4m3_value(c);
   const float u = s * g;
   const float R = __builtin_amdgcn_rcpf(u);
-  const float r1 = R * kBracketDown, r2 = R * kBracketUp;
+  const bool fast = clear && u >= 0x1p-125f;
+  const float r1 = fast ? R : R * kBracketDown;
   uint32_t w0 = cvt_pack8(&y[0], r1), w1 = cvt_pack8(&y[8], r1);
-  const bool same = u >= 0x1p-125f && w0 == cvt_pack8(&y[0], r2) && w1 == cvt_pack8(&y[8], r2);
+  bool same = true;
+  if (!fast) {
+    const float r2 = R * kBracketUp;
+    same = u >= 0x1p-125f && w0 == cvt_pack8(&y[0], r2) && w1 == cvt_pack8(&y[8], r2);
+  }
   if (__builtin_expect(!same, 0)) {
     const E2m1Thresholds t(s, g);
     w0 = e2m1_pack8(&y[0], t);
@@ -436,7 +468,8 @@ __device__ __forceinline__ double mse_code_criterion_aligned(const float (&y)[kB
 // candidate replacing the best only when strictly better.  The run's codes all have
 // g sigma >= A/7, so they take the integer form; S0 does too unless its scale is below A/8
 // (a saturated block), where it takes the fp64 form.
-__device__ __forceinline__ uint32_t mse_scale_code(const float (&y)[kBlock], float A, float g, uint32_t S0) {
+__device__ __forceinline__ uint32_t mse_scale_code(const float (&y)[kBlock], float A, float g, uint32_t S0,
+                                                  bool clear) {
 #pragma clang fp contract(off)
   MseAligned m;
   mse_align(y, A, m);
@@ -445,7 +478,7 @@ __device__ __forceinline__ uint32_t mse_scale_code(const float (&y)[kBlock], flo
   if (S0) {
     const float s0 = e4m3_value(S0);
     if (__builtin_fmaf(-8.0f * s0, g, A) <= 0.0f) {      // A <= 8 g sigma_0, exactly
-      best_j = mse_code_criterion_aligned(y, m, S0, g);
+      best_j = mse_code_criterion_aligned(y, m, S0, g, clear);
     } else {
       double ay[kBlock];
 #pragma unroll
@@ -459,7 +492,7 @@ __device__ __forceinline__ uint32_t mse_scale_code(const float (&y)[kBlock], flo
     const float s = e4m3_value(c);
     if (mse_above(s, A, g)) break;                 // this code and every larger one
     if (mse_below(s, A, g) || c == S0) continue;
-    const double j = mse_code_criterion_aligned(y, m, c, g);
+    const double j = mse_code_criterion_aligned(y, m, c, g, clear);
     if (j < best_j) {
       best_j = j;
       best = c;
@@ -533,7 +566,8 @@ __device__ __forceinline__ uint32_t mse_scale_code_row(const float* row, float g
 __device__ __forceinline__ uint32_t encode_block_mse(const float (&y)[kBlock], float g, uint32_t& lo,
                                                      uint32_t& hi) {
   const float A = block_absmax(y);
-  const uint32_t S = mse_scale_code(y, A, g, e4m3_scale_code(A, g));
+  const bool clear = clear_of_midpoints(y, __builtin_amdgcn_rcpf(g));
+  const uint32_t S = mse_scale_code(y, A, g, e4m3_scale_code(A, g), clear);
   encode_block_with(y, g, S, lo, hi);
   return S;
 }

@@ -12,6 +12,11 @@ Corner blocks (tensor scale g = 2^-7, so every constructed value is exact in bf1
 * tie-heavy blocks: every element a signed E2M1 midpoint times the scale of a code c of the
   search run (times 2^-1, 1 or 2, so that the quotients of the codes c - 8, c and c + 8 land
   on midpoints as well), some of them one bf16 ulp off.
+
+Near-midpoint blocks at a generic tensor scale (smoothed keys ±2^m times per-channel factors
+placed 2 to 64 units of 2^-24 off an E2M1 midpoint of an E4M3 scale): the blocks that pass the
+append kernel's midpoint screen take one converter pass per candidate scale, the others the
+bracketed pass, and both must match the oracle.
 """
 import numpy as np
 import pytest
@@ -71,6 +76,49 @@ def test_mse_corner_blocks_append_kernel(lib):
     pages = P.Pages(1, N, True)
     cache = lib.CacheLayer(pages.num_pages, pages.page_size, hkv, k_flags=lib.K_MSE_SCALE)
     cache.gscale.copy_(torch.tensor([G, G]))
+    lib.quantize_append_kv(cache.struct(), P.to_dev_u16(kbits), P.to_dev_u16(vbits),
+                           P.to_dev_i32(pages.slots(0, 0, N)), N)
+    torch.cuda.synchronize()
+    check_rows(cache, pages, hkv, N, kc, ks, vc, vs)
+
+
+def screen_distance(y: np.ndarray, g: np.float32) -> np.ndarray:
+    """Distance, in units of the last place, of fl(|y| / g) from the nearest number with 7
+    significant bits (the quantity the append kernel's midpoint screen bounds from below)."""
+    w = (np.abs(y).astype(np.float64) / np.float64(g)).astype(np.float32)
+    low = w.view(np.uint32) & np.uint32(0x1FFFF)
+    return np.minimum(low, np.uint32(0x20000) - low)
+
+
+def test_mse_near_midpoints_append_kernel(lib):
+    hkv, N = 8, 128
+    g = np.float32(0.0021)
+    rng = np.random.default_rng(21)
+    sig = np.vectorize(lambda c: float(O.e4m3_decode(int(c))))(rng.integers(40, 80, (hkv, 8)))
+    mids = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], (hkv, 8, 16))
+    # half the blocks 36 to 64 units off (fl(|y|/g) 18 to 64 ulps from a 7-bit number), half 2 to 24
+    far = rng.random((hkv, 8, 1)) < 0.5
+    off = rng.choice([-1, 1], (hkv, 8, 16)) * np.where(far, rng.integers(36, 65, (hkv, 8, 16)),
+                                                      rng.integers(2, 25, (hkv, 8, 16)))
+    r = (np.float64(g) * sig[..., None] * mids * (1.0 + off * 2.0 ** -24)).astype(np.float32).reshape(hkv, 128)
+    # keys +-2^m, m in {-1, 0, 1}: y = k r is exact, so every element keeps its offset
+    kf = (rng.choice([-1.0, 1.0], (N, hkv, 128)) * 2.0 ** rng.integers(-1, 2, (N, hkv, 128))).astype(np.float32)
+    kbits = S.bf16_round(kf)
+    vbits = S.bf16_round(rng.standard_normal((N, hkv, 128)).astype(np.float32))
+    flags = lib.K_SMOOTH | lib.K_MSE_SCALE
+    y = O.key_transform(S.bf16_to_f32(kbits)[None], r[None, None], flags)[0]
+    assert np.array_equal(y, kf * r[None])
+    kc, ks = O.quantize_rows_mse(y, g)
+    vc, vs = O.quantize_rows(S.bf16_to_f32(vbits), g)
+    # the construction reaches both sides of the screen, and blocks that pass it by a few units
+    dist = screen_distance(y, g).reshape(N, hkv, 8, 16).min(-1)
+    assert np.count_nonzero(dist < 16) > 100 and np.count_nonzero((dist >= 16) & (dist < 32)) > 100
+    assert np.any(ks != O.quantize_rows(y, g)[1])
+    pages = P.Pages(1, N, True)
+    cache = lib.CacheLayer(pages.num_pages, pages.page_size, hkv, k_flags=flags)
+    cache.smooth.copy_(torch.from_numpy((np.float32(1.0) / r).astype(np.float32)))
+    cache.inv_smooth.copy_(torch.from_numpy(r))
+    cache.gscale.copy_(torch.tensor([g, g]))
     lib.quantize_append_kv(cache.struct(), P.to_dev_u16(kbits), P.to_dev_u16(vbits),
                            P.to_dev_i32(pages.slots(0, 0, N)), N)
     torch.cuda.synchronize()
