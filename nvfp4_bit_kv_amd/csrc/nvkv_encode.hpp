@@ -464,10 +464,13 @@ __device__ __forceinline__ double mse_code_criterion_aligned(const float (&y)[kB
   return mse_criterion(s, g, p2, m4);
 }
 
-// Search for a block held by one lane: S0 first, then the run in increasing code order, a
-// candidate replacing the best only when strictly better.  The run's codes all have
-// g sigma >= A/7, so they take the integer form; S0 does too unless its scale is below A/8
-// (a saturated block), where it takes the fp64 form.
+// Search for a block held by one lane, in the order of the definition: S0 first, then the run
+// in increasing code order, a candidate replacing the best only when strictly better.  When S0
+// lies in the run (its scale maps the absmax near 6, so nearly always) it is evaluated at its
+// place in the run instead, and it takes a tie with the best so far: the same result with one
+// evaluation fewer.  The run's codes all have g sigma >= A/7, so they take the integer form;
+// S0 outside the run does too unless its scale is below A/8 (a saturated block), where it
+// takes the fp64 form.
 __device__ __forceinline__ uint32_t mse_scale_code(const float (&y)[kBlock], float A, float g, uint32_t S0,
                                                   bool clear) {
 #pragma clang fp contract(off)
@@ -477,7 +480,9 @@ __device__ __forceinline__ uint32_t mse_scale_code(const float (&y)[kBlock], flo
   double best_j = 0.0;
   if (S0) {
     const float s0 = e4m3_value(S0);
-    if (__builtin_fmaf(-8.0f * s0, g, A) <= 0.0f) {      // A <= 8 g sigma_0, exactly
+    if (!mse_below(s0, A, g) && !mse_above(s0, A, g)) {
+      best_j = __builtin_inf();                       // S0 comes up in the run
+    } else if (__builtin_fmaf(-8.0f * s0, g, A) <= 0.0f) {      // A <= 8 g sigma_0, exactly
       best_j = mse_code_criterion_aligned(y, m, S0, g, clear);
     } else {
       double ay[kBlock];
@@ -491,9 +496,9 @@ __device__ __forceinline__ uint32_t mse_scale_code(const float (&y)[kBlock], flo
     if (c > 126u) break;
     const float s = e4m3_value(c);
     if (mse_above(s, A, g)) break;                 // this code and every larger one
-    if (mse_below(s, A, g) || c == S0) continue;
+    if (mse_below(s, A, g)) continue;
     const double j = mse_code_criterion_aligned(y, m, c, g, clear);
-    if (j < best_j) {
+    if (j < best_j || (c == S0 && j == best_j)) {
       best_j = j;
       best = c;
     }
@@ -503,10 +508,14 @@ __device__ __forceinline__ uint32_t mse_scale_code(const float (&y)[kBlock], flo
 
 // Search for the 8 blocks of a 128-element row staged in LDS (row[128]), by a whole
 // wavefront: lane L takes block L >> 3 and evaluates entries v = (L & 7) + 8t, t = 0, 1, 2,
-// of the block's candidate list (entry 0: S0; entry v >= 1: code first + v - 1 of the run,
-// at most kMseMaxCand entries); the block's eight lanes then keep the smallest (J, rank),
-// rank = -1 for S0 and the code otherwise, which is the order of the one-lane search.  The
-// call must be reached by all 64 lanes; every lane returns its block's code.
+// of the block's candidate list: entry v < kMseMaxCand is code first + v of the run, entry
+// kMseMaxCand is S0 when S0 lies outside the run (inside it, S0 is one of the run's
+// entries).  The block's eight lanes then keep the smallest (J, rank), rank = -1 for S0 and
+// the code otherwise, which is the order of the one-lane search.  A run spans a factor of 4
+// in scale, which holds 16 E4M3 values unless both ends are values, and S0 maps the absmax
+// near 6, inside the run, so the third round usually has no entry in any block: it runs only
+// when some lane has one.  The call must be reached by all 64 lanes; every lane returns its
+// block's code.
 __device__ __forceinline__ uint32_t mse_scale_code_row(const float* row, float g, int lane) {
 #pragma clang fp contract(off)
   const int sub = lane & 7;
@@ -526,20 +535,29 @@ __device__ __forceinline__ uint32_t mse_scale_code_row(const float* row, float g
   const float A = block_absmax(y);
   const uint32_t S0 = e4m3_scale_code(A, g);
   const uint32_t first = mse_first_code(S0, A, g);
+  bool s0_in_run = false;
+  if (S0) {
+    const float s = e4m3_value(S0);
+    s0_in_run = !mse_below(s, A, g) && !mse_above(s, A, g);
+  }
   double best_j = __builtin_inf();
   int best_rank = 0x7FFFFFFF;
   uint32_t best = S0;
-  static_assert(3 * 8 >= kMseMaxCand + 1, "three entries per lane cover the list");
+  static_assert(2 * 8 < kMseMaxCand && 3 * 8 > kMseMaxCand, "two full rounds, then the rest");
 #pragma unroll
   for (int t = 0; t < 3; ++t) {
     const int v = sub + 8 * t;
-    const uint32_t c = v == 0 ? S0 : first + static_cast<uint32_t>(v - 1);
-    bool valid = v == 0;
-    if (v > 0 && v <= kMseMaxCand && c <= 126u) {
-      const float s = e4m3_value(c);
-      valid = !mse_below(s, A, g) && !mse_above(s, A, g);
+    uint32_t c = S0;
+    bool valid = v == kMseMaxCand && !s0_in_run;
+    if (v < kMseMaxCand) {
+      c = first + static_cast<uint32_t>(v);
+      valid = false;
+      if (c <= 126u) {
+        const float s = e4m3_value(c);
+        valid = !mse_below(s, A, g) && !mse_above(s, A, g);
+      }
     }
-    if (!valid) continue;
+    if (!valid) continue;                   // the third round: skipped when no lane has an entry
     const double j = c == 0u ? 0.0 : mse_code_criterion(y, ay, c, g);
     const int rank = c == S0 ? -1 : static_cast<int>(c);
     if (j < best_j || (j == best_j && rank < best_rank)) {

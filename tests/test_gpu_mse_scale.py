@@ -8,6 +8,7 @@ Corner blocks (tensor scale g = 2^-7, so every constructed value is exact in bf1
 * an all-zero block; a block past 7 * 448 * g (only the saturated absmax code qualifies);
 * a block whose absmax-to-6 scale underflows to 0 while the smallest E4M3 scale keeps it;
 * a block whose absmax code lies outside the search interval and still wins;
+* blocks whose absmax is exactly 7 g times an E4M3 value, so that the run holds 17 codes;
 * random blocks spanning the E4M3 subnormal scales, clustered blocks and one-outlier blocks;
 * tie-heavy blocks: every element a signed E2M1 midpoint times the scale of a code c of the
   search run (times 2^-1, 1 or 2, so that the quotients of the codes c - 8, c and c + 8 land
@@ -43,6 +44,10 @@ def corner_rows(hkv: int, n: int, seed: int = 3) -> np.ndarray:
     blocks[0, 0, 3] = 2.5 * 2.0 ** -9 * G                   # absmax scale underflows
     blocks[0, 0, 4] = 0.5 * 2.0 ** -9 * G
     blocks[0, 0, 4, 0] = 7.5 * 2.0 ** -9 * G                # absmax code outside the interval
+    for b, code in ((0, 60), (1, 21)):                     # A = 7 g sigma_c: a run of 17 codes
+        sig = float(O.e4m3_decode(code))
+        blocks[0, 1, b] = rng.uniform(-6.5, 6.5, 16) * sig * G
+        blocks[0, 1, b, 3] = -7.0 * sig * G
     for i in range(1, n):                                   # clustered and one-outlier blocks
         blocks[i, 0, 5] = rng.choice([-1, 1], 16) * (2.5 + 0.3 * rng.random(16)) * G * 40
         blocks[i, 0, 6] = rng.standard_normal(16) * 0.05 * G * 40
@@ -72,6 +77,10 @@ def test_mse_corner_blocks_append_kernel(lib):
     vc, vs = O.quantize_rows(v32, G)
     # the constructed blocks decide as derived by hand
     assert list(ks[0, 0, :5]) == [0x3D, 0, 126, 1, 1]
+    grid = np.array([float(O.e4m3_decode(c)) for c in range(1, 127)])
+    for b in (0, 1):
+        A = float(np.max(np.abs(k32[0, 1, 16 * b:16 * b + 16])))
+        assert np.count_nonzero((A >= 1.75 * G * grid) & (A <= 7.0 * G * grid)) == 17
     assert np.any(ks != O.quantize_rows(k32, G)[1])
     pages = P.Pages(1, N, True)
     cache = lib.CacheLayer(pages.num_pages, pages.page_size, hkv, k_flags=lib.K_MSE_SCALE)
