@@ -205,7 +205,10 @@ template <bool MSE>
 __global__ void __launch_bounds__(256, 4) k_quantize_append(AppendPair p) {
   const int row = static_cast<int>(blockIdx.y);
   const int which = row >= p.hkv ? 1 : 0;
-  const AppendArgs a = which ? p.a[1] : p.a[0];   // uniform select, no dynamic indexing
+  // the selected half of the arguments, read from the kernel-argument segment (p, the only
+  // argument, is at its start) at a uniform offset: a select between the two copies in
+  // registers keeps both alive up to the stores, and their scalar registers spill
+  const AppendArgs a = ((const AppendPair*)__builtin_amdgcn_kernarg_segment_ptr())->a[which];
   const int h = row - (which ? p.hkv : 0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // E4M3 values and 6x midpoints for the block-scale decisions
