@@ -506,6 +506,23 @@ __device__ __forceinline__ uint32_t mse_scale_code(const float (&y)[kBlock], flo
   return best;
 }
 
+// Keep the smaller (J, rank) of this lane's and the lane that DPP control CTRL names.
+template <int CTRL>
+__device__ __forceinline__ void mse_keep_best_dpp(double& best_j, int& best_rank, uint32_t& best) {
+  const uint64_t jb = __builtin_bit_cast(uint64_t, best_j);
+  const uint32_t jlo = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(jb), CTRL, 0xF, 0xF, true));
+  const uint32_t jhi =
+      static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(jb >> 32), CTRL, 0xF, 0xF, true));
+  const double oj = __builtin_bit_cast(double, static_cast<uint64_t>(jlo) | (static_cast<uint64_t>(jhi) << 32));
+  const int orank = __builtin_amdgcn_mov_dpp(best_rank, CTRL, 0xF, 0xF, true);
+  const uint32_t oc = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(best), CTRL, 0xF, 0xF, true));
+  if (oj < best_j || (oj == best_j && orank < best_rank)) {
+    best_j = oj;
+    best_rank = orank;
+    best = oc;
+  }
+}
+
 // Search for the 8 blocks of a 128-element row staged in LDS (row[128]), by a whole
 // wavefront: lane L takes block L >> 3 and evaluates entries v = (L & 7) + 8t, t = 0, 1, 2,
 // of the block's candidate list: entry v < kMseMaxCand is code first + v of the run, entry
@@ -566,17 +583,11 @@ __device__ __forceinline__ uint32_t mse_scale_code_row(const float* row, float g
       best = c;
     }
   }
-#pragma unroll
-  for (int d = 1; d < 8; d <<= 1) {
-    const double oj = __shfl_xor(best_j, d, 64);
-    const int orank = __shfl_xor(best_rank, d, 64);
-    const uint32_t oc = static_cast<uint32_t>(__shfl_xor(static_cast<int>(best), d, 64));
-    if (oj < best_j || (oj == best_j && orank < best_rank)) {
-      best_j = oj;
-      best_rank = orank;
-      best = oc;
-    }
-  }
+  // the block's eight lanes by DPP: pairs (xor 1), quads (xor 2), then the mirrored half row
+  // (lane i of the eight takes lane 7 - i, in the other quad)
+  mse_keep_best_dpp<0xB1>(best_j, best_rank, best);
+  mse_keep_best_dpp<0x4E>(best_j, best_rank, best);
+  mse_keep_best_dpp<0x141>(best_j, best_rank, best);
   return best;
 }
 
