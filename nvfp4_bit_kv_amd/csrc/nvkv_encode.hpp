@@ -292,11 +292,31 @@ __device__ __forceinline__ uint32_t encode_block(const float (&y)[kBlock], float
   return S;
 }
 
-// The same with the E4M3 values (val[c], c = 0..126) and 6x midpoints (t6) read from tables.
-__device__ __forceinline__ uint32_t encode_block_t(const float (&y)[kBlock], float g, const float* val,
-                                                   const float* t6, uint32_t& lo, uint32_t& hi) {
-  const uint32_t S = e4m3_scale_code_t(block_absmax(y), g, t6);
-  encode_block_sigma(y, g, val[S], lo, hi);
+// Absmax-to-6 scale code through gfx950's E4M3 converter (OCP E4M3, round to nearest even),
+// on the same bracketing argument as the E2M1 codes: x = A rcp(fl(6g)) is within 2^-22 of
+// the exact A/(6g) (fl(6g), the reciprocal and the product), so x (1 -/+ 2^-20) bracket it,
+// and where the converter gives both the same code that code is RNE of the exact quotient.
+// Both are clamped to 448 first, where the code saturates (the converter is not told to
+// saturate).  Returns false where the two differ (the quotient within about 2^-20 of a
+// midpoint between codes); S is then unset.
+__device__ __forceinline__ bool e4m3_scale_code_cvt(float A, float r6g, uint32_t& S) {
+#pragma clang fp contract(off)
+  const float x = A * r6g;
+  const float b0 = fminf(x * kBracketDown, 448.0f), b1 = fminf(x * kBracketUp, 448.0f);
+  const uint32_t w = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(b0, b1, 0, false));
+  S = w & 0xFFu;
+  return S == ((w >> 8) & 0xFFu);
+}
+
+// The same with the 6x midpoints (t6) read from a table: the converter decides, and the exact
+// midpoint tests decide where its two brackets differ.  The scale value comes from the
+// converter too (codes 0..126 are exact in fp32).
+__device__ __forceinline__ uint32_t encode_block_t(const float (&y)[kBlock], float g, float r6g, const float* t6,
+                                                   uint32_t& lo, uint32_t& hi) {
+  const float A = block_absmax(y);
+  uint32_t S;
+  if (!e4m3_scale_code_cvt(A, r6g, S)) S = e4m3_scale_code_t(A, g, t6);
+  encode_block_sigma(y, g, __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(S), 0), lo, hi);
   return S;
 }
 
@@ -596,7 +616,9 @@ __device__ __forceinline__ uint32_t encode_block_mse(const float (&y)[kBlock], f
                                                      uint32_t& hi) {
   const float A = block_absmax(y);
   const bool clear = clear_of_midpoints(y, __builtin_amdgcn_rcpf(g));
-  const uint32_t S = mse_scale_code(y, A, g, e4m3_scale_code(A, g), clear);
+  uint32_t S0;
+  if (!e4m3_scale_code_cvt(A, __builtin_amdgcn_rcpf(6.0f * g), S0)) S0 = e4m3_scale_code(A, g);
+  const uint32_t S = mse_scale_code(y, A, g, S0, clear);
   encode_block_with(y, g, S, lo, hi);
   return S;
 }

@@ -132,6 +132,7 @@ __device__ __forceinline__ void quads_finish(const AppendPair& p, const AppendAr
     }
   }
   const float gsc = *a.gscale;
+  const float r6g = __builtin_amdgcn_rcpf(6.0f * gsc);
   uint32_t lo[kQuad], hi[kQuad], S[kQuad];
 #pragma unroll
   for (int t = 0; t < kQuad; ++t) {
@@ -145,7 +146,7 @@ __device__ __forceinline__ void quads_finish(const AppendPair& p, const AppendAr
     if (MSE && (a.flags & NVKV_K_MSE_SCALE))
       S[t] = encode_block_mse(y, gsc, lo[t], hi[t]);
     else if (TAB)
-      S[t] = encode_block_t(y, gsc, tval, tt6, lo[t], hi[t]);
+      S[t] = encode_block_t(y, gsc, r6g, tt6, lo[t], hi[t]);
     else
       S[t] = encode_block(y, gsc, lo[t], hi[t]);
   }

@@ -317,6 +317,56 @@ def test_near_midpoint_keys_bit_exact(lib, flags):
     assert np.array_equal(gs, vs[0]) and np.array_equal(gc, vc[0])
 
 
+@pytest.mark.parametrize("flags", [1, 1 | 4])
+def test_absmax_near_e4m3_midpoints_bit_exact(lib, flags):
+    """Smoothed keys whose block absmax lies 0, 1, 3 or 64 fp32 ulp from 6 g times an E4M3
+    midpoint (subnormal, normal and near-saturation codes): the append's E4M3 converter
+    brackets disagree within about 2^-20 of a midpoint and the exact tests decide there; also
+    with the MSE-searched scales, whose search starts from that code.  The smoothing factor of
+    each block's first channel puts y there exactly (x = 1 in bf16)."""
+    rng = np.random.default_rng(31)
+    hkv, N = 8, 16
+    g = np.float32(2.0 ** -7)
+    grid = O.E4M3_GRID
+    codes = [1, 3, 6, 7, 8, 21, 50, 77, 100, 118, 124, 125]
+    offs = [-64, -3, -1, 0, 1, 3, 64]
+    r = np.ones((hkv, 128), np.float32)
+    x = S.bf16_to_f32(S.bf16_round(rng.uniform(-1, 1, (hkv, 128)).astype(np.float32)))
+    targets = []
+    for h in range(hkv):
+        for blk in range(8):
+            i = 8 * h + blk
+            k, off = codes[i % len(codes)], offs[(i // len(codes) + i) % len(offs)]
+            m6 = np.float32(3.0 * (grid[k] + grid[k + 1]) * np.float64(g))     # 6 g midpoint, exact
+            t = (m6.view(np.uint32) + np.int64(off)).astype(np.uint32).view(np.float32)
+            j0 = 16 * blk
+            x[h, j0] = 1.0
+            r[h, j0] = t
+            x[h, j0 + 1:j0 + 16] *= np.float32(0.9) * t          # r = 1 there: |y| < t
+            targets.append(t)
+    x = S.bf16_to_f32(S.bf16_round(x))
+    kbits = np.broadcast_to(S.bf16_round(x)[None, None], (1, N, hkv, 128)).copy()
+    kbits[0, 1::2] ^= np.uint16(0x8000)                          # odd tokens negated
+    vbits = S.bf16_round(rng.standard_normal((1, N, hkv, 128)).astype(np.float32))
+    y = O.key_transform(S.bf16_to_f32(kbits), r[None, None], flags)
+    amax = np.abs(y[0, 0]).reshape(hkv, 8, 16).max(-1)
+    assert np.array_equal(amax.ravel(), np.array(targets, np.float32))
+    gg = np.array([g, g], np.float32)
+    kc, ks = O.quantize_keys(y, gg[0], flags)
+    if flags == 1:      # exact ties went to the even code, and the neighbours to their side
+        assert len(set(ks[0, 0].ravel().tolist())) > 12
+    vc, vs = O.quantize_rows(S.bf16_to_f32(vbits), gg[1])
+    pages = P.Pages(1, N, True)
+    s = (np.float32(1.0) / r).astype(np.float32)
+    cache = gpu_fill_cache(lib, kbits, vbits, hkv, flags, pages, torch.from_numpy(s).cuda(),
+                           torch.from_numpy(r).cuda(), gg)
+    gc, gs = P.rows_from_cache_vec(cache.k_data.cpu().numpy(), cache.k_scales.cpu().numpy(), pages, hkv, 0, N)
+    assert np.array_equal(gs, ks[0]) and np.array_equal(gc, kc[0])
+    gc, gs = P.rows_from_cache_vec(cache.v_data.cpu().numpy(), cache.v_scales.cpu().numpy(), pages, hkv, 0, N,
+                                   values=True)
+    assert np.array_equal(gs, vs[0]) and np.array_equal(gc, vc[0])
+
+
 def test_scale_code_at_every_e4m3_midpoint(lib):
     """Block absmax exactly at 6*g times each of the 126 E4M3 midpoints (ties: the even code
     wins), and one bf16 step above and below each, for two tensor scales; codes and scales
